@@ -1,0 +1,176 @@
+"""ctypes binding of the plain C oracle (moe_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and bench.py's cpu_baseline leg may
+import this package.  The HIP library never does, and this package never imports it.
+
+Every function takes host numpy arrays (or CPU torch tensors) and returns numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_DIR, "moe_oracle.c")
+_LIB = os.path.join(_DIR, "_build", "libmoe_oracle.so")
+_lib = None
+
+SCORE_FN = {"softmax": 0, "sigmoid": 1}
+
+
+def build(force: bool = False) -> str:
+    """Compile moe_oracle.c with gcc (IEEE double arithmetic: no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        os.makedirs(os.path.dirname(_LIB), exist_ok=True)
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
+                               "-fopenmp", "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("wdtype", ctypes.c_int32), ("n", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("I", ctypes.c_int32), ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p),
+                ("down", ctypes.c_void_p), ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p),
+                ("s_down", ctypes.c_void_p)]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        L = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int
+        L.oracle_fp8_e4m3fn_to_double.restype = ctypes.c_double
+        L.oracle_fp8_e4m3fn_to_double.argtypes = [ctypes.c_uint8]
+        L.oracle_bf16_to_double.restype = ctypes.c_double
+        L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_double_to_bf16.restype = ctypes.c_uint16
+        L.oracle_double_to_bf16.argtypes = [ctypes.c_double]
+        L.oracle_route.restype = i32
+        L.oracle_route.argtypes = [P, i32, i32, i32, i32, i32, P, P]
+        L.oracle_permute.restype = i32
+        L.oracle_permute.argtypes = [P, i32, i32, i32, P, P, P, P]
+        L.oracle_moe_layer.restype = i32
+        L.oracle_moe_layer.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32,
+                                       ctypes.POINTER(_Weights), P, ctypes.POINTER(_Weights),
+                                       P, i32, P, P, P, P, P, P, i32]
+        L.oracle_max_threads.restype = i32
+        L.oracle_max_threads.argtypes = [i32]
+        _lib = L
+    return _lib
+
+
+def _np(a, dtype):
+    """Contiguous host numpy view/copy of a numpy array or torch tensor with the given dtype."""
+    if hasattr(a, "detach"):
+        a = a.detach().cpu()
+        import torch  # local: only needed for tensors
+        tmap = {np.uint16: torch.int16, np.uint8: torch.uint8, np.float32: torch.float32,
+                np.int32: torch.int32, np.float64: torch.float64}
+        a = a.contiguous().view(tmap[dtype]).numpy()
+    a = np.ascontiguousarray(a)
+    return a.view(dtype) if a.dtype.itemsize == np.dtype(dtype).itemsize else a.astype(dtype)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+# ------------------------------------------------------------------ number formats
+
+def fp8_e4m3fn_to_double(code: int) -> float:
+    return lib().oracle_fp8_e4m3fn_to_double(int(code))
+
+
+def bf16_to_double(bits: int) -> float:
+    return lib().oracle_bf16_to_double(int(bits))
+
+
+def double_to_bf16(v: float) -> int:
+    return int(lib().oracle_double_to_bf16(float(v)))
+
+
+# ------------------------------------------------------------------ steps
+
+def route(scores, k: int, score_fn: str, renorm: int = 1):
+    s = _np(scores, np.float32)
+    T, E = s.shape
+    ids = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k), np.float32)
+    if lib().oracle_route(_ptr(s), T, E, k, SCORE_FN[score_fn], int(renorm), _ptr(ids), _ptr(w)):
+        raise ValueError("oracle_route: invalid arguments")
+    return ids, w
+
+
+def permute(ids, E: int):
+    a = _np(ids, np.int32)
+    T, k = a.shape
+    counts = np.zeros(E, np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    perm = np.zeros(T * k, np.int32)
+    inv = np.zeros(T * k, np.int32)
+    if lib().oracle_permute(_ptr(a), T, k, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv)):
+        raise ValueError("oracle_permute: expert id out of range")
+    return counts, offsets, perm, inv
+
+
+def _weights(ew, keep):
+    """ctypes struct for a synth.ExpertWeights-like object (host copies kept alive in `keep`)."""
+    wd = 1 if ew.wdtype == "bf16" else 0
+    mats = [_np(ew.gate, np.uint16 if wd else np.uint8), _np(ew.up, np.uint16 if wd else np.uint8),
+            _np(ew.down, np.uint16 if wd else np.uint8)]
+    scales = [None, None, None] if wd else [_np(ew.s_gate, np.float32), _np(ew.s_up, np.float32),
+                                            _np(ew.s_down, np.float32)]
+    keep.extend(mats + scales)
+    n, I, H = mats[0].shape
+    return _Weights(wd, n, H, I, *[_ptr(m) for m in mats], *[_ptr(s) for s in scales])
+
+
+def moe_layer(layer, rows=None, routed=None, expert_slot=None, with_shared=True, want_h=False,
+              want_y=False, n_threads: int = 0):
+    """Oracle of the whole layer for token rows `rows` (default: all).
+
+    `layer` is a synth.Layer (its tensors may live on any device; they are copied to host).
+    `routed` overrides layer.experts with a subset of experts (e.g. the ones the sampled rows
+    select, copied from the device), in which case `expert_slot` maps expert id -> slot.
+    Returns a dict with ids, w, out (bf16 bits, uint16) and optionally h (uint16), y, S (float64).
+    """
+    keep = []
+    scores = _np(layer.scores, np.float32)
+    x = _np(layer.x, np.uint16)
+    T, E, H, I, k = layer.T, layer.E, layer.H, layer.I, layer.k
+    rw = _weights(routed if routed is not None else layer.experts, keep)
+    sw = _weights(layer.shared, keep) if with_shared else None
+    slot = None if expert_slot is None else _np(expert_slot, np.int32)
+    r = None if rows is None else _np(np.asarray(rows), np.int32)
+    n = T if r is None else len(r)
+    res = dict(ids=np.zeros((n, k), np.int32), w=np.zeros((n, k), np.float32),
+               out=np.zeros((n, H), np.uint16))
+    if want_h:
+        res["h"] = np.zeros((n, k, I), np.uint16)
+    if want_y:
+        res["y"] = np.zeros((n, k, H), np.float64)
+        res["S"] = np.zeros((n, H), np.float64)
+    rc = lib().oracle_moe_layer(
+        _ptr(scores), _ptr(x), T, H, I, E, k, SCORE_FN[layer.score_fn], int(layer.renorm),
+        ctypes.byref(rw), _ptr(slot), ctypes.byref(sw) if sw is not None else None,
+        _ptr(r), n, _ptr(res["ids"]), _ptr(res["w"]), _ptr(res["out"]), _ptr(res.get("h")),
+        _ptr(res.get("y")), _ptr(res.get("S")), int(n_threads))
+    if rc:
+        raise ValueError("oracle_moe_layer: invalid arguments (row, k or expert slot)")
+    return res
+
+
+def max_threads(n_threads: int = 0) -> int:
+    return lib().oracle_max_threads(int(n_threads))
+
+
+def bf16_bits_to_float(a) -> np.ndarray:
+    """uint16 bf16 bit patterns -> float64 (host numpy)."""
+    a = _np(a, np.uint16)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

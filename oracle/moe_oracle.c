@@ -1,0 +1,286 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle of the routed sparse-MoE expert FFN.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg may load this library.  It shares no code, header, table or helper with the HIP library;
+ * both only consume the same seeded input tensors.
+ *
+ * What it computes is the plain definition of one MoE layer, evaluated token by token:
+ *   route   : each token keeps the k experts with the largest router score and gets
+ *             normalised gate weights (sparse MoE FFN: one big FFN split into many small
+ *             experts of which a few are active per token -- CMU 11-868 appendix A2 lecture
+ *             notes (semidirectx.com), section 4.1; DeepSeek-V3: 256 routed experts, 8 per
+ *             token, plus one shared expert -- KTransformers article (chenxutan.com), 1.2).
+ *   permute : expert histogram, exclusive prefix sum and the stable order of the (token, slot)
+ *             assignments by expert ("gating and sorting" before expert compute in the
+ *             expert-parallel MoE flow -- Xingyun OSDI'26 hybrid-inference article
+ *             (xingyun.xin), DSLP / expert-parallel section).
+ *   expert  : gate and up projections, activation times up, then down (the article's
+ *             "CPU fine-grained parallelism" section: each expert is gate, up and down, and
+ *             down consumes the activated product of gate and up).  Weights are E4M3FN FP8
+ *             with one fp32 scale per 128x128 block that multiplies the code (the article's
+ *             "native FP8 GEMV" section), or plain bf16.  Activations are bf16.
+ *   combine : weighted sum of the token's expert outputs plus the shared expert ("weighted
+ *             reduction" after combine in the same DSLP / expert-parallel section).
+ *
+ * Precision: every sum is accumulated in double.  Dequantised weights are exact in double
+ * (a 4-bit significand times a 24-bit scale).  The two roundings the method fixes are
+ * modelled: the intermediate h = SiLU(gate) * up is rounded to bf16 (round to nearest even),
+ * and the layer output is rounded to bf16.  Router weights are computed in double and
+ * rounded to fp32, the type the layer hands between steps.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - the selection key is the raw fp32 score (softmax and sigmoid are monotone); ties go to
+ *     the lower expert id; slots are stored in descending order of that key;
+ *   - softmax weights are normalised over the selected k (renorm=1) or over all E (renorm=0);
+ *     sigmoid weights are divided by their sum over the selected k (renorm=1) or used as is;
+ *   - the activation is SiLU(g) = g / (1 + exp(-g));
+ *   - the permutation is stable: within an expert, assignments keep ascending flat index t*k+j.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR 1
+
+/* ---------------------------------------------------------------- number formats ---------- */
+
+/* E4M3FN as defined by the OCP 8-bit floating point specification: sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent field 0 encodes subnormals m * 2^-9; S.1111.111 is NaN and
+ * there is no infinity.  The article's "native FP8 GEMV" section names this encoding. */
+double oracle_fp8_e4m3fn_to_double(uint8_t code) {
+    int sign = code >> 7, expo = (code >> 3) & 15, mant = code & 7;
+    double v;
+    if (expo == 15 && mant == 7) return NAN;
+    if (expo == 0)
+        v = ldexp((double)mant, -9);
+    else
+        v = ldexp(1.0 + mant / 8.0, expo - 7);
+    return sign ? -v : v;
+}
+
+/* bf16 is the upper half of an IEEE binary32. */
+double oracle_bf16_to_double(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bf16 value, ties to even, in one step.
+ * bf16 keeps 8 significant bits; its normal range starts at 2^-126 and its subnormals are
+ * multiples of 2^-133.  For |v| in [2^(e-1), 2^e) the spacing of bf16 values is 2^(e-8), and
+ * 2^-133 below the normal range. */
+uint16_t oracle_double_to_bf16(double v) {
+    if (isnan(v)) return 0x7FC0;
+    int e;
+    frexp(v, &e);
+    if (v == 0.0) e = -125;
+    int q = (e > -125 ? e : -125) - 8;
+    double r = ldexp(rint(ldexp(v, -q)), q); /* rint: round half to even (default mode) */
+    float f;
+    if (fabs(r) >= ldexp(1.0, 128))
+        f = (r > 0) ? INFINITY : -INFINITY;
+    else
+        f = (float)r; /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* ---------------------------------------------------------------- routing ------------------ */
+
+/* Top-k routing of T tokens over E experts.  scores [T][E] fp32 row-major.
+ * Outputs ids [T][k] (descending key, ties to the lower id) and weights w [T][k] fp32.
+ * score_fn 0 = softmax, 1 = sigmoid. */
+int oracle_route(const float* scores, int T, int E, int k, int score_fn, int renorm,
+                 int32_t* ids, float* w) {
+    if (k < 1 || k > E) return ORACLE_ERR;
+    unsigned char* taken = (unsigned char*)malloc((size_t)E);
+    for (int t = 0; t < T; ++t) {
+        const float* s = scores + (size_t)t * E;
+        int32_t* id = ids + (size_t)t * k;
+        memset(taken, 0, (size_t)E);
+        /* selection by repeated search for the largest remaining score */
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || s[e] > s[best])) best = e;
+            taken[best] = 1;
+            id[j] = best;
+        }
+        double den = 0.0, num[1024];
+        if (k > 1024) { free(taken); return ORACLE_ERR; }
+        if (score_fn == 0) {
+            double mx = (double)s[id[0]];
+            for (int j = 0; j < k; ++j) num[j] = exp((double)s[id[j]] - mx);
+            if (renorm)
+                for (int j = 0; j < k; ++j) den += num[j];
+            else
+                for (int e = 0; e < E; ++e) den += exp((double)s[e] - mx);
+        } else {
+            for (int j = 0; j < k; ++j) num[j] = 1.0 / (1.0 + exp(-(double)s[id[j]]));
+            if (renorm)
+                for (int j = 0; j < k; ++j) den += num[j];
+            else
+                den = 1.0;
+        }
+        for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = (float)(num[j] / den);
+    }
+    free(taken);
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- grouping ----------------- */
+
+/* Histogram, exclusive prefix sum and stable permutation of the T*k assignments by expert.
+ * perm[p] = flat index t*k+j of the p-th assignment in expert order; inv[perm[p]] = p. */
+int oracle_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                   int32_t* perm, int32_t* inv) {
+    long n = (long)T * k;
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (long f = 0; f < n; ++f) {
+        if (ids[f] < 0 || ids[f] >= E) return ORACLE_ERR;
+        counts[ids[f]]++;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    long p = 0;
+    for (int e = 0; e < E; ++e)
+        for (long f = 0; f < n; ++f)
+            if (ids[f] == e) perm[p++] = (int32_t)f;
+    for (p = 0; p < n; ++p) inv[perm[p]] = (int32_t)p;
+    return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- expert FFN --------------- */
+
+/* n experts of one layer, nn.Linear layout (output rows, input contiguous):
+ * gate, up [n][I][H]; down [n][H][I].  wdtype 0: E4M3FN codes with fp32 scales
+ * s_gate, s_up [n][I/128][H/128], s_down [n][H/128][I/128]; wdtype 1: bf16 bits, no scales. */
+typedef struct {
+    int32_t wdtype, n, H, I;
+    const void *gate, *up, *down;
+    const float *s_gate, *s_up, *s_down;
+} oracle_weights;
+
+/* Dequantised weight (row r, column c) of matrix `mat` of expert slot `x`, shape rows x cols. */
+static double weight(const oracle_weights* W, const void* mat, const float* sc, int x, int rows,
+                     int cols, int r, int c) {
+    size_t at = ((size_t)x * rows + r) * cols + c;
+    if (W->wdtype == 1) return oracle_bf16_to_double(((const uint16_t*)mat)[at]);
+    double scale = sc[((size_t)x * (rows / 128) + r / 128) * (cols / 128) + c / 128];
+    return oracle_fp8_e4m3fn_to_double(((const uint8_t*)mat)[at]) * scale;
+}
+
+/* One expert (slot x) on one token row xrow (bf16 bits, length H):
+ * h[n] = bf16(SiLU(g_n) * u_n) with g = Wg x, u = Wu x; y = Wd h (double). */
+static void expert_on_token(const oracle_weights* W, int x, const uint16_t* xrow, uint16_t* h_out,
+                            double* y_out, double* xd, double* hd) {
+    const int H = W->H, I = W->I;
+    for (int c = 0; c < H; ++c) xd[c] = oracle_bf16_to_double(xrow[c]);
+    for (int n = 0; n < I; ++n) {
+        double g = 0.0, u = 0.0;
+        for (int c = 0; c < H; ++c) {
+            g += xd[c] * weight(W, W->gate, W->s_gate, x, I, H, n, c);
+            u += xd[c] * weight(W, W->up, W->s_up, x, I, H, n, c);
+        }
+        double a = g / (1.0 + exp(-g)) * u;
+        uint16_t hb = oracle_double_to_bf16(a);
+        if (h_out) h_out[n] = hb;
+        hd[n] = oracle_bf16_to_double(hb);
+    }
+    for (int c = 0; c < H; ++c) {
+        double y = 0.0;
+        for (int n = 0; n < I; ++n) y += hd[n] * weight(W, W->down, W->s_down, x, H, I, c, n);
+        y_out[c] = y;
+    }
+}
+
+static void set_error(int* err) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+    *err = 1;
+}
+
+/* The whole layer for the tokens listed in rows[0..n_rows) (rows == NULL: all T tokens).
+ *   scores [T][E], x [T][H] bf16 bits;
+ *   routed: the routed experts; expert_slot[e] gives the slot of expert e in `routed`
+ *           (NULL: slot = e; -1: expert not provided, an error if selected);
+ *   shared: the shared expert (slot 0, gate weight 1) or NULL.
+ * Outputs for row i (all optional except out):
+ *   ids [i][k], w [i][k], out [i][H] bf16 bits, h [i][k][I] bf16 bits, y [i][k][H] double,
+ *   S [i][H] double (shared expert output).
+ * out = bf16( S + sum_j w_j * y_j ), accumulated in double in the order S, j = 0..k-1. */
+int oracle_moe_layer(const float* scores, const uint16_t* x, int T, int H, int I, int E, int k,
+                     int score_fn, int renorm, const oracle_weights* routed,
+                     const int32_t* expert_slot, const oracle_weights* shared,
+                     const int32_t* rows, int n_rows, int32_t* ids_out, float* w_out,
+                     uint16_t* out, uint16_t* h_out, double* y_out, double* S_out,
+                     int n_threads) {
+    if (routed->H != H || routed->I != I) return ORACLE_ERR;
+    if (shared && (shared->H != H || shared->I != I)) return ORACLE_ERR;
+    if (rows == NULL) n_rows = T;
+    int err = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel
+#endif
+    {
+        double* xd = (double*)malloc(sizeof(double) * H);
+        double* hd = (double*)malloc(sizeof(double) * I);
+        double* y = (double*)malloc(sizeof(double) * H * (size_t)(k + 1));
+        uint16_t* hb = (uint16_t*)malloc(sizeof(uint16_t) * I);
+        int32_t id[1024];
+        float wt[1024];
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int i = 0; i < n_rows; ++i) {
+            int t = rows ? rows[i] : i;
+            if (t < 0 || t >= T || k > 1024 ||
+                oracle_route(scores + (size_t)t * E, 1, E, k, score_fn, renorm, id, wt)) {
+                set_error(&err);
+                continue;
+            }
+            const uint16_t* xrow = x + (size_t)t * H;
+            double* S = y + (size_t)k * H;
+            for (int c = 0; c < H; ++c) S[c] = 0.0;
+            if (shared) expert_on_token(shared, 0, xrow, NULL, S, xd, hd);
+            for (int j = 0; j < k; ++j) {
+                int slot = expert_slot ? expert_slot[id[j]] : id[j];
+                if (slot < 0 || slot >= routed->n) { set_error(&err); break; }
+                expert_on_token(routed, slot, xrow, hb, y + (size_t)j * H, xd, hd);
+                if (h_out) memcpy(h_out + ((size_t)i * k + j) * I, hb, sizeof(uint16_t) * I);
+            }
+            for (int c = 0; c < H; ++c) {
+                double acc = S[c];
+                for (int j = 0; j < k; ++j) acc += (double)wt[j] * y[(size_t)j * H + c];
+                out[(size_t)i * H + c] = oracle_double_to_bf16(acc);
+            }
+            if (ids_out) memcpy(ids_out + (size_t)i * k, id, sizeof(int32_t) * k);
+            if (w_out) memcpy(w_out + (size_t)i * k, wt, sizeof(float) * k);
+            if (y_out) memcpy(y_out + (size_t)i * k * H, y, sizeof(double) * (size_t)k * H);
+            if (S_out) memcpy(S_out + (size_t)i * H, S, sizeof(double) * H);
+        }
+        free(xd); free(hd); free(y); free(hb);
+    }
+    return err ? ORACLE_ERR : ORACLE_OK;
+}
+
+/* Number of threads an OpenMP parallel region of this library uses with n_threads requested. */
+int oracle_max_threads(int n_threads) {
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+    return omp_get_max_threads();
+#else
+    (void)n_threads;
+    return 1;
+#endif
+}

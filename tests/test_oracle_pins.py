@@ -1,0 +1,298 @@
+"""Pins of the CPU oracle against things other than itself (runs without a GPU).
+
+* number formats: all 256 E4M3FN codes against torch's float8_e4m3fn and the OCP spec's closed
+  forms; bf16 round-to-nearest-even against torch's cast and hand-made ties;
+* routing: numpy's stable argsort (brute force over a full sort), argmax for k=1, torch/scipy
+  softmax and logistic functions for the weights, invariants;
+* grouping: numpy's stable argsort of the flat expert ids, bincount, inverse-permutation identity,
+  and the lecture notes' worked answer for the mean number of tokens per expert;
+* expert FFN + combine: a dense brute force (every expert on every token, masked by its gate
+  weight, numpy float64 matrix products, torch's FP8 decode, numpy-expanded scale blocks);
+  the E=1, k=1 textbook SwiGLU case; the identical-experts closed form; k=1 combine.
+"""
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import synth
+
+# ----------------------------------------------------------------------------- number formats
+
+
+def test_fp8_all_codes_match_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.fp8_e4m3fn_to_double(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zero
+    assert np.signbit(got[0x80]) and not np.signbit(got[0x00])
+
+
+def test_fp8_closed_forms_from_the_ocp_spec():
+    d = oracle.fp8_e4m3fn_to_double
+    assert d(0x7E) == 448.0  # largest finite
+    assert d(0x01) == 2.0 ** -9  # smallest subnormal
+    assert d(0x07) == 7 * 2.0 ** -9  # largest subnormal
+    assert d(0x08) == 2.0 ** -6  # smallest normal
+    assert d(0x38) == 1.0  # exponent field 7 = bias
+    assert d(0x3F) == 1.875
+    assert d(0xC0) == -2.0
+
+
+def test_bf16_round_to_nearest_even():
+    r = oracle.double_to_bf16
+    one = 0x3F80
+    assert r(1.0) == one
+    assert r(1.0 + 2.0 ** -8) == one  # tie -> even (1.0)
+    assert r(1.0 + 3 * 2.0 ** -8) == one + 2  # tie -> even (1 + 2^-6)
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -40) == one + 1  # just above a tie: up (no double rounding)
+    assert r(2.0 ** -133) == 0x0001  # smallest subnormal
+    assert r(2.0 ** -134) == 0x0000  # tie between 0 and the smallest subnormal -> 0
+    assert r(3 * 2.0 ** -134) == 0x0002  # tie -> even
+    assert r(-0.0) == 0x8000
+    assert r((2 - 2.0 ** -7) * 2.0 ** 127) == 0x7F7F  # largest finite
+    assert r((2 - 2.0 ** -8) * 2.0 ** 127) == 0x7F80  # rounds to +inf
+    assert r(float("nan")) & 0x7F80 == 0x7F80
+    # random fp32 values against torch's fp32 -> bf16 cast (a single rounding)
+    rng = np.random.default_rng(1)
+    v = np.concatenate([rng.standard_normal(3000).astype(np.float32),
+                        (rng.standard_normal(1000) * 1e-38).astype(np.float32),
+                        (rng.standard_normal(1000) * 1e30).astype(np.float32)])
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([r(float(a)) for a in v], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_decode():
+    bits = np.arange(0, 65536, 97, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.bf16_to_double(b) for b in bits])
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]) and np.array_equal(np.isnan(got), ~ok)
+
+
+# ----------------------------------------------------------------------------- routing
+
+
+def _tied_scores(T, E, seed):
+    """Scores on a coarse grid (many ties), with some +0.0 / -0.0 pairs."""
+    rng = np.random.default_rng(seed)
+    s = (rng.integers(-4, 5, size=(T, E)) / 4.0).astype(np.float32)
+    zero = rng.random((T, E)) < 0.2
+    s[zero] = np.where(rng.random(zero.sum()) < 0.5, np.float32(0.0), np.float32(-0.0))
+    return s
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 16, 2), (40, 256, 8), (17, 384, 8), (9, 5, 5), (33, 7, 1)])
+def test_route_ids_match_stable_full_sort(T, E, k):
+    for s in (_tied_scores(T, E, T + E), np.random.default_rng(E).random((T, E), dtype=np.float32)):
+        ids, w = oracle.route(s, k, "sigmoid")
+        ref = np.argsort(-s, axis=1, kind="stable")[:, :k]
+        assert np.array_equal(ids, ref)
+        assert all(len(set(r)) == k for r in ids)
+        if k == 1:
+            assert np.array_equal(ids[:, 0], np.argmax(s, axis=1))
+
+
+def test_route_weights_softmax_and_sigmoid():
+    rng = np.random.default_rng(3)
+    s = rng.standard_normal((50, 64)).astype(np.float32)
+    k = 6
+    ref_ids = np.argsort(-s, axis=1, kind="stable")[:, :k]
+    g = np.take_along_axis(s, ref_ids, axis=1).astype(np.float64)
+    # softmax over the selected logits
+    ids, w = oracle.route(s, k, "softmax", renorm=1)
+    assert np.array_equal(ids, ref_ids)
+    ref = torch.softmax(torch.from_numpy(g), dim=1).numpy()
+    np.testing.assert_allclose(w, ref, rtol=2e-7, atol=0)
+    # softmax over all experts, then the selected probabilities
+    _, w0 = oracle.route(s, k, "softmax", renorm=0)
+    full = torch.softmax(torch.from_numpy(s.astype(np.float64)), dim=1).numpy()
+    np.testing.assert_allclose(w0, np.take_along_axis(full, ref_ids, axis=1), rtol=2e-7, atol=0)
+    # sigmoid, renormalised over the selected
+    _, ws = oracle.route(s, k, "sigmoid", renorm=1)
+    e = scipy.special.expit(g)
+    np.testing.assert_allclose(ws, e / e.sum(axis=1, keepdims=True), rtol=2e-7, atol=0)
+    _, ws0 = oracle.route(s, k, "sigmoid", renorm=0)
+    np.testing.assert_allclose(ws0, e, rtol=2e-7, atol=0)
+    for ww in (w, ws):
+        np.testing.assert_allclose(ww.astype(np.float64).sum(axis=1), 1.0, atol=1e-6)
+        assert np.all(np.diff(ww, axis=1) <= 0)  # descending with the scores
+
+
+def test_route_rejects_bad_k():
+    s = np.zeros((2, 4), np.float32)
+    with pytest.raises(ValueError):
+        oracle.route(s, 5, "softmax")
+    with pytest.raises(ValueError):
+        oracle.route(s, 0, "softmax")
+
+
+# ----------------------------------------------------------------------------- grouping
+
+
+@pytest.mark.parametrize("T,E,k,skew", [(64, 256, 8, 0.0), (333, 16, 2, 0.0), (200, 32, 4, 1.5),
+                                        (1, 8, 8, 0.0), (128, 64, 1, 3.0)])
+def test_permute_matches_stable_argsort(T, E, k, skew):
+    ids = synth.random_topk_ids(T, E, k, seed=T, skew=skew).numpy()
+    counts, offsets, perm, inv = oracle.permute(ids, E)
+    flat = ids.ravel()
+    assert np.array_equal(counts, np.bincount(flat, minlength=E))
+    assert offsets[0] == 0 and offsets[-1] == T * k
+    assert np.array_equal(np.diff(offsets), counts)
+    assert np.array_equal(perm, np.argsort(flat, kind="stable"))
+    assert np.array_equal(inv[perm], np.arange(T * k))
+    for e in range(E):
+        seg = perm[offsets[e]:offsets[e + 1]]
+        assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+
+
+def test_permute_mean_tokens_per_expert_worked_answer():
+    # CMU 11-868 appendix A2 notes, exercise 7 (worked answer): at batch 64, a DeepSeek-V3
+    # routed expert (256 experts, 8 per token) is used by 64*8/256 = 2 tokens on average.
+    ids = synth.random_topk_ids(64, 256, 8, seed=0).numpy()
+    counts, offsets, _, _ = oracle.permute(ids, 256)
+    assert counts.sum() / 256 == 2.0 and offsets[-1] == 512
+
+
+def test_permute_rejects_out_of_range_ids():
+    with pytest.raises(ValueError):
+        oracle.permute(np.array([[0, 9]], np.int32), 4)
+
+
+# ----------------------------------------------------------------------------- expert FFN
+
+
+def _dense_weights(ew, H, I):
+    """float64 [n, rows, cols] dequantised weights via torch's FP8/bf16 decode and numpy scale expansion."""
+    def deq(q, s):
+        if ew.wdtype == "bf16":
+            return q.view(torch.bfloat16).to(torch.float64).numpy()
+        v = q.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        sx = np.repeat(np.repeat(s.numpy().astype(np.float64), 128, axis=1), 128, axis=2)
+        return v * sx
+    return deq(ew.gate, ew.s_gate), deq(ew.up, ew.s_up), deq(ew.down, ew.s_down)
+
+
+def _to_bf16_f64(a):
+    return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _dense_brute_force(layer, ids, w):
+    """Every expert on every token (float64), masked by its gate weight, plus the shared expert."""
+    x = torch.from_numpy(oracle._np(layer.x, np.uint16).view(np.int16)).view(torch.bfloat16)
+    x = x.to(torch.float64).numpy()
+    Wg, Wu, Wd = _dense_weights(layer.experts, layer.H, layer.I)
+    Sg, Su, Sd = _dense_weights(layer.shared, layer.H, layer.I)
+
+    def ffn(g, u, d):
+        G, U = x @ g.T, x @ u.T
+        h = _to_bf16_f64(scipy.special.expit(G) * G * U)  # note: h is exact within fp32 first
+        return h, h @ d.T
+
+    _, S = ffn(Sg[0], Su[0], Sd[0])
+    gate = np.zeros((layer.T, layer.E))
+    np.put_along_axis(gate, ids, w.astype(np.float64), axis=1)
+    acc = S.copy()
+    ys, hs = [], []
+    for e in range(layer.E):
+        h, y = ffn(Wg[e], Wu[e], Wd[e])
+        acc += gate[:, e:e + 1] * y
+        hs.append(h)
+        ys.append(y)
+    return acc, np.stack(hs, 1), np.stack(ys, 1), S
+
+
+def _check_layer_against_dense(layer):
+    res = oracle.moe_layer(layer, want_h=True, want_y=True)
+    acc, hs, ys, S = _dense_brute_force(layer, res["ids"], res["w"])
+    T = layer.T
+    y_sel = ys[np.arange(T)[:, None], res["ids"]]  # [T, k, H]
+    h_sel = hs[np.arange(T)[:, None], res["ids"]]
+    np.testing.assert_allclose(res["S"], S, rtol=1e-9, atol=1e-14)
+    np.testing.assert_allclose(res["y"], y_sel, rtol=1e-9, atol=1e-14)
+    hb = oracle.bf16_bits_to_float(res["h"])
+    # h: identical bf16 values except where the dense path's fp32 detour moves a value across a tie
+    assert np.mean(hb == h_sel) > 0.999
+    np.testing.assert_allclose(hb, h_sel, rtol=2.0 ** -7, atol=0)
+    out = oracle.bf16_bits_to_float(res["out"])
+    np.testing.assert_allclose(out, _to_bf16_f64(acc), rtol=2.0 ** -7, atol=1e-30)
+    assert np.mean(out == _to_bf16_f64(acc)) > 0.99
+    return res
+
+
+def test_ffn_dense_brute_force_tiny_bf16():
+    _check_layer_against_dense(synth.make_layer("tiny", seed=0))
+
+
+def test_ffn_dense_brute_force_tiny_fp8():
+    _check_layer_against_dense(synth.make_layer("tiny_fp8", seed=0))
+
+
+def test_ffn_dense_brute_force_rectangular_scale_grid():
+    # H != I so that a transposed scale index or weight layout cannot go unnoticed; random
+    # per-block scales so that every block's scale matters.
+    layer = synth.make_layer(dict(T=24, H=384, I=256, E=6, k=3, score_fn="sigmoid", scores="uniform",
+                                  wdtype="fp8"), seed=3)
+    g = torch.Generator().manual_seed(5)
+    for ew in (layer.experts, layer.shared):
+        for s in (ew.s_gate, ew.s_up, ew.s_down):
+            s.mul_(torch.rand(s.shape, generator=g) * 4 + 0.25)
+    _check_layer_against_dense(layer)
+
+
+def test_ffn_single_expert_is_textbook_swiglu():
+    # E = 1, k = 1: softmax over one logit gives weight 1, so out = bf16(shared(x) + FFN(x)).
+    layer = synth.make_layer(dict(T=8, H=256, I=128, E=1, k=1, score_fn="softmax", scores="normal",
+                                  wdtype="fp8"), seed=2)
+    res = oracle.moe_layer(layer, want_y=True, want_h=True)
+    assert np.all(res["w"] == 1.0) and np.all(res["ids"] == 0)
+    x = oracle.bf16_bits_to_float(layer.x)
+    Wg, Wu, Wd = (a[0] for a in _dense_weights(layer.experts, 256, 128))
+    g, u = x @ Wg.T, x @ Wu.T
+    h = _to_bf16_f64(g / (1 + np.exp(-g)) * u)
+    np.testing.assert_allclose(res["y"][:, 0], h @ Wd.T, rtol=1e-9, atol=1e-14)
+    expect = _to_bf16_f64(res["S"] + res["y"][:, 0])
+    got = oracle.bf16_bits_to_float(res["out"])
+    np.testing.assert_allclose(got, expect, rtol=2.0 ** -8, atol=0)
+    assert np.mean(got == expect) > 0.99
+
+
+def test_ffn_identical_experts_closed_form():
+    # All routed experts equal: sum_j w_j FFN(x) = FFN(x) since the renormalised weights sum to 1.
+    base = dict(T=12, H=256, I=128, k=4, score_fn="sigmoid", scores="uniform", wdtype="fp8")
+    many = synth.make_layer(dict(base, E=8), seed=4)
+    one = synth.make_layer(dict(base, E=1, k=1), seed=4)
+    for name in ("gate", "up", "down", "s_gate", "s_up", "s_down"):
+        t = getattr(one.experts, name)
+        setattr(many.experts, name, t.expand(8, *t.shape[1:]).contiguous())
+    one.shared = many.shared
+    one.x = many.x
+    a = oracle.moe_layer(many, want_y=True)
+    b = oracle.moe_layer(one, want_y=True)
+    for j in range(4):
+        np.testing.assert_array_equal(a["y"][:, j], b["y"][:, 0])
+    fa, fb = oracle.bf16_bits_to_float(a["out"]), oracle.bf16_bits_to_float(b["out"])
+    np.testing.assert_allclose(fa, fb, rtol=2.0 ** -8, atol=0)
+
+
+def test_layer_row_subset_and_expert_slots_agree_with_full_run():
+    layer = synth.make_layer("tiny_fp8", seed=1)
+    full = oracle.moe_layer(layer, want_y=True, want_h=True)
+    rows = [3, 0, 15, 7]
+    used = sorted(set(full["ids"][rows].ravel().tolist()))
+    slot = np.full(layer.E, -1, np.int32)
+    slot[used] = np.arange(len(used))
+    sub = oracle.moe_layer(layer, rows=rows, routed=layer.experts.select(used), expert_slot=slot,
+                           want_y=True, want_h=True)
+    for key in ("ids", "w", "out", "h", "y", "S"):
+        np.testing.assert_array_equal(sub[key], full[key][rows])
+    with pytest.raises(ValueError):  # an expert that was not provided
+        slot2 = slot.copy()
+        slot2[used[0]] = -1
+        oracle.moe_layer(layer, rows=rows, routed=layer.experts.select(used), expert_slot=slot2)
