@@ -1,0 +1,174 @@
+/*
+ * libmoe.h -- C ABI of the routed sparse-MoE expert FFN for AMD Instinct MI355X (gfx950).
+ *
+ * One MoE layer of a DeepSeek-V3-class model: each token is routed to k of E experts, the
+ * (token, expert) assignments are grouped by expert so that every expert runs one GEMM over
+ * all of its tokens instead of one GEMV per token, every expert computes
+ * down( SiLU(gate x) * up x ), and the expert outputs are summed back per token with the gate
+ * weights, together with the always-active shared expert.
+ *
+ * Sources (web pages; titles and sections):
+ *   [A2]  CMU 11-868 appendix A2 lecture notes, "LLM serving on heterogeneous hardware"
+ *         (semidirectx.com): 4.1 (sparse MoE FFN: a few of hundreds of small experts per
+ *         token), 4.2 (per-expert reuse B*k/E tokens; DeepSeek-V3 expert = three 7168x2048
+ *         matrices), exercises 6-7 and their worked answers.
+ *   [OSDI] Xingyun / Tsinghua OSDI'26 CPU-GPU hybrid MoE inference article (xingyun.xin):
+ *         DSLP / expert-parallel section (gating and sorting, expert compute, weighted
+ *         reduction), "native FP8 GEMV" section with Figures 9-10 (E4M3FN weights, bf16
+ *         activations, fp32 accumulation, one scale per 128-element block applied after the
+ *         block's partial sum), "CPU fine-grained parallelism" section (gate and up before
+ *         down within each expert; two global synchronisations per layer).
+ *   [KT]  KTransformers article (chenxutan.com): 1.2 (256 routed experts, 8 per token, plus
+ *         one shared expert), 2.2 (tokens that hit the same expert are batched so that GEMV
+ *         becomes GEMM).
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless marked (host); all device buffers are owned by the
+ *     caller, must not alias each other, and must be 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls only
+ *     enqueue work on that stream and return; they never allocate, free or synchronise.
+ *   - Arguments are validated on the host before anything is enqueued; a failed validation
+ *     returns an error and enqueues nothing.  T == 0 is valid and enqueues nothing (after the
+ *     scalar arguments are checked, pointers are not looked at and may be NULL).
+ *   - MOE_ERR_DEVICE is returned when the HIP runtime reports a launch error; faults that
+ *     happen while kernels run surface at the caller's next stream synchronisation.
+ *   - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *   - The library keeps no state between calls and is safe to call from several threads.
+ */
+#ifndef LIBMOE_H
+#define LIBMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* null pointer, negative size, k outside [1, E], ... */
+    MOE_ERR_UNSUPPORTED = 2, /* valid but outside this build's kernel limits (see each call) */
+    MOE_ERR_WORKSPACE = 3,   /* workspace smaller than the size query returned */
+    MOE_ERR_DEVICE = 4       /* the HIP runtime rejected a launch */
+} moe_status;
+
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
+
+typedef enum {
+    MOE_W_FP8_E4M3_B128 = 0, /* OCP E4M3FN codes + one fp32 scale per 128x128 block: w = code * s */
+    MOE_W_BF16 = 1           /* plain bf16 weights, no scales */
+} moe_wdtype;
+
+/* Kernel limits of this build. */
+#define MOE_MAX_EXPERTS 1024 /* E (and n_groups) */
+#define MOE_MAX_TOPK 32      /* k */
+
+/* Weights of n_groups experts of one layer, in nn.Linear layout (rows = outputs, the input
+ * dimension contiguous) [OSDI "native FP8 GEMV"; A2 4.2 for the 7168 x 2048 shape]:
+ *   w_gate, w_up : [n_groups][I][H]     w_down : [n_groups][H][I]
+ *   s_gate, s_up : [n_groups][I/128][H/128] fp32   s_down : [n_groups][H/128][I/128] fp32
+ * For MOE_W_BF16 the s_* pointers are ignored (may be NULL).  H and I must be multiples of 128.
+ * The struct itself is read on the host during the call; the arrays it points to are device
+ * memory and must stay valid until the enqueued work completes. */
+typedef struct {
+    int32_t dtype;    /* moe_wdtype */
+    int32_t n_groups; /* number of experts in the arrays */
+    int32_t H;        /* hidden size (input of gate/up, output of down) */
+    int32_t I;        /* expert intermediate size */
+    const void* w_gate;
+    const void* w_up;
+    const void* w_down;
+    const float* s_gate;
+    const float* s_up;
+    const float* s_down;
+} moe_expert_weights;
+
+/* Top-k routing [A2 4.1; KT 1.2; OSDI DSLP section "gating"].
+ *   scores   : fp32 [T][E] router logits, row-major, finite.
+ *   topk_ids : int32 [T][k] out. The k experts with the largest score, in descending order of
+ *              (score, then lower expert id); scores compare as floats (-0 == +0).
+ *   topk_w   : fp32 [T][k] out. score_fn SOFTMAX: exp(s_j - s_max) / D with D the sum over the
+ *              k selected (renorm != 0) or over all E experts (renorm == 0).  SIGMOID:
+ *              g_j = 1/(1+exp(-s_j)), divided by the sum of the k selected g (renorm != 0) or
+ *              used as is (renorm == 0).  Computed in double, rounded to fp32.
+ * Limits: 1 <= k <= min(E, MOE_MAX_TOPK), E <= MOE_MAX_EXPERTS.  Errors: INVALID_ARG for null
+ * pointers, T < 0, k outside [1, E], unknown score_fn; UNSUPPORTED beyond the limits. */
+moe_status moe_route(const float* scores, int32_t T, int32_t E, int32_t k, int32_t score_fn,
+                     int32_t renorm, int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Grouping of the T*k assignments by expert [OSDI DSLP section "sorting"; KT 2.2].
+ *   topk_ids : int32 [T][k], each row k distinct ids in [0, E) (as moe_route writes them).
+ *   counts   : int32 [E] out, number of assignments per expert.
+ *   offsets  : int32 [E+1] out, exclusive prefix sum of counts; offsets[E] = T*k.
+ *   perm     : int32 [T*k] out, perm[p] = flat index t*k+j of the p-th assignment in expert
+ *              order; stable: within one expert the flat indices ascend (so do the tokens).
+ *   inv      : int32 [T*k] out, inv[perm[p]] = p.
+ * The result is unique and deterministic (no atomics decide an order).  Ids outside [0, E) are
+ * a precondition violation: they are skipped and leave perm/inv entries unwritten.
+ * Limits: E <= MOE_MAX_EXPERTS, T*k < 2^31.  Errors: INVALID_ARG for null pointers, T < 0,
+ * k < 1, E < 1. */
+moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* inv, void* stream);
+
+/* Expert phase 1: gate and up projections with the activated product
+ * [OSDI "CPU fine-grained parallelism" (gate and up feed act*mul before down), "native FP8
+ * GEMV" (E4M3FN, 128-blocks, post-scaling); KT 2.2 (grouped GEMM)].
+ * For every grouped row p (p in [0, T*k)), with expert e such that offsets[e] <= p < offsets[e+1]
+ * and token t = perm[p] / k:
+ *     g = Wg[e] x_t,  u = Wu[e] x_t   (bf16 x, weights dequantised exactly, fp32 accumulation;
+ *                                      FP8 block scales applied to each 128-long partial sum)
+ *     h[p][n] = bf16_rne( SiLU(g_n) * u_n ),  SiLU(v) = v / (1 + exp(-v))
+ *   x       : bf16 [T][H].
+ *   perm    : int32 [T*k] from moe_permute; NULL selects the identity grouping used for the
+ *             shared expert (then k must be 1, offsets NULL, w->n_groups 1, and row p = token p).
+ *   offsets : int32 [n_groups+1] from moe_permute (n_groups = E); NULL with perm == NULL.
+ *   h       : bf16 [T*k][I] out, in grouped order.
+ * Rows of experts with no assignment cost nothing: their weights are not read.
+ * Errors: INVALID_ARG for null pointers, T < 0, k < 1, inconsistent identity grouping, unknown
+ * dtype; UNSUPPORTED when H or I is not a multiple of 128 or n_groups > MOE_MAX_EXPERTS. */
+moe_status moe_expert_gate_up(const uint16_t* x, int32_t T, int32_t k, const int32_t* perm,
+                              const int32_t* offsets, const moe_expert_weights* w, uint16_t* h,
+                              void* stream);
+
+/* Expert phase 2: down projection [OSDI "CPU fine-grained parallelism"; "native FP8 GEMV"].
+ *     y[p] = Wd[e] h[p]   (fp32 accumulation, block scales after each 128-long partial sum)
+ *   h       : bf16 [T*k][I] from moe_expert_gate_up (grouped order).
+ *   offsets : as for moe_expert_gate_up (NULL = one group of T rows, k must be 1).
+ *   y       : bf16 [T*k][H] out, grouped order (rounded to nearest even).
+ * Errors as for moe_expert_gate_up. */
+moe_status moe_expert_down(const uint16_t* h, int32_t T, int32_t k, const int32_t* offsets,
+                           const moe_expert_weights* w, uint16_t* y, void* stream);
+
+/* Bytes of workspace moe_expert_ffn needs (host output): the bf16 intermediate h [T*k][I]. */
+moe_status moe_expert_ffn_workspace_size(int32_t T, int32_t k, const moe_expert_weights* w,
+                                         size_t* bytes);
+
+/* Both expert phases in one call: h goes to the first T*k*I*2 bytes of `ws` (where it can be
+ * read after the stream synchronises), y as in moe_expert_down.  Arguments as for the two
+ * phases; ws must hold at least moe_expert_ffn_workspace_size bytes (else ERR_WORKSPACE). */
+moe_status moe_expert_ffn(const uint16_t* x, int32_t T, int32_t k, const int32_t* perm,
+                          const int32_t* offsets, const moe_expert_weights* w, uint16_t* y,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine [OSDI DSLP section "weighted reduction"; KT 1.2 shared expert]:
+ *     out[t][c] = bf16_rne( S[t][c] + sum_{j=0..k-1} w[t][j] * y[inv[t*k+j]][c] )
+ * accumulated in fp32 in that order (S first, then j ascending).
+ *   y        : bf16 [T*k][H] grouped order (moe_expert_down / moe_expert_ffn).
+ *   inv      : int32 [T*k] from moe_permute.
+ *   topk_w   : fp32 [T][k] from moe_route.
+ *   shared_y : bf16 [T][H], the shared expert's output (weight 1), or NULL for none.
+ *   out      : bf16 [T][H] out.
+ * Limits: H a multiple of 8.  Errors: INVALID_ARG for null pointers, T < 0, k < 1, H < 1. */
+moe_status moe_combine(const uint16_t* y, const int32_t* inv, const float* topk_w,
+                       const uint16_t* shared_y, int32_t T, int32_t k, int32_t H, uint16_t* out,
+                       void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* moe_status_string(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_H */

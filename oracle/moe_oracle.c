@@ -169,13 +169,30 @@ typedef struct {
     const float *s_gate, *s_up, *s_down;
 } oracle_weights;
 
+/* The 256 E4M3FN values, tabulated once from oracle_fp8_e4m3fn_to_double (a cache of that
+ * function, so the inner loops do not call ldexp per weight). */
+static double fp8_table[256];
+static int fp8_table_ready = 0;
+
+static void fill_fp8_table(void) {
+#ifdef _OPENMP
+#pragma omp critical(oracle_fp8_table)
+#endif
+    {
+        if (!fp8_table_ready) {
+            for (int i = 0; i < 256; ++i) fp8_table[i] = oracle_fp8_e4m3fn_to_double((uint8_t)i);
+            fp8_table_ready = 1;
+        }
+    }
+}
+
 /* Dequantised weight (row r, column c) of matrix `mat` of expert slot `x`, shape rows x cols. */
 static double weight(const oracle_weights* W, const void* mat, const float* sc, int x, int rows,
                      int cols, int r, int c) {
     size_t at = ((size_t)x * rows + r) * cols + c;
     if (W->wdtype == 1) return oracle_bf16_to_double(((const uint16_t*)mat)[at]);
     double scale = sc[((size_t)x * (rows / 128) + r / 128) * (cols / 128) + c / 128];
-    return oracle_fp8_e4m3fn_to_double(((const uint8_t*)mat)[at]) * scale;
+    return fp8_table[((const uint8_t*)mat)[at]] * scale;
 }
 
 /* One expert (slot x) on one token row xrow (bf16 bits, length H):
@@ -227,6 +244,7 @@ int oracle_moe_layer(const float* scores, const uint16_t* x, int T, int H, int I
     if (routed->H != H || routed->I != I) return ORACLE_ERR;
     if (shared && (shared->H != H || shared->I != I)) return ORACLE_ERR;
     if (rows == NULL) n_rows = T;
+    fill_fp8_table();
     int err = 0;
 #ifdef _OPENMP
     if (n_threads > 0) omp_set_num_threads(n_threads);

@@ -1,0 +1,216 @@
+"""Python binding of libmoe (include/libmoe.h): argument marshalling only.
+
+Every function has the name of the C entry point it calls.  Tensors are torch tensors on the
+GPU; calls enqueue on torch's current stream (or `stream=`) and do not synchronise.  Every step
+of the MoE layer runs in libmoe's HIP kernels; this module only passes pointers and sizes.  A
+missing libmoe.so is an error (build it with `python -m routed_expert_grouped_amd.build`).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_W_FP8_E4M3_B128, MOE_W_BF16 = 0, 1
+SCORE_FN = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
+
+EXPORTS = ("moe_route", "moe_permute", "moe_expert_gate_up", "moe_expert_down",
+           "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine", "moe_status_string")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        super().__init__(f"{call} failed: {moe_status_string(status)} ({status})")
+
+
+class MoeExpertWeights(ctypes.Structure):
+    """ctypes mirror of moe_expert_weights."""
+    _fields_ = [("dtype", ctypes.c_int32), ("n_groups", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("I", ctypes.c_int32), ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p), ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p),
+                ("s_down", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libmoe.so not found at {LIB_PATH}; build it with "
+                               "`python -m routed_expert_grouped_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
+        W = ctypes.POINTER(MoeExpertWeights)
+        L.moe_route.argtypes = [P, i32, i32, i32, i32, i32, P, P, P]
+        L.moe_permute.argtypes = [P, i32, i32, i32, P, P, P, P, P]
+        L.moe_expert_gate_up.argtypes = [P, i32, i32, P, P, W, P, P]
+        L.moe_expert_down.argtypes = [P, i32, i32, P, W, P, P]
+        L.moe_expert_ffn_workspace_size.argtypes = [i32, i32, W, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_expert_ffn.argtypes = [P, i32, i32, P, P, W, P, P, ctypes.c_size_t, P]
+        L.moe_combine.argtypes = [P, P, P, P, i32, i32, i32, P, P]
+        for name in EXPORTS[:-1]:
+            getattr(L, name).restype = st
+        L.moe_status_string.argtypes = [st]
+        L.moe_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _p(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _s(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(call, status):
+    if status != MOE_OK:
+        raise MoeError(call, status)
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def expert_weights(ew) -> MoeExpertWeights:
+    """moe_expert_weights for an object with .wdtype ("fp8"/"bf16"), .gate/.up/.down and
+    .s_gate/.s_up/.s_down device tensors (the arrays must outlive the calls that use it)."""
+    n, I, H = ew.gate.shape
+    fp8 = ew.wdtype == "fp8"
+    return MoeExpertWeights(MOE_W_FP8_E4M3_B128 if fp8 else MOE_W_BF16, n, H, I,
+                            ew.gate.data_ptr(), ew.up.data_ptr(), ew.down.data_ptr(),
+                            ew.s_gate.data_ptr() if fp8 else None,
+                            ew.s_up.data_ptr() if fp8 else None,
+                            ew.s_down.data_ptr() if fp8 else None)
+
+
+def moe_route(scores, k: int, score_fn="sigmoid", renorm: int = 1, topk_ids=None, topk_w=None,
+              stream=None):
+    T, E = scores.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=scores.device)
+    fn = SCORE_FN[score_fn] if isinstance(score_fn, str) else int(score_fn)
+    _check("moe_route", lib().moe_route(_p(scores), T, E, k, fn, int(renorm), _p(topk_ids),
+                                        _p(topk_w), _s(stream)))
+    return topk_ids, topk_w
+
+
+def moe_permute(topk_ids, E: int, counts=None, offsets=None, perm=None, inv=None, stream=None):
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev) if perm is None else perm
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev) if inv is None else inv
+    _check("moe_permute", lib().moe_permute(_p(topk_ids), T, k, E, _p(counts), _p(offsets),
+                                            _p(perm), _p(inv), _s(stream)))
+    return counts, offsets, perm, inv
+
+
+def moe_expert_gate_up(x, k: int, perm, offsets, w: MoeExpertWeights, h=None, stream=None):
+    T = x.shape[0]
+    if h is None:
+        h = torch.empty((T * k, w.I), dtype=torch.int16, device=x.device)
+    _check("moe_expert_gate_up", lib().moe_expert_gate_up(
+        _p(x), T, k, _p(perm), _p(offsets), ctypes.byref(w), _p(h), _s(stream)))
+    return h
+
+
+def moe_expert_down(h, T: int, k: int, offsets, w: MoeExpertWeights, y=None, stream=None):
+    if y is None:
+        y = torch.empty((T * k, w.H), dtype=torch.int16, device=h.device)
+    _check("moe_expert_down", lib().moe_expert_down(
+        _p(h), T, k, _p(offsets), ctypes.byref(w), _p(y), _s(stream)))
+    return y
+
+
+def moe_expert_ffn_workspace_size(T: int, k: int, w: MoeExpertWeights) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_expert_ffn_workspace_size",
+           lib().moe_expert_ffn_workspace_size(T, k, ctypes.byref(w), ctypes.byref(n)))
+    return n.value
+
+
+def moe_expert_ffn(x, k: int, perm, offsets, w: MoeExpertWeights, y=None, ws=None, stream=None):
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T * k, w.H), dtype=torch.int16, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(1, moe_expert_ffn_workspace_size(T, k, w)), dtype=torch.uint8,
+                         device=x.device)
+    _check("moe_expert_ffn", lib().moe_expert_ffn(
+        _p(x), T, k, _p(perm), _p(offsets), ctypes.byref(w), _p(y), _p(ws), ws.numel(),
+        _s(stream)))
+    return y, ws
+
+
+def moe_combine(y, inv, topk_w, shared_y, T: int, k: int, H: int, out=None, stream=None):
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.int16, device=y.device)
+    _check("moe_combine", lib().moe_combine(_p(y), _p(inv), _p(topk_w), _p(shared_y), T, k, H,
+                                            _p(out), _s(stream)))
+    return out
+
+
+class MoeLayer:
+    """Buffers and the call sequence of one MoE layer forward (route -> permute -> routed
+    gate/up -> routed down -> shared expert -> combine), all on one stream.
+
+    `experts` and `shared` are objects accepted by expert_weights(); `x` is bf16 bits [T, H]
+    (torch.int16) and `scores` fp32 [T, E], all on the GPU.
+    """
+
+    def __init__(self, T, H, I, E, k, experts, shared, score_fn="sigmoid", renorm=1, device="cuda"):
+        self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
+        self.score_fn, self.renorm = score_fn, renorm
+        self.w = expert_weights(experts)
+        self.ws_ = expert_weights(shared) if shared is not None else None
+        self._keep = (experts, shared)
+        d, i32 = device, torch.int32
+        self.topk_ids = torch.empty((T, k), dtype=i32, device=d)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=d)
+        self.counts = torch.empty(E, dtype=i32, device=d)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=d)
+        self.perm = torch.empty(max(1, T * k), dtype=i32, device=d)
+        self.inv = torch.empty(max(1, T * k), dtype=i32, device=d)
+        self.h = torch.empty((max(1, T * k), I), dtype=torch.int16, device=d)
+        self.y = torch.empty((max(1, T * k), H), dtype=torch.int16, device=d)
+        self.sh_h = torch.empty((max(1, T), I), dtype=torch.int16, device=d)
+        self.sh_y = torch.empty((max(1, T), H), dtype=torch.int16, device=d)
+        self.out = torch.empty((max(1, T), H), dtype=torch.int16, device=d)
+
+    def forward(self, scores, x, stream=None, gate_up_events=None):
+        """Enqueue the layer; returns `out` (bf16 bits [T, H]).  gate_up_events=(start, stop)
+        records torch events around the routed gate/up kernel (for timing)."""
+        T, k = self.T, self.k
+        moe_route(scores, k, self.score_fn, self.renorm, self.topk_ids, self.topk_w, stream)
+        moe_permute(self.topk_ids, self.E, self.counts, self.offsets, self.perm, self.inv, stream)
+        if gate_up_events is not None:
+            gate_up_events[0].record(stream)
+        moe_expert_gate_up(x, k, self.perm, self.offsets, self.w, self.h, stream)
+        if gate_up_events is not None:
+            gate_up_events[1].record(stream)
+        moe_expert_down(self.h, T, k, self.offsets, self.w, self.y, stream)
+        shared_y = None
+        if self.ws_ is not None:
+            moe_expert_gate_up(x, 1, None, None, self.ws_, self.sh_h, stream)
+            moe_expert_down(self.sh_h, T, 1, None, self.ws_, self.sh_y, stream)
+            shared_y = self.sh_y
+        moe_combine(self.y, self.inv, self.topk_w, shared_y, T, k, self.H, self.out, stream)
+        return self.out

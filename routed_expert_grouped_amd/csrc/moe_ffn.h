@@ -1,0 +1,44 @@
+// moe_ffn.h -- shared declarations of the grouped expert-projection kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "libmoe.h"
+
+namespace moe {
+
+// Arguments of one projection phase over grouped rows.
+//   phase 1: act = x [T][H] gathered through perm, w0/w1 = gate/up [G][N=I][K=H], out = h
+//   phase 2: act = h [rows][I] (grouped order),   w0 = down [G][N=H][K=I],        out = y
+struct GemmArgs {
+    const uint16_t* act;
+    const int32_t* perm;     // phase 1 only; NULL = identity
+    const int32_t* offsets;  // [n_groups+1]; NULL = one group of `rows` rows
+    int k;                   // slots per token (perm[p] / k = token)
+    int rows;                // grouped rows (T*k)
+    int n_groups;
+    int N, K;
+    const void* w0;
+    const void* w1;
+    const float* s0;
+    const float* s1;
+    bool fp8;
+    uint16_t* out;  // [rows][N]
+};
+
+// gemv shape: m-tiles of 16 rows; output columns per workgroup in each phase.
+constexpr int kGemvBM = 16;
+constexpr int kGemvColsP1 = 64;   // 4 waves x 16 h-columns (16 gate + 16 up rows each)
+constexpr int kGemvColsP2 = 128;  // 4 waves x 32 y-columns
+
+// The grouped-GEMV kernel serves every shape for now.
+inline bool use_gemv(int rows, int n_groups) {
+    (void)rows;
+    (void)n_groups;
+    return true;
+}
+
+moe_status launch_gemm(int phase, const GemmArgs& a, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,127 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad arguments on the
+host before anything is enqueued (no GPU needed: no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routed_expert_grouped_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmoe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH), reason="libmoe.so not built")
+
+# A non-null, 16-byte aligned address that is never dereferenced by the calls below: each of
+# them fails validation (or has T == 0) before any device work is enqueued.
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:moe_status|const char\*)\s+(moe_\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(moe.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert moe.moe_status_string(moe.MOE_OK) == "MOE_OK"
+    assert moe.moe_status_string(moe.MOE_ERR_WORKSPACE) == "MOE_ERR_WORKSPACE"
+    assert moe.moe_status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+def _w(dtype=0, n=4, H=256, I=128, ptr=FAKE, scales=True):
+    s = ptr if scales else None
+    return moe.MoeExpertWeights(dtype, n, H, I, ptr.value, ptr.value, ptr.value,
+                                s.value if s else None, s.value if s else None,
+                                s.value if s else None)
+
+
+def test_route_validation():
+    L = moe.lib()
+    st = None
+    assert L.moe_route(None, 4, 8, 2, 0, 1, FAKE, FAKE, st) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route(FAKE, 4, 8, 9, 0, 1, FAKE, FAKE, st) == moe.MOE_ERR_INVALID_ARG  # k > E
+    assert L.moe_route(FAKE, 4, 8, 0, 0, 1, FAKE, FAKE, st) == moe.MOE_ERR_INVALID_ARG  # k < 1
+    assert L.moe_route(FAKE, -1, 8, 2, 0, 1, FAKE, FAKE, st) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route(FAKE, 4, 8, 2, 7, 1, FAKE, FAKE, st) == moe.MOE_ERR_INVALID_ARG  # score_fn
+    assert L.moe_route(FAKE, 4, 2048, 2, 0, 1, FAKE, FAKE, st) == moe.MOE_ERR_UNSUPPORTED  # E
+    assert L.moe_route(FAKE, 4, 64, 33, 0, 1, FAKE, FAKE, st) == moe.MOE_ERR_UNSUPPORTED  # k
+    assert L.moe_route(FAKE, 0, 8, 2, 0, 1, FAKE, FAKE, st) == moe.MOE_OK  # T == 0: no-op
+
+
+def test_permute_validation():
+    L = moe.lib()
+    assert L.moe_permute(None, 4, 2, 8, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_permute(FAKE, 4, 0, 8, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_permute(FAKE, 4, 2, 0, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_permute(FAKE, 4, 2, 1025, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_permute(FAKE, 1 << 28, 16, 8, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_permute(FAKE, 0, 2, 8, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_OK
+
+
+def test_expert_validation():
+    L = moe.lib()
+    gu, dn = L.moe_expert_gate_up, L.moe_expert_down
+    ok = _w()
+    assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(ok), None, None) == moe.MOE_ERR_INVALID_ARG
+    assert gu(FAKE, 4, 2, FAKE, FAKE, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert gu(FAKE, 4, 2, FAKE, None, ctypes.byref(ok), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    # identity grouping needs k == 1 and one group
+    assert gu(FAKE, 4, 2, None, None, ctypes.byref(ok), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert gu(FAKE, 4, 1, None, None, ctypes.byref(ok), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    bad_dtype = _w(dtype=5)
+    assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(bad_dtype), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    no_scales = _w(scales=False)
+    assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(no_scales), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    bf16_no_scales = _w(dtype=1, scales=False)
+    assert gu(FAKE, 0, 2, FAKE, FAKE, ctypes.byref(bf16_no_scales), FAKE, None) == moe.MOE_OK
+    odd = _w(H=200)
+    assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(odd), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    many = _w(n=2000)
+    assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(many), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    unaligned = _w(ptr=ctypes.c_void_p(0x1004))
+    assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(unaligned), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert gu(FAKE, 0, 2, FAKE, FAKE, ctypes.byref(ok), FAKE, None) == moe.MOE_OK
+    assert dn(FAKE, 4, 0, FAKE, ctypes.byref(ok), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert dn(None, 4, 2, FAKE, ctypes.byref(ok), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert dn(FAKE, 0, 2, FAKE, ctypes.byref(ok), FAKE, None) == moe.MOE_OK
+
+
+def test_ffn_workspace():
+    L = moe.lib()
+    w = _w()
+    n = ctypes.c_size_t()
+    assert L.moe_expert_ffn_workspace_size(16, 2, ctypes.byref(w), ctypes.byref(n)) == moe.MOE_OK
+    assert n.value == 16 * 2 * 128 * 2
+    assert L.moe_expert_ffn_workspace_size(16, 2, None, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn(FAKE, 16, 2, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, n.value - 1,
+                            None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_expert_ffn(FAKE, 16, 2, FAKE, FAKE, ctypes.byref(w), FAKE, None, n.value,
+                            None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_expert_ffn(FAKE, 0, 2, FAKE, FAKE, ctypes.byref(w), FAKE, None, 0, None) == moe.MOE_OK
+
+
+def test_combine_validation():
+    L = moe.lib()
+    c = L.moe_combine
+    assert c(None, FAKE, FAKE, None, 4, 2, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert c(FAKE, FAKE, FAKE, None, 4, 0, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert c(FAKE, FAKE, FAKE, None, 4, 2, 60, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert c(FAKE, FAKE, FAKE, ctypes.c_void_p(0x1008), 4, 2, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert c(FAKE, FAKE, FAKE, None, 0, 2, 64, FAKE, None) == moe.MOE_OK
+
+
+def test_binding_raises_on_error_status():
+    with pytest.raises(moe.MoeError) as ei:
+        moe._check("moe_route", moe.MOE_ERR_UNSUPPORTED)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED and "MOE_ERR_UNSUPPORTED" in str(ei.value)
