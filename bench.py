@@ -1,0 +1,246 @@
+"""Benchmark of one MoE layer forward on one MI355X (libmoe, HIP).
+
+A step is one pass of the whole path over one batch of synthetic tokens, with every input and
+weight resident in HBM:  route -> permute -> routed gate/up -> routed down -> shared gate/up ->
+shared down -> combine, all on one stream.
+
+The headline `value` is tokens/s of the DeepSeek-V3-shaped decode layer (T=16, 256 experts,
+top-8, FP8 block-scaled weights).  The same line carries the 4096-token prefill layer under
+"prefill", the roofline of the dominant kernel (the routed gate/up projection, HIP events around
+its launch in every timed step) and the CPU oracle timed on a bounded sample on the host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_decode] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
+METRIC = "MoE-layer tokens/s at T=16 and T=4096; % of HBM BW / FP8 MFMA peak"
+
+
+# ------------------------------------------------------------------ algorithmic accounting
+
+def expert_bytes(H: int, I: int, wdtype: str = "fp8") -> int:
+    """Bytes of one expert's three projection matrices (+ fp32 128x128 block scales for FP8)."""
+    if wdtype == "fp8":
+        return 3 * H * I + 3 * (H // 128) * (I // 128) * 4
+    return 3 * H * I * 2
+
+
+def gate_up_bytes(T: int, k: int, H: int, I: int, touched: int, wdtype: str = "fp8") -> int:
+    """Algorithmic bytes of the routed gate/up launch: the gate and up weights of every touched
+    expert once, every token's activation row once, and the bf16 intermediate h written once."""
+    w = 2 * H * I + 2 * (H // 128) * (I // 128) * 4 if wdtype == "fp8" else 2 * H * I * 2
+    return touched * w + T * H * 2 + T * k * I * 2
+
+
+def gate_up_flops(T: int, k: int, H: int, I: int) -> int:
+    return 2 * 2 * T * k * H * I
+
+
+def layer_bytes(T, H, I, E, k, touched, wdtype="fp8", shared=True) -> int:
+    """Algorithmic bytes of the layer: touched experts' weights + the shared expert's, x read,
+    out written, router scores read, top-k ids and weights."""
+    eb = expert_bytes(H, I, wdtype)
+    return touched * eb + (eb if shared else 0) + 2 * T * H * 2 + T * E * 4 + T * k * 8
+
+
+def layer_flops(T, H, I, k, shared=True) -> int:
+    """2 FLOP per weight per token row over the three matrices (routed rows + shared rows)."""
+    return (T * k + (T if shared else 0)) * 6 * H * I
+
+
+# ------------------------------------------------------------------ counter-derived traffic
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "routed_expert_grouped_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per launch of the gate/up kernel from the committed rocprofv3 counter summary,
+    or None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"gate_up_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("traffic_bytes")
+
+
+# ------------------------------------------------------------------ timing
+
+def time_layer(layer, steps: int, warmup: int):
+    import torch
+
+    import routed_expert_grouped_amd as moe
+
+    L = moe.MoeLayer(layer.T, layer.H, layer.I, layer.E, layer.k, layer.experts, layer.shared,
+                     layer.score_fn, layer.renorm)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        L.forward(layer.scores, layer.x)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        L.forward(layer.scores, layer.x, gate_up_events=ev[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    gu_ms = [a.elapsed_time(b) for a, b in ev]
+    counts = L.counts.cpu().numpy()
+    return dict(total_ms=total_ms, wall_s=wall, gate_up_ms=sum(gu_ms) / len(gu_ms),
+                gate_up_ms_min=min(gu_ms), counts=counts)
+
+
+def cpu_baseline(layer, rows, n_threads: int):
+    """The oracle on `rows` of the same layer, wall-clock on the host (inputs copied first)."""
+    import numpy as np
+
+    import oracle
+    import routed_expert_grouped_amd as moe
+
+    ids, _ = moe.moe_route(layer.scores, layer.k, layer.score_fn, layer.renorm)
+    used = sorted(set(ids.cpu().numpy()[rows].ravel().tolist()))
+    slot = np.full(layer.E, -1, np.int32)
+    slot[used] = np.arange(len(used), dtype=np.int32)
+    import dataclasses
+
+    host = dataclasses.replace(layer, scores=layer.scores.cpu(), x=layer.x.cpu(),
+                               experts=layer.experts.select(used), shared=layer.shared.to("cpu"))
+    oracle.lib()
+    t = time.perf_counter()
+    oracle.moe_layer(host, rows=rows, expert_slot=slot, n_threads=n_threads)
+    dt = time.perf_counter() - t
+    return dt, oracle.max_threads(n_threads)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def run_workload(name: str, steps: int, warmup: int, seed: int = 0):
+    import synth
+
+    layer = synth.make_layer(name, seed=seed, device="cuda")
+    r = time_layer(layer, steps, warmup)
+    T, H, I, E, k = layer.T, layer.H, layer.I, layer.E, layer.k
+    touched = int((r["counts"] > 0).sum())
+    ms = r["total_ms"] / steps
+    lb = layer_bytes(T, H, I, E, k, touched)
+    lf = layer_flops(T, H, I, k)
+    gb = gate_up_bytes(T, k, H, I, touched)
+    gf = gate_up_flops(T, k, H, I)
+    gu_s = r["gate_up_ms"] * 1e-3
+    bw = gb / gu_s / 1e9
+    tf = gf / gu_s / 1e12
+    bound = "hbm" if gb / (HBM_PEAK_GBS * 1e9) >= gf / (BF16_PEAK_TFLOPS * 1e12) else "mfma"
+    if bound == "hbm":
+        roof = dict(bound="hbm", achieved=round(bw, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(bw / HBM_PEAK_GBS, 4))
+    else:
+        roof = dict(bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(tf / BF16_PEAK_TFLOPS, 4))
+    roof.update(traffic=counter_traffic(name), kernel="gate_up (routed)",
+                kernel_ms=round(r["gate_up_ms"], 4), algorithmic_bytes=gb, algorithmic_flops=gf)
+    res = dict(
+        workload=name, T=T, tokens_per_s=T * steps / (r["total_ms"] * 1e-3), ms_per_step=ms,
+        touched_experts=touched, layer_bytes=lb, layer_flops=lf,
+        layer_hbm_frac=round(lb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+        layer_bf16_mfma_frac=round(lf / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+        layer_fp8_mfma_frac=round(lf / (ms * 1e-3) / (FP8_PEAK_TFLOPS * 1e12), 4),
+        roofline=roof, wall_s=r["wall_s"])
+    return layer, res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_decode")
+    ap.add_argument("--prefill", default="dsv3_prefill", help="second workload ('' to skip)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-threads", type=int, default=int(os.environ.get("OMP_NUM_THREADS", "0") or 0))
+    a = ap.parse_args(argv)
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    torch.cuda.set_device(0)
+    layer, main_res = run_workload(a.workload, a.steps, a.warmup)
+    cpu = None
+    if not a.no_cpu:
+        rows = list(range(layer.T))  # the decode layer has 16 tokens: the sample is all of them
+        dt, threads = cpu_baseline(layer, rows, a.cpu_threads)
+        cpu = dict(value=round(len(rows) / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
+                   sample=f"{len(rows)} tokens of the {a.workload} layer (all experts they select "
+                          f"+ shared), {dt:.2f} s wall", cpu=cpu_model())
+    del layer
+    prefill = None
+    if a.prefill:
+        torch.cuda.empty_cache()
+        _, prefill = run_workload(a.prefill, max(3, a.steps // 2), max(1, a.warmup // 2))
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["tokens_per_s"], 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": a.workload, "T": main_res["T"], "H": 7168, "I": 2048, "E": 256,
+                   "k": 8, "weights": "fp8_e4m3fn, fp32 128x128 block scales",
+                   "activations": "bf16", "accumulate": "fp32", "shared_experts": 1,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": main_res["roofline"],
+        "cpu_baseline": cpu,
+        "layer": {k: main_res[k] for k in ("touched_experts", "layer_bytes", "layer_flops",
+                                           "layer_hbm_frac", "layer_bf16_mfma_frac",
+                                           "layer_fp8_mfma_frac")},
+        "prefill": None if prefill is None else {
+            k: (round(v, 4) if isinstance(v, float) else v) for k, v in prefill.items()},
+    }
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
