@@ -191,6 +191,9 @@ def main(argv=None):
     ap.add_argument("--prefill", default="dsv3_prefill", help="second workload ('' to skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-threads", type=int, default=int(os.environ.get("OMP_NUM_THREADS", "0") or 0))
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB 5 times (a known-size "
+                         "kernel that calibrates the HBM byte counters of a profiler run)")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -200,6 +203,13 @@ def main(argv=None):
     import torch
 
     torch.cuda.set_device(0)
+    if a.copy_probe_mib:
+        src = torch.empty(a.copy_probe_mib << 18, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     layer, main_res = run_workload(a.workload, a.steps, a.warmup)
     cpu = None
     if not a.no_cpu:

@@ -25,12 +25,13 @@ namespace moe {
 
 // One workgroup = 4 waves; each wave owns two 16-row weight groups (phase 1: the same 16 rows
 // of gate and of up; phase 2: 32 consecutive rows of down) over the full K, for one m-tile of
-// up to 16 grouped rows.
-template <bool kFP8, int kPhase>
+// up to 16 grouped rows.  kGrouped = false is the identity grouping (shared expert).
+template <bool kFP8, int kPhase, bool kGrouped>
 __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs a) {
     Tile tile;
     const int n_tiles = a.N / (kPhase == 1 ? kGemvColsP1 : kGemvColsP2);
-    if (!find_tile(a.offsets, a.n_groups, a.rows, kGemvBM, n_tiles, tile)) return;
+    if (!find_tile(kGrouped ? a.offsets : nullptr, a.n_groups, a.rows, kGemvBM, n_tiles, tile))
+        return;
 
     const int lane = lane_id(), wave = (int)(threadIdx.x >> 6);
     const int m = lane & 15, kq = lane >> 4;
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs a) {
     const uint16_t* arow = nullptr;
     if (valid) {
         if (kPhase == 1) {
-            const int tok = a.perm ? a.perm[p] / a.k : p;
+            const int tok = kGrouped ? a.perm[p] / a.k : p;
             arow = a.act + (size_t)tok * K;
         } else {
             arow = a.act + (size_t)p * K;
@@ -170,13 +171,16 @@ static moe_status launch_phase(int phase, const GemmArgs& a, int rows_per_group_
     const int cols = phase == 1 ? kGemvColsP1 : kGemvColsP2;
     const int64_t wgs = (int64_t)max_mtiles(a.rows, a.offsets ? a.n_groups : 1, kGemvBM) * (a.N / cols);
     const dim3 grid((unsigned)((wgs + 7) & ~int64_t(7))), block(256);
+#define MOE_GEMV(F, P, G) gemv_kernel<F, P, G><<<grid, block, 0, st>>>(a)
+    const bool g = a.offsets != nullptr;
     if (phase == 1) {
-        if (fp8) gemv_kernel<true, 1><<<grid, block, 0, st>>>(a);
-        else gemv_kernel<false, 1><<<grid, block, 0, st>>>(a);
+        if (fp8) g ? MOE_GEMV(true, 1, true) : MOE_GEMV(true, 1, false);
+        else g ? MOE_GEMV(false, 1, true) : MOE_GEMV(false, 1, false);
     } else {
-        if (fp8) gemv_kernel<true, 2><<<grid, block, 0, st>>>(a);
-        else gemv_kernel<false, 2><<<grid, block, 0, st>>>(a);
+        if (fp8) g ? MOE_GEMV(true, 2, true) : MOE_GEMV(true, 2, false);
+        else g ? MOE_GEMV(false, 2, true) : MOE_GEMV(false, 2, false);
     }
+#undef MOE_GEMV
     return launch_status();
 }
 

@@ -144,15 +144,20 @@ def quantize_fp8_blocks(w: torch.Tensor):
     return q.view(torch.uint8).reshape(*lead, N, K).contiguous(), s.contiguous()
 
 
+CHUNK = 16  # experts drawn per generator call
+
+
 def _expert_weights(n: int, H: int, I: int, wdtype: str, seed: int, stream0: int, device) -> ExpertWeights:
-    """n experts; expert j draws its three matrices from streams (stream0 + j, 0..2)."""
+    """n experts, drawn in chunks of CHUNK experts: chunk c draws its gate, up and down tensors
+    [m, rows, cols] from streams (stream0 + c, 0..2)."""
     gate, up, down, sg, su, sd = [], [], [], [], [], []
-    for j in range(n):
+    for c0 in range(0, n, CHUNK):
+        m_ = min(CHUNK, n - c0)
         mats = []
         for m, shape in enumerate(((I, H), (I, H), (H, I))):
             g = torch.Generator(device=device)
-            g.manual_seed(_seed(seed, stream0 + j, m))
-            w = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * 0.02
+            g.manual_seed(_seed(seed, stream0 + c0, m))
+            w = torch.randn((m_, *shape), generator=g, device=device, dtype=torch.float32) * 0.02
             mats.append(w)
         if wdtype == "fp8":
             (qg, s_g), (qu, s_u), (qd, s_d) = (quantize_fp8_blocks(w) for w in mats)
@@ -162,7 +167,7 @@ def _expert_weights(n: int, H: int, I: int, wdtype: str, seed: int, stream0: int
         else:
             raise ValueError(wdtype)
         del mats
-    st = lambda xs: torch.stack(xs).contiguous() if xs else None
+    st = lambda xs: torch.cat(xs).contiguous() if xs else None
     return ExpertWeights(wdtype, st(gate), st(up), st(down), st(sg), st(su), st(sd))
 
 
