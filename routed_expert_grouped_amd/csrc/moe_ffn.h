@@ -32,12 +32,9 @@ constexpr int kGemvBM = 16;
 constexpr int kGemvColsP1 = 64;   // 4 waves x 16 h-columns (16 gate + 16 up rows each)
 constexpr int kGemvColsP2 = 128;  // 4 waves x 32 y-columns
 
-// The grouped-GEMV kernel serves every shape for now.
-inline bool use_gemv(int rows, int n_groups) {
-    (void)rows;
-    (void)n_groups;
-    return true;
-}
+// Few rows per expert (decode): stream the weights with 16-row m-tiles; many rows (prefill):
+// 128-row LDS-staged GEMM tiles, which read each expert's weights once per 128 rows.
+inline bool use_gemv(int rows, int n_groups) { return rows <= 32 * n_groups; }
 
 moe_status launch_gemm(int phase, const GemmArgs& a, hipStream_t st);
 
