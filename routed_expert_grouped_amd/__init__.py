@@ -169,14 +169,16 @@ def moe_combine(y, inv, topk_w, shared_y, T: int, k: int, H: int, out=None, stre
 
 
 class MoeLayer:
-    """Buffers and the call sequence of one MoE layer forward (route -> permute -> routed
-    gate/up -> routed down -> shared expert -> combine), all on one stream.
+    """Buffers and the call sequence of one MoE layer forward: route -> permute -> routed
+    gate/up -> routed down -> combine on the caller's stream, and the shared expert (which only
+    needs x) on a second stream that runs alongside the routed experts and joins before combine.
 
     `experts` and `shared` are objects accepted by expert_weights(); `x` is bf16 bits [T, H]
     (torch.int16) and `scores` fp32 [T, E], all on the GPU.
     """
 
-    def __init__(self, T, H, I, E, k, experts, shared, score_fn="sigmoid", renorm=1, device="cuda"):
+    def __init__(self, T, H, I, E, k, experts, shared, score_fn="sigmoid", renorm=1, device="cuda",
+                 overlap_shared=True):
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
         self.score_fn, self.renorm = score_fn, renorm
         self.w = expert_weights(experts)
@@ -194,11 +196,20 @@ class MoeLayer:
         self.sh_h = torch.empty((max(1, T), I), dtype=torch.int16, device=d)
         self.sh_y = torch.empty((max(1, T), H), dtype=torch.int16, device=d)
         self.out = torch.empty((max(1, T), H), dtype=torch.int16, device=d)
+        self.side = torch.cuda.Stream(device=d) if (overlap_shared and shared is not None) else None
 
     def forward(self, scores, x, stream=None, gate_up_events=None):
         """Enqueue the layer; returns `out` (bf16 bits [T, H]).  gate_up_events=(start, stop)
         records torch events around the routed gate/up kernel (for timing)."""
         T, k = self.T, self.k
+        main = torch.cuda.current_stream() if stream is None else stream
+        shared_y = None
+        if self.ws_ is not None and self.side is not None:
+            # shared expert on the side stream, ordered after everything already on `main`
+            self.side.wait_stream(main)
+            moe_expert_gate_up(x, 1, None, None, self.ws_, self.sh_h, self.side)
+            moe_expert_down(self.sh_h, T, 1, None, self.ws_, self.sh_y, self.side)
+            shared_y = self.sh_y
         moe_route(scores, k, self.score_fn, self.renorm, self.topk_ids, self.topk_w, stream)
         moe_permute(self.topk_ids, self.E, self.counts, self.offsets, self.perm, self.inv, stream)
         if gate_up_events is not None:
@@ -207,10 +218,11 @@ class MoeLayer:
         if gate_up_events is not None:
             gate_up_events[1].record(stream)
         moe_expert_down(self.h, T, k, self.offsets, self.w, self.y, stream)
-        shared_y = None
-        if self.ws_ is not None:
+        if self.ws_ is not None and self.side is None:
             moe_expert_gate_up(x, 1, None, None, self.ws_, self.sh_h, stream)
             moe_expert_down(self.sh_h, T, 1, None, self.ws_, self.sh_y, stream)
             shared_y = self.sh_y
+        elif self.side is not None:
+            main.wait_stream(self.side)
         moe_combine(self.y, self.inv, self.topk_w, shared_y, T, k, self.H, self.out, stream)
         return self.out

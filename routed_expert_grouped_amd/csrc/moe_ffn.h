@@ -27,10 +27,13 @@ struct GemmArgs {
     uint16_t* out;  // [rows][N]
 };
 
-// gemv shape: m-tiles of 16 rows; output columns per workgroup in each phase.
+// gemv shape: m-tiles of 16 rows; kGemvWaves waves per workgroup, each wave owning 16 h-columns
+// (phase 1: 16 gate + 16 up rows) or 32 y-columns (phase 2).
 constexpr int kGemvBM = 16;
-constexpr int kGemvColsP1 = 64;   // 4 waves x 16 h-columns (16 gate + 16 up rows each)
-constexpr int kGemvColsP2 = 128;  // 4 waves x 32 y-columns
+#ifndef MOE_GEMV_WAVES
+#define MOE_GEMV_WAVES 4
+#endif
+constexpr int kGemvWaves = MOE_GEMV_WAVES;
 
 // Few rows per expert (decode): stream the weights with 16-row m-tiles; many rows (prefill):
 // 128-row LDS-staged GEMM tiles, which read each expert's weights once per 128 rows.

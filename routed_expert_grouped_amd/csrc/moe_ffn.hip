@@ -23,122 +23,137 @@
 
 namespace moe {
 
-// One workgroup = 4 waves; each wave owns two 16-row weight groups (phase 1: the same 16 rows
-// of gate and of up; phase 2: 32 consecutive rows of down) over the full K, for one m-tile of
-// up to 16 grouped rows.  kGrouped = false is the identity grouping (shared expert).
-template <bool kFP8, int kPhase, bool kGrouped>
-__global__ __launch_bounds__(256) void gemv_kernel(GemmArgs a) {
+// One workgroup = kWaves waves; each wave owns two 16-row weight groups (phase 1: the same 16
+// rows of gate and of up; phase 2: 32 consecutive rows of down) over the full K, for one m-tile
+// of up to 16 grouped rows.  kGrouped = false is the identity grouping (shared expert).
+//
+// HBM access: a wave's load instruction covers 8 weight rows x 128 contiguous bytes (whole
+// cache lines; 16 rows x 64 B per instruction, the MFMA operand layout, reaches only ~75% of the
+// bandwidth).  Each block goes through the wave's private LDS rows once to change from that
+// load layout to the MFMA operand layout (no workgroup barrier: a wave's LDS operations
+// complete in order).  The K loop keeps two 128-blocks of loads in flight (2-stage ring).
+template <bool kFP8, int kPhase, bool kGrouped, int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
+    constexpr int kWaveCols = kPhase == 1 ? 16 : 32;  // output columns per wave
+    constexpr int kCols = kWaves * kWaveCols;
+    constexpr int kRowB = kFP8 ? 128 : 256;           // bytes of one weight row per 128-block
+    constexpr int kLD = kRowB + 16;                   // LDS row stride: conflict-free reads
+    constexpr int kLPR = kRowB / 16;                  // lanes per row in a load instruction
+    constexpr int kRPI = 64 / kLPR;                   // rows per load instruction
+    constexpr int kIns = 16 / kRPI;                   // load instructions per 16-row group
+    __shared__ __attribute__((aligned(16))) uint8_t sW[kWaves][2 * 16 * kLD];
+
     Tile tile;
-    const int n_tiles = a.N / (kPhase == 1 ? kGemvColsP1 : kGemvColsP2);
+    const int n_tiles = a.N / kCols;
     if (!find_tile(kGrouped ? a.offsets : nullptr, a.n_groups, a.rows, kGemvBM, n_tiles, tile))
         return;
 
-    const int lane = lane_id(), wave = (int)(threadIdx.x >> 6);
+    const int lane = lane_id(), wave = uniform((int)(threadIdx.x >> 6));
     const int m = lane & 15, kq = lane >> 4;
     const int K = a.K;
     const int e = tile.group;
     const int p = tile.row0 + m;
     const bool valid = p < tile.row1;
+    uint8_t* lds = sW[wave];
 
-    // activation row of this lane's M index
-    const uint16_t* arow = nullptr;
-    if (valid) {
-        if (kPhase == 1) {
-            const int tok = kGrouped ? a.perm[p] / a.k : p;
-            arow = a.act + (size_t)tok * K;
-        } else {
-            arow = a.act + (size_t)p * K;
-        }
-    }
-    // weight rows of this lane's N index, in both groups
-    const int n0 = tile.nt * (kPhase == 1 ? kGemvColsP1 : kGemvColsP2) +
-                   wave * (kPhase == 1 ? 16 : 32);
+    // activation row of this lane's M index.  Lanes past the m-tile's last row read the tile's
+    // first row instead: MFMA output rows depend only on their own A row, and those rows are
+    // never stored, so the loads stay unconditional (exact load counters, no branches).
+    const int pa = valid ? p : tile.row0;
+    const int ra = (kPhase == 1 && kGrouped) ? a.perm[pa] / a.k : pa;
+    const uint16_t* arow = a.act + (size_t)ra * K;
+    // weight rows: load layout row lrow (+ kRPI per instruction), 16-byte chunk lchunk
+    const int n0 = tile.nt * kCols + wave * kWaveCols;
     const size_t esz = kFP8 ? 1 : 2;
-    const uint8_t* w0;
-    const uint8_t* w1;
+    const int kblocks = K / 128;
+    const int lrow = lane / kLPR, lchunk = lane % kLPR;
+    const uint8_t* g0 = (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + lrow) * K * esz + lchunk * 16;
+    const uint8_t* g1 = kPhase == 1
+        ? (const uint8_t*)a.w1 + ((size_t)e * a.N + n0 + lrow) * K * esz + lchunk * 16
+        : (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + 16 + lrow) * K * esz + lchunk * 16;
+    const size_t ins_stride = (size_t)kRPI * K * esz;  // bytes between a group's instructions
     const float* s0 = nullptr;
     const float* s1 = nullptr;
-    const int kblocks = K / 128;
-    if (kPhase == 1) {
-        w0 = (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + m) * K * esz;
-        w1 = (const uint8_t*)a.w1 + ((size_t)e * a.N + n0 + m) * K * esz;
-        if (kFP8) {
-            s0 = a.s0 + ((size_t)e * (a.N / 128) + n0 / 128) * kblocks;
-            s1 = a.s1 + ((size_t)e * (a.N / 128) + n0 / 128) * kblocks;
-        }
-    } else {
-        w0 = (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + m) * K * esz;
-        w1 = (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + 16 + m) * K * esz;
-        if (kFP8) {
-            s0 = a.s0 + ((size_t)e * (a.N / 128) + n0 / 128) * kblocks;
-            s1 = s0;
-        }
+    if (kFP8) {
+        s0 = a.s0 + ((size_t)e * (a.N / 128) + n0 / 128) * kblocks;
+        s1 = kPhase == 1 ? a.s1 + ((size_t)e * (a.N / 128) + n0 / 128) * kblocks : s0;
     }
 
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    constexpr int kWVec = kFP8 ? 2 : 4;  // 16-byte vectors of weights per lane per 128-block
-    u32x4 b0[kWVec], b1[kWVec], xa[4];
-    auto load = [&](int kb) {
-        const int k0 = kb * 128 + kq * 32;  // this lane's 32 K values of the block
-        const u32x4* q0 = (const u32x4*)(w0 + (size_t)k0 * esz);
-        const u32x4* q1 = (const u32x4*)(w1 + (size_t)k0 * esz);
+    u32x4 b0[2][kIns], b1[2][kIns], xa[2][4];
+    float sg0[2], sg1[2];  // block scales of the staged blocks (wave-uniform)
+    auto load = [&](int kb, int st) {
+        sg0[st] = kFP8 ? s0[kb] : 1.0f;
+        sg1[st] = kFP8 ? s1[kb] : 1.0f;
+        const size_t kofs = (size_t)kb * kRowB;
 #pragma unroll
-        for (int i = 0; i < kWVec; ++i) {
-            b0[i] = __builtin_nontemporal_load(q0 + i);
-            b1[i] = __builtin_nontemporal_load(q1 + i);
+        for (int i = 0; i < kIns; ++i) {
+            b0[st][i] = __builtin_nontemporal_load((const u32x4*)(g0 + i * ins_stride + kofs));
+            b1[st][i] = __builtin_nontemporal_load((const u32x4*)(g1 + i * ins_stride + kofs));
         }
-        if (valid) {
-            const u32x4* xr = (const u32x4*)(arow + k0);
+        const u32x4* xr = (const u32x4*)(arow + kb * 128 + kq * 32);  // this lane's 32 K values
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xa[i] = xr[i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xa[i] = u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int i = 0; i < 4; ++i) xa[st][i] = xr[i];
     };
-    load(0);
-    for (int kb = 0; kb < kblocks; ++kb) {
-        u32x4 cb0[kWVec], cb1[kWVec], cx[4];
+    auto compute = [&](int st) {
+        // load layout -> LDS rows -> MFMA layout (lane: row m, bytes [kq*32*esz, +32*esz))
 #pragma unroll
-        for (int i = 0; i < kWVec; ++i) {
-            cb0[i] = b0[i];
-            cb1[i] = b1[i];
+        for (int i = 0; i < kIns; ++i) {
+            *(u32x4*)&lds[(i * kRPI + lrow) * kLD + lchunk * 16] = b0[st][i];
+            *(u32x4*)&lds[(16 + i * kRPI + lrow) * kLD + lchunk * 16] = b1[st][i];
         }
+        constexpr int kV = kFP8 ? 2 : 4;  // 16-byte vectors per lane per group
+        u32x4 r0[kV], r1[kV];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cx[i] = xa[i];
-        if (kb + 1 < kblocks) load(kb + 1);
+        for (int i = 0; i < kV; ++i) {
+            r0[i] = *(const u32x4*)&lds[m * kLD + kq * 32 * esz + i * 16];
+            r1[i] = *(const u32x4*)&lds[(16 + m) * kLD + kq * 32 * esz + i * 16];
+        }
         f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            bf16x8 g0, g1;
+            bf16x8 w0v, w1v;
             if (kFP8) {
-                const uint32_t* u0 = (const uint32_t*)cb0;
-                const uint32_t* u1 = (const uint32_t*)cb1;
-                g0 = fp8x8_to_bf16x8(u0[2 * i], u0[2 * i + 1]);
-                g1 = fp8x8_to_bf16x8(u1[2 * i], u1[2 * i + 1]);
+                const uint32_t* u0 = (const uint32_t*)r0;
+                const uint32_t* u1 = (const uint32_t*)r1;
+                w0v = fp8x8_to_bf16x8(u0[2 * i], u0[2 * i + 1]);
+                w1v = fp8x8_to_bf16x8(u1[2 * i], u1[2 * i + 1]);
             } else {
-                g0 = as_bf16x8(cb0[i]);
-                g1 = as_bf16x8(cb1[i]);
+                w0v = as_bf16x8(r0[i]);
+                w1v = as_bf16x8(r1[i]);
             }
-            const bf16x8 xv = as_bf16x8(cx[i]);
-            p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, g0, p0, 0, 0, 0);
-            p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, g1, p1, 0, 0, 0);
+            const bf16x8 xv = as_bf16x8(xa[st][i]);
+            p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w0v, p0, 0, 0, 0);
+            p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w1v, p1, 0, 0, 0);
         }
-        if (kFP8) {
-            const float sc0 = s0[kb], sc1 = s1[kb];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                acc0[r] = fmaf(p0[r], sc0, acc0[r]);
-                acc1[r] = fmaf(p1[r], sc1, acc1[r]);
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                acc0[r] += p0[r];
-                acc1[r] += p1[r];
-            }
+        for (int r = 0; r < 4; ++r) {
+            acc0[r] = fmaf(p0[r], sg0[st], acc0[r]);
+            acc1[r] = fmaf(p1[r], sg1[st], acc1[r]);
         }
+    };
+    // 2-stage ring: two blocks in flight.  The steady-state loop issues its loads without
+    // conditions so the compiler's load counters wait only for the block being used; the tail
+    // (1 to 3 blocks) is peeled.  With a single block, stage 1 reloads block 0 (unused).
+    // (scheduling barriers keep each block's loads after the MFMAs of the block they replace)
+    load(0, 0);
+    load(kblocks > 1 ? 1 : 0, 1);
+    int kb = 0;
+    for (; kb + 3 < kblocks; kb += 2) {
+        compute(0);
+        __builtin_amdgcn_sched_barrier(0);
+        load(kb + 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1);
+        __builtin_amdgcn_sched_barrier(0);
+        load(kb + 3, 1);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    const int rest = kblocks - kb;  // 1, 2 or 3
+    compute(0);
+    if (rest == 3) load(kb + 2, 0);
+    if (rest >= 2) compute(1);
+    if (rest == 3) compute(0);
 
     // D layout of the 16x16 MFMA: lane holds rows 4*(lane/16)+r (grouped rows), column lane%16
 #pragma unroll
@@ -162,22 +177,20 @@ static int max_mtiles(int rows, int n_groups, int BM) {
 }
 
 // Launch one phase.  rows = grouped rows (T*k).
-static moe_status launch_phase(int phase, const GemmArgs& a, int rows_per_group_hint,
-                               hipStream_t st) {
-    const bool fp8 = a.fp8;
-    const bool gemv = use_gemv(a.rows, a.n_groups);
-    (void)rows_per_group_hint;
-    if (!gemv) return launch_gemm(phase, a, st);
-    const int cols = phase == 1 ? kGemvColsP1 : kGemvColsP2;
+static moe_status launch_phase(int phase, const GemmArgs& a, hipStream_t st) {
+    if (!use_gemv(a.rows, a.n_groups)) return launch_gemm(phase, a, st);
+    constexpr int W = kGemvWaves;
+    const int cols = W * (phase == 1 ? 16 : 32);
     const int64_t wgs = (int64_t)max_mtiles(a.rows, a.offsets ? a.n_groups : 1, kGemvBM) * (a.N / cols);
-    const dim3 grid((unsigned)((wgs + 7) & ~int64_t(7))), block(256);
-#define MOE_GEMV(F, P, G) gemv_kernel<F, P, G><<<grid, block, 0, st>>>(a)
+    if (wgs > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    const dim3 grid((unsigned)((wgs + 7) & ~int64_t(7))), block(W * 64);
+#define MOE_GEMV(F, P, G) gemv_kernel<F, P, G, W><<<grid, block, 0, st>>>(a)
     const bool g = a.offsets != nullptr;
     if (phase == 1) {
-        if (fp8) g ? MOE_GEMV(true, 1, true) : MOE_GEMV(true, 1, false);
+        if (a.fp8) g ? MOE_GEMV(true, 1, true) : MOE_GEMV(true, 1, false);
         else g ? MOE_GEMV(false, 1, true) : MOE_GEMV(false, 1, false);
     } else {
-        if (fp8) g ? MOE_GEMV(true, 2, true) : MOE_GEMV(true, 2, false);
+        if (a.fp8) g ? MOE_GEMV(true, 2, true) : MOE_GEMV(true, 2, false);
         else g ? MOE_GEMV(false, 2, true) : MOE_GEMV(false, 2, false);
     }
 #undef MOE_GEMV
@@ -212,7 +225,7 @@ extern "C" moe_status moe_expert_gate_up(const uint16_t* x, int32_t T, int32_t k
     a.s1 = w->s_up;
     a.fp8 = w->dtype == MOE_W_FP8_E4M3_B128;
     a.out = h;
-    return launch_phase(1, a, 0, as_stream(stream));
+    return launch_phase(1, a, as_stream(stream));
 }
 
 extern "C" moe_status moe_expert_down(const uint16_t* h, int32_t T, int32_t k,
@@ -239,7 +252,7 @@ extern "C" moe_status moe_expert_down(const uint16_t* h, int32_t T, int32_t k,
     a.s1 = nullptr;
     a.fp8 = w->dtype == MOE_W_FP8_E4M3_B128;
     a.out = y;
-    return launch_phase(2, a, 0, as_stream(stream));
+    return launch_phase(2, a, as_stream(stream));
 }
 
 extern "C" moe_status moe_expert_ffn_workspace_size(int32_t T, int32_t k,

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
     const int n_tiles = a.N / kCols;
     if (!find_tile(kGrouped ? a.offsets : nullptr, a.n_groups, a.rows, kBM, n_tiles, tile)) return;
 
-    const int tid = (int)threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int tid = (int)threadIdx.x, lane = lane_id(), wave = uniform(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int e = tile.group;
     const int c0 = tile.nt * kCols;
