@@ -63,6 +63,7 @@ typedef enum {
 /* Kernel limits of this build. */
 #define MOE_MAX_EXPERTS 1024 /* E (and n_groups) */
 #define MOE_MAX_TOPK 32      /* k */
+#define MOE_MAX_DIM 16384    /* H and I */
 
 /* Weights of n_groups experts of one layer, in nn.Linear layout (rows = outputs, the input
  * dimension contiguous) [OSDI "native FP8 GEMV"; A2 4.2 for the 7168 x 2048 shape]:
@@ -126,7 +127,8 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
  *   h       : bf16 [T*k][I] out, in grouped order.
  * Rows of experts with no assignment cost nothing: their weights are not read.
  * Errors: INVALID_ARG for null pointers, T < 0, k < 1, inconsistent identity grouping, unknown
- * dtype; UNSUPPORTED when H or I is not a multiple of 128 or n_groups > MOE_MAX_EXPERTS. */
+ * dtype; UNSUPPORTED when H or I is not a multiple of 128, H or I > MOE_MAX_DIM, or
+ * n_groups > MOE_MAX_EXPERTS. */
 moe_status moe_expert_gate_up(const uint16_t* x, int32_t T, int32_t k, const int32_t* perm,
                               const int32_t* offsets, const moe_expert_weights* w, uint16_t* h,
                               void* stream);

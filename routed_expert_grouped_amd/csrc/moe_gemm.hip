@@ -5,30 +5,41 @@
 // computes one m-tile against 128 weight rows over the whole K:
 //   phase 1: 64 gate rows + the same 64 up rows -> 64 columns of h = SiLU(gate) * up
 //   phase 2: 128 down rows -> 128 columns of y
-// Per 128-long K block (one FP8 scale block) the workgroup stages the activation tile (gathered
-// through the grouping for phase 1) and the weight tile in LDS -- the FP8 codes expanded exactly
-// to bf16 on the way in -- then 4 waves (2 x 2, 64 x 64 each) run MFMA 32x32x16 chains into a
-// per-block partial that is multiplied by the block's scale into the fp32 accumulator (the
-// post-scaling of the OSDI'26 article's FP8 GEMV, section "native FP8 GEMV", Figures 9-10).
-// The next block's global loads are issued before the current block's MFMAs, and two
-// workgroups share a CU (69.6 KB of LDS each) so one computes while the other waits at a
-// barrier.
+//
+// Per 128-long K block (= one FP8 scale block) the workgroup stages in LDS the activation tile
+// (128 rows x 128 bf16, gathered through the grouping in phase 1) and the weight tile (128 rows
+// x 128 FP8 codes, kept as codes), both loaded as whole 128-byte lines.  Four waves (2 x 2) then
+// run MFMA 32x32x16 chains: each wave owns 2 of the 4 32-row m-subtiles (interleaved, so a
+// partly filled tile still spreads over both wave rows) and 2 32-row weight subtiles (phase 1:
+// matching gate and up rows, so SiLU(gate)*up is formed in registers).  Weight fragments are
+// expanded exactly from FP8 to bf16 as they leave LDS; each block's chain goes into a partial
+// sum that is multiplied by the block's scale into the fp32 accumulator (the post-scaling of
+// the OSDI'26 article's FP8 GEMV, section "native FP8 GEMV", Figures 9-10).  Subtiles past the
+// last row are skipped.  Two workgroups share a CU, so one computes while the other stages.
 #include "libmoe.h"
 #include "moe_device.h"
 #include "moe_ffn.h"
 #include "moe_host.h"
 
+#include <type_traits>
+
 namespace moe {
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kBK = 128;
-constexpr int kLD = kBK + 8;  // LDS row stride (bf16 elements): 272 B keeps 16-lane reads conflict-free
+constexpr int kBM = 128;            // rows per m-tile
+constexpr int kBN = 128;            // weight rows per tile
+constexpr int kBK = 128;            // K per block (one scale block)
+constexpr int kLDA = kBK * 2 + 16;  // A row stride in LDS (bytes): 16-lane b128 reads hit distinct banks
+constexpr int kMaxKBlocks = 128;    // K <= 16384 (block scales are staged in LDS)
 
 template <bool kFP8, int kPhase, bool kGrouped>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[kBM * kLD];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[kBN * kLD];
+    constexpr int kRowB = kFP8 ? kBK : kBK * 2;    // bytes of one weight row per block
+    constexpr int kLDB = kRowB + (kFP8 ? 8 : 16);  // B row stride (bytes)
+    constexpr int kBLanes = kRowB / 16;            // threads per weight row
+    constexpr int kBPer = kBN * kBLanes / 256;     // 16-byte B chunks per thread
+    __shared__ __attribute__((aligned(16))) uint8_t sA[kBM * kLDA];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[kBN * kLDB];
+    __shared__ float sScale[2][kMaxKBlocks];
 
     constexpr int kCols = kPhase == 1 ? kBN / 2 : kBN;  // output columns per tile
     Tile tile;
@@ -40,26 +51,24 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
     const int e = tile.group;
     const int c0 = tile.nt * kCols;
     const int K = a.K, kblocks = K / kBK;
-    const size_t esz = kFP8 ? 1 : 2;
+    const int fr = lane & 31, half = lane >> 5;
 
-    // ---- staging assignment: A chunk i -> row tid/16 + 16i, 8 bf16 at column (tid%16)*8
-    const uint16_t* arow[8];
+    // ---- activation staging: thread -> 16-byte chunk (tid % 16) of rows tid/16 + 16i.
+    // Rows past the end of the m-tile load the tile's first row (never stored), so the loads
+    // are unconditional.
+    uint32_t arow[8];  // source row (token, or grouped row) of each staged row
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int p = tile.row0 + (tid >> 4) + 16 * i;
-        arow[i] = nullptr;
-        if (p < tile.row1) {
-            const int r = (kPhase == 1 && kGrouped) ? a.perm[p] / a.k : p;
-            arow[i] = a.act + (size_t)r * K + (tid & 15) * 8;
-        }
+        const int p0 = tile.row0 + (tid >> 4) + 16 * i;
+        const int p = p0 < tile.row1 ? p0 : tile.row0;
+        arow[i] = (uint32_t)((kPhase == 1 && kGrouped) ? a.perm[p] / a.k : p);
     }
-    // B chunks: fp8 -> row tid/8 + 32i, 16 codes at (tid%8)*16; bf16 -> row tid/16 + 16i, 8 at (tid%16)*8
-    constexpr int kBChunks = kFP8 ? 4 : 8;
-    const uint8_t* brow[kBChunks];
+    const uint16_t* abase = a.act + (tid & 15) * 8;
+    // ---- weight staging: thread -> 16-byte chunk (tid % kBLanes) of LDS rows tid/kBLanes + ...
+    const uint8_t* brow[kBPer];
 #pragma unroll
-    for (int i = 0; i < kBChunks; ++i) {
-        const int r = kFP8 ? (tid >> 3) + 32 * i : (tid >> 4) + 16 * i;  // LDS row 0..127
-        const int col = kFP8 ? (tid & 7) * 16 : (tid & 15) * 8;
+    for (int i = 0; i < kBPer; ++i) {
+        const int r = tid / kBLanes + (256 / kBLanes) * i;  // LDS row 0..127
         const uint8_t* base;
         int wr;
         if (kPhase == 1) {
@@ -69,52 +78,47 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
             base = (const uint8_t*)a.w0;
             wr = c0 + r;
         }
-        brow[i] = base + (((size_t)e * a.N + wr) * K + col) * esz;
+        brow[i] = base + ((size_t)e * a.N + wr) * (size_t)K * (kFP8 ? 1 : 2) + (tid % kBLanes) * 16;
+    }
+    // ---- block scales of this tile, staged once: gate and up (phase 1) or down (phase 2)
+    if (kFP8 && tid < kblocks) {
+        const size_t srow = ((size_t)e * (a.N / 128) + c0 / 128) * kblocks;
+        sScale[0][tid] = a.s0[srow + tid];
+        sScale[1][tid] = kPhase == 1 ? a.s1[srow + tid] : a.s0[srow + tid];
     }
 
-    u32x4 ra[8], rb[kBChunks];
+    u32x4 ra[8], rb[kBPer];
     auto load = [&](int kb) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            ra[i] = arow[i] ? *(const u32x4*)(arow[i] + kb * kBK) : u32x4{0u, 0u, 0u, 0u};
+            ra[i] = *(const u32x4*)(abase + (size_t)arow[i] * K + kb * kBK);
 #pragma unroll
-        for (int i = 0; i < kBChunks; ++i)
-            rb[i] = __builtin_nontemporal_load((const u32x4*)(brow[i] + (size_t)kb * kBK * esz));
+        for (int i = 0; i < kBPer; ++i)
+            rb[i] = __builtin_nontemporal_load((const u32x4*)(brow[i] + (size_t)kb * kRowB));
     };
     auto store = [&]() {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            *(u32x4*)&sA[((tid >> 4) + 16 * i) * kLD + (tid & 15) * 8] = ra[i];
+            *(u32x4*)&sA[((tid >> 4) + 16 * i) * kLDA + (tid & 15) * 16] = ra[i];
 #pragma unroll
-        for (int i = 0; i < kBChunks; ++i) {
-            if (kFP8) {
-                const int r = (tid >> 3) + 32 * i, col = (tid & 7) * 16;
-                const bf16x8 lo = fp8x8_to_bf16x8(rb[i][0], rb[i][1]);
-                const bf16x8 hi = fp8x8_to_bf16x8(rb[i][2], rb[i][3]);
-                *(bf16x8*)&sB[r * kLD + col] = lo;
-                *(bf16x8*)&sB[r * kLD + col + 8] = hi;
+        for (int i = 0; i < kBPer; ++i) {
+            uint8_t* dst = &sB[(tid / kBLanes + (256 / kBLanes) * i) * kLDB + (tid % kBLanes) * 16];
+            if (kFP8) {  // 8-byte aligned rows
+                *(uint64_t*)dst = ((uint64_t)rb[i][1] << 32) | rb[i][0];
+                *(uint64_t*)(dst + 8) = ((uint64_t)rb[i][3] << 32) | rb[i][2];
             } else {
-                const int r = (tid >> 4) + 16 * i, col = (tid & 15) * 8;
-                *(u32x4*)&sB[r * kLD + col] = rb[i];
+                *(u32x4*)dst = rb[i];
             }
         }
     };
 
-    // per-lane fragment rows in LDS
-    const int fr = lane & 31, fk = (lane >> 5) * 8;
-    int brow_l[2];
+    // subtiles of this wave: m-subtiles wm and wm + 2 (32 rows each); weight subtiles:
+    // phase 1 gate rows wn*32.. and up rows 64 + wn*32..; phase 2 rows wn*64.. and wn*64 + 32..
+    const int nvalid = (tile.row1 - tile.row0 + 31) >> 5;  // filled 32-row subtiles (1..4)
+    const int mine = (nvalid > wm) + (nvalid > wm + 2);     // this wave's filled subtiles (0..2)
+    int bsub[2];
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-        brow_l[ni] = kPhase == 1 ? ni * 64 + wn * 32 + fr : wn * 64 + ni * 32 + fr;
-
-    // block scales of this tile (phase 1: gate / up of block c0/128; phase 2: down of c0/128)
-    const float* sc0 = nullptr;
-    const float* sc1 = nullptr;
-    if (kFP8) {
-        const size_t srow = ((size_t)e * (a.N / 128) + c0 / 128) * kblocks;
-        sc0 = a.s0 + srow;
-        sc1 = kPhase == 1 ? a.s1 + srow : sc0;
-    }
+    for (int ni = 0; ni < 2; ++ni) bsub[ni] = kPhase == 1 ? ni * 64 + wn * 32 : wn * 64 + ni * 32;
 
     f32x16 acc[2][2];
 #pragma unroll
@@ -124,64 +128,81 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-    load(0);
-    for (int kb = 0; kb < kblocks; ++kb) {
-        __syncthreads();  // every wave is done reading the previous block
-        store();
-        __syncthreads();
-        if (kb + 1 < kblocks) load(kb + 1);
-        f32x16 part[2][2];
+    // weight subtile 0 uses scale 0 and subtile 1 scale 1 (phase 2 staged both equal)
+    auto compute = [&](int kb, auto nsub_tag) {
+        constexpr int NS = decltype(nsub_tag)::value;  // m-subtiles to compute (1 or 2)
+        f32x16 part[NS][2];
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < NS; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) part[mi][ni][r] = 0.0f;
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
-            bf16x8 fa[2], fb[2];
+            bf16x8 fa[NS], fb[2];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                fa[mi] = *(const bf16x8*)&sA[(wm * 64 + mi * 32 + fr) * kLD + kk * 16 + fk];
+            for (int mi = 0; mi < NS; ++mi)
+                fa[mi] = *(const bf16x8*)&sA[((wm + 2 * mi) * 32 + fr) * kLDA + (kk * 16 + half * 8) * 2];
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-                fb[ni] = *(const bf16x8*)&sB[brow_l[ni] * kLD + kk * 16 + fk];
+            for (int ni = 0; ni < 2; ++ni) {
+                const uint8_t* q = &sB[(bsub[ni] + fr) * kLDB];
+                if (kFP8) {
+                    const uint2 v = *(const uint2*)(q + kk * 16 + half * 8);
+                    fb[ni] = fp8x8_to_bf16x8(v.x, v.y);
+                } else {
+                    fb[ni] = *(const bf16x8*)(q + (kk * 16 + half * 8) * 2);
+                }
+            }
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
+            for (int mi = 0; mi < NS; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
                     part[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni],
                                                                            part[mi][ni], 0, 0, 0);
         }
-        const float s0 = kFP8 ? sc0[kb] : 1.0f;
-        const float s1 = kFP8 ? sc1[kb] : 1.0f;
+        const float s0 = kFP8 ? sScale[0][kb] : 1.0f;
+        const float s1 = kFP8 ? sScale[1][kb] : 1.0f;
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < NS; ++mi)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 acc[mi][0][r] = fmaf(part[mi][0][r], s0, acc[mi][0][r]);
                 acc[mi][1][r] = fmaf(part[mi][1][r], s1, acc[mi][1][r]);
             }
+    };
+
+    load(0);
+    for (int kb = 0; kb < kblocks; ++kb) {
+        __syncthreads();  // every wave is done reading the previous block (and the scales are in)
+        store();
+        __syncthreads();
+        if (kb + 1 < kblocks) load(kb + 1);
+        if (mine == 2)
+            compute(kb, std::integral_constant<int, 2>{});
+        else if (mine == 1)
+            compute(kb, std::integral_constant<int, 1>{});
     }
 
     // D layout of the 32x32 MFMA: value r of a lane is row 8*(r/4) + 4*(lane/32) + r%4 of the
-    // fragment, column lane%32
+    // subtile, column lane%32
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < 2; ++mi) {
+        if (mi >= mine) break;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int m = wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const int p = tile.row0 + m;
+            const int p = tile.row0 + (wm + 2 * mi) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
             if (p >= tile.row1) continue;
+            uint16_t* o = a.out + (size_t)p * a.N + c0 + fr;
             if (kPhase == 1) {
                 const float g = acc[mi][0][r], u = acc[mi][1][r];
-                a.out[(size_t)p * a.N + c0 + wn * 32 + fr] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+                o[wn * 32] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
             } else {
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    a.out[(size_t)p * a.N + c0 + wn * 64 + ni * 32 + fr] = f32_to_bf16(acc[mi][ni][r]);
+                o[wn * 64] = f32_to_bf16(acc[mi][0][r]);
+                o[wn * 64 + 32] = f32_to_bf16(acc[mi][1][r]);
             }
         }
+    }
 }
 
 moe_status launch_gemm(int phase, const GemmArgs& a, hipStream_t st) {
@@ -189,7 +210,7 @@ moe_status launch_gemm(int phase, const GemmArgs& a, hipStream_t st) {
     const int groups = a.offsets ? a.n_groups : 1;
     const int64_t mt = ((int64_t)a.rows + kBM - 1) / kBM + std::min<int64_t>(groups, a.rows);
     const int64_t wgs = mt * (a.N / cols);
-    if (wgs > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (wgs > INT32_MAX || a.K / kBK > kMaxKBlocks) return MOE_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((wgs + 7) & ~int64_t(7))), block(256);
     const bool g = a.offsets != nullptr;
 #define MOE_GEMM(F, P, G) gemm_kernel<F, P, G><<<grid, block, 0, st>>>(a)

@@ -33,6 +33,7 @@ inline moe_status check_weights(const moe_expert_weights* w) {
     if (!aligned16(w->w_gate) || !aligned16(w->w_up) || !aligned16(w->w_down))
         return MOE_ERR_INVALID_ARG;
     if (w->H % 128 != 0 || w->I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if (w->H > MOE_MAX_DIM || w->I > MOE_MAX_DIM) return MOE_ERR_UNSUPPORTED;
     if (w->n_groups > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }

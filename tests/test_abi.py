@@ -87,6 +87,8 @@ def test_expert_validation():
     assert gu(FAKE, 0, 2, FAKE, FAKE, ctypes.byref(bf16_no_scales), FAKE, None) == moe.MOE_OK
     odd = _w(H=200)
     assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(odd), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    huge = _w(H=16384 + 128)
+    assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(huge), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
     many = _w(n=2000)
     assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(many), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
     unaligned = _w(ptr=ctypes.c_void_p(0x1004))
