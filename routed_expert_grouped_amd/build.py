@@ -16,7 +16,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC,
          # packed fp32 VALU forms are kept out of the generated code
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in VGPRs: the block-scale FMAs read them without AGPR copies
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def sources():

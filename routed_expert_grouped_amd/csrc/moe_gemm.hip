@@ -11,8 +11,10 @@
 // x 128 FP8 codes, kept as codes), both loaded as whole 128-byte lines.  Four waves (2 x 2) then
 // run MFMA 32x32x16 chains: each wave owns 2 of the 4 32-row m-subtiles (interleaved, so a
 // partly filled tile still spreads over both wave rows) and 2 32-row weight subtiles (phase 1:
-// matching gate and up rows, so SiLU(gate)*up is formed in registers).  Weight fragments are
-// expanded exactly from FP8 to bf16 as they leave LDS; each block's chain goes into a partial
+// matching gate and up rows, so SiLU(gate)*up is formed in registers).  k-steps go in pairs
+// whose lane halves cover 16 consecutive K each, so one 16-byte LDS read of FP8 codes feeds two
+// MFMAs.  Weight fragments are expanded exactly from FP8 to bf16 as they leave LDS (the row
+// stride of 144 bytes keeps those reads free of bank conflicts); each block's chain goes into a partial
 // sum that is multiplied by the block's scale into the fp32 accumulator (the post-scaling of
 // the OSDI'26 article's FP8 GEMV, section "native FP8 GEMV", Figures 9-10).  Subtiles past the
 // last row are skipped.  Two workgroups share a CU, so one computes while the other stages.
@@ -34,7 +36,7 @@ constexpr int kMaxKBlocks = 128;    // K <= 16384 (block scales are staged in LD
 template <bool kFP8, int kPhase, bool kGrouped>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
     constexpr int kRowB = kFP8 ? kBK : kBK * 2;    // bytes of one weight row per block
-    constexpr int kLDB = kRowB + (kFP8 ? 8 : 16);  // B row stride (bytes)
+    constexpr int kLDB = kRowB + 16;               // B row stride (bytes): 16-aligned, conflict-free b128
     constexpr int kBLanes = kRowB / 16;            // threads per weight row
     constexpr int kBPer = kBN * kBLanes / 256;     // 16-byte B chunks per thread
     __shared__ __attribute__((aligned(16))) uint8_t sA[kBM * kLDA];
@@ -103,12 +105,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < kBPer; ++i) {
             uint8_t* dst = &sB[(tid / kBLanes + (256 / kBLanes) * i) * kLDB + (tid % kBLanes) * 16];
-            if (kFP8) {  // 8-byte aligned rows
-                *(uint64_t*)dst = ((uint64_t)rb[i][1] << 32) | rb[i][0];
-                *(uint64_t*)(dst + 8) = ((uint64_t)rb[i][3] << 32) | rb[i][2];
-            } else {
-                *(u32x4*)dst = rb[i];
-            }
+            *(u32x4*)dst = rb[i];
         }
     };
 
@@ -138,28 +135,44 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
             for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) part[mi][ni][r] = 0.0f;
+        // k-steps in pairs: for pair j, lane half h covers K elements [32j + 16h, +16) (first 8
+        // for step 2j, next 8 for step 2j+1) on both operands, so one b128 weight read feeds two
+        // MFMAs
+        constexpr int KP = kBK / 32;
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            bf16x8 fa[NS], fb[2];
+        for (int j = 0; j < KP; ++j) {
+            bf16x8 fa[2][NS];
+            u32x4 fbq[2];
+            bf16x8 fbh[2][2];
 #pragma unroll
-            for (int mi = 0; mi < NS; ++mi)
-                fa[mi] = *(const bf16x8*)&sA[((wm + 2 * mi) * 32 + fr) * kLDA + (kk * 16 + half * 8) * 2];
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int mi = 0; mi < NS; ++mi)
+                    fa[t][mi] = *(const bf16x8*)&sA[((wm + 2 * mi) * 32 + fr) * kLDA + (32 * j + 16 * half + 8 * t) * 2];
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni) {
                 const uint8_t* q = &sB[(bsub[ni] + fr) * kLDB];
                 if (kFP8) {
-                    const uint2 v = *(const uint2*)(q + kk * 16 + half * 8);
-                    fb[ni] = fp8x8_to_bf16x8(v.x, v.y);
+                    fbq[ni] = *(const u32x4*)(q + 32 * j + 16 * half);
                 } else {
-                    fb[ni] = *(const bf16x8*)(q + (kk * 16 + half * 8) * 2);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        fbh[t][ni] = *(const bf16x8*)(q + (32 * j + 16 * half + 8 * t) * 2);
                 }
             }
 #pragma unroll
-            for (int mi = 0; mi < NS; ++mi)
+            for (int t = 0; t < 2; ++t) {
+                bf16x8 fb[2];
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-                    part[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni],
-                                                                           part[mi][ni], 0, 0, 0);
+                    fb[ni] = kFP8 ? fp8x8_to_bf16x8(fbq[ni][2 * t], fbq[ni][2 * t + 1]) : fbh[t][ni];
+#pragma unroll
+                for (int mi = 0; mi < NS; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni)
+                        part[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            fa[t][mi], fb[ni], part[mi][ni], 0, 0, 0);
+            }
         }
         const float s0 = kFP8 ? sScale[0][kb] : 1.0f;
         const float s1 = kFP8 ? sScale[1][kb] : 1.0f;
