@@ -79,8 +79,15 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 //
 // XCD-aware order: MI355X dispatches consecutive workgroups round-robin to its 8 XCDs, each with
 // a private L2.  Workgroup i gets logical tile (i % 8) * (R8 / 8) + i / 8 (R8 = real tile count
-// rounded up to 8), so each XCD walks one contiguous range of logical tiles, whose n-tiles of the
-// same m-tile (same activation rows) and m-tiles of the same expert stay in one L2.
+// rounded up to 8), so each XCD walks one contiguous range of logical tiles, and tiles that are
+// close in that range run at about the same time on the same L2.
+//
+// Within a group, logical tiles go in supertiles of up to kSuperM m-tiles: the m-tiles of one
+// supertile are the fastest index, its n-tiles the next.  Workgroups that read the same weight
+// tile (same expert and n-tile, different rows) are therefore neighbours and walk K together,
+// so the weight bytes come from HBM once per supertile instead of once per m-tile; the few
+// activation row blocks of a supertile stay in L2 across the n-tiles that run alongside.
+constexpr int kSuperM = 8;
 
 struct Tile {
     int group;  // expert
@@ -114,37 +121,60 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
     if (wg >= R8) return false;
     const int L = (wg & 7) * (R8 >> 3) + (wg >> 3);
     if (L >= R) return false;
+    // the group that owns L: group g owns logical tiles [m0 * n_tiles, (m0 + m_g) * n_tiles),
+    // m0 = m-tiles of the groups before it; then L's place inside the group's supertiles
+    struct Place { int m, nt; };  // m-tile inside the group, n-tile
+    auto place = [L, n_tiles](int m0, int m_g) -> Place {
+        const int r = L - m0 * n_tiles;
+        const int b = r / (kSuperM * n_tiles);
+        const int rb = r - b * (kSuperM * n_tiles);
+        const int gm = min(kSuperM, m_g - b * kSuperM);  // m-tiles in this supertile
+        const int nt = rb / gm;
+        return Place{b * kSuperM + (rb - nt * gm), nt};
+    };
     const int mt = L / n_tiles;
-    t.nt = L - mt * n_tiles;
     if (offsets == nullptr) {
+        const Place pl = place(0, total_m);
+        t.nt = pl.nt;
         t.group = 0;
-        t.row0 = mt * BM;
+        t.row0 = pl.m * BM;
         t.row1 = min(t.row0 + BM, identity_rows);
         return true;
     }
     const bool mine = (mt >= incl - local) && (mt < incl);
     const uint64_t owner = __ballot(mine);
     const int src = __ffsll((unsigned long long)owner) - 1;
-    int group = 0, row0 = 0, row1 = 0;
+    // the owning lane finds the group; the placement inside it is computed on the broadcast
+    // (wave-uniform) values
+    int group = 0, gm0 = 0, gtiles = 1, ga = 0, gn = 0;
     if (lane == src) {
-        int m = incl - local;  // first m-tile of this lane's first group
+        int m0 = incl - local;  // first m-tile of this lane's first group
         for (int i = 0; i < G; ++i) {
             const int g = lane * G + i;
             if (g >= n_groups) break;
             const int a = offsets[g], n = offsets[g + 1] - a;
             const int tiles = (n + BM - 1) / BM;
-            if (mt < m + tiles) {
+            if (mt < m0 + tiles) {
                 group = g;
-                row0 = a + (mt - m) * BM;
-                row1 = min(row0 + BM, a + n);
+                gm0 = m0;
+                gtiles = tiles;
+                ga = a;
+                gn = n;
                 break;
             }
-            m += tiles;
+            m0 += tiles;
         }
     }
-    t.group = uniform(__shfl(group, src, kWave));
-    t.row0 = uniform(__shfl(row0, src, kWave));
-    t.row1 = uniform(__shfl(row1, src, kWave));
+    group = uniform(__shfl(group, src, kWave));
+    gm0 = uniform(__shfl(gm0, src, kWave));
+    gtiles = uniform(__shfl(gtiles, src, kWave));
+    ga = uniform(__shfl(ga, src, kWave));
+    gn = uniform(__shfl(gn, src, kWave));
+    const Place pl = place(gm0, gtiles);
+    t.group = group;
+    t.nt = pl.nt;
+    t.row0 = ga + pl.m * BM;
+    t.row1 = min(t.row0 + BM, ga + gn);
     return true;
 }
 

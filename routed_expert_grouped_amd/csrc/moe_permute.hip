@@ -5,9 +5,10 @@
 // gating (OSDI'26 hybrid-inference article, DSLP section).
 //
 // One workgroup of 16 waves does the whole job, so the order is decided without atomics:
-//   pass 1  each wave walks its contiguous run of 64-assignment chunks and counts, per expert,
-//           its own assignments (peers with the same expert are found with one ballot per bit
-//           of the expert id; the lowest peer adds the group's size to the wave's LDS row);
+//   pass 1  each wave walks its contiguous run of 64-assignment chunks (the ids of 8 chunks
+//           are loaded together, so the loads overlap) and counts, per expert, its own
+//           assignments (peers with the same expert are found with one ballot per bit of the
+//           expert id; the lowest peer adds the group's size to the wave's LDS row);
 //   scan    per expert: exclusive sum over the waves (in wave order) and the total; then an
 //           exclusive sum of the totals over experts gives `offsets`;
 //   pass 2  each wave walks its chunks again in order; an assignment's slot is
@@ -21,6 +22,7 @@
 namespace moe {
 
 constexpr int kPermWaves = 16;
+constexpr int kBatch = 8;  // 64-assignment chunks whose ids are loaded together
 
 __global__ __launch_bounds__(kPermWaves * kWave) void permute_kernel(
     const int32_t* __restrict__ ids, int n, int E, int nbits, int32_t* __restrict__ counts,
@@ -38,13 +40,26 @@ __global__ __launch_bounds__(kPermWaves * kWave) void permute_kernel(
     const int c1 = (int)((int64_t)(wave + 1) * chunks / kPermWaves);
     int* myrow = rowbase + wave * E;
 
+    // ids of kBatch chunks are loaded together (independent loads), then walked in order
+    auto load_batch = [&](int c, int (&ev)[kBatch]) {
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int f = (c + b) * kWave + lane;
+            ev[b] = (c + b < c1 && f < n) ? ids[f] : -1;
+        }
+    };
+
     // pass 1: per-wave histogram
-    for (int c = c0; c < c1; ++c) {
-        const int f = c * kWave + lane;
-        const int e = f < n ? ids[f] : -1;
-        const bool valid = e >= 0 && e < E;
-        const uint64_t peers = match_peers(e, valid, nbits);
-        if (valid && lane == __ffsll((unsigned long long)peers) - 1) myrow[e] += __popcll(peers);
+    for (int c = c0; c < c1; c += kBatch) {
+        int ev[kBatch];
+        load_batch(c, ev);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int e = ev[b];
+            const bool valid = e >= 0 && e < E;
+            const uint64_t peers = match_peers(e, valid, nbits);
+            if (valid && lane == __ffsll((unsigned long long)peers) - 1) myrow[e] += __popcll(peers);
+        }
     }
     __syncthreads();
 
@@ -79,22 +94,27 @@ __global__ __launch_bounds__(kPermWaves * kWave) void permute_kernel(
     __syncthreads();
 
     // pass 2: slots
-    for (int c = c0; c < c1; ++c) {
-        const int f = c * kWave + lane;
-        const int e = f < n ? ids[f] : -1;
-        const bool valid = e >= 0 && e < E;
-        const uint64_t peers = match_peers(e, valid, nbits);
-        int base = 0;
-        if (valid) {
-            base = myrow[e];
-            const int pos = base + __popcll(peers & ((1ull << lane) - 1ull));
-            perm[pos] = f;
-            inv[f] = pos;
+    for (int c = c0; c < c1; c += kBatch) {
+        int ev[kBatch];
+        load_batch(c, ev);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int f = (c + b) * kWave + lane;
+            const int e = ev[b];
+            const bool valid = e >= 0 && e < E;
+            const uint64_t peers = match_peers(e, valid, nbits);
+            int base = 0;
+            if (valid) {
+                base = myrow[e];
+                const int pos = base + __popcll(peers & ((1ull << lane) - 1ull));
+                perm[pos] = f;
+                inv[f] = pos;
+            }
+            // the wave's reads of myrow above are issued before this write (in-order LDS per wave)
+            __builtin_amdgcn_wave_barrier();
+            if (valid && lane == __ffsll((unsigned long long)peers) - 1) myrow[e] = base + __popcll(peers);
+            __builtin_amdgcn_wave_barrier();
         }
-        // the wave's reads of myrow above are issued before this write (in-order LDS per wave)
-        __builtin_amdgcn_wave_barrier();
-        if (valid && lane == __ffsll((unsigned long long)peers) - 1) myrow[e] = base + __popcll(peers);
-        __builtin_amdgcn_wave_barrier();
     }
 }
 

@@ -105,6 +105,23 @@ def test_skewed_routing_one_hot_expert():
     compare_with_oracle(layer, g)
 
 
+def test_block_scales_zero_and_wide_range():
+    """Weight blocks with zero scales and scales spread over six decades, on the grouped-GEMM
+    path (many rows per expert) of the routed and the shared experts; phase 2 has an odd number
+    of 128-long K blocks (I = 384).  A zero scale makes its whole block contribute nothing."""
+    layer = synth.make_layer(mid(T=200, E=8, k=2), seed=5)
+    rng = np.random.default_rng(5)
+    for ew in (layer.experts, layer.shared):
+        for name in ("s_gate", "s_up", "s_down"):
+            s = getattr(ew, name)
+            f = rng.choice(np.array([0.0, 1e-3, 1.0, 1e3], np.float32), size=tuple(s.shape))
+            s.mul_(torch.from_numpy(f))
+    layer = layer.to(DEV)
+    g = run_gpu(layer)
+    assert g["counts"].max() > 32  # the grouped GEMM runs (more than 32 rows per expert)
+    compare_with_oracle(layer, g)
+
+
 def test_repeat_runs_are_bit_identical():
     layer = layer_for(mid(), seed=1)
     a, b = run_gpu(layer), run_gpu(layer)
