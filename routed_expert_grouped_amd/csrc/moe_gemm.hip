@@ -1,23 +1,23 @@
-// moe_gemm.hip -- grouped expert GEMM for many rows per expert (prefill shapes).
+// moe_gemm.hip -- grouped expert GEMMs for many rows per expert (prefill shapes).
 //
 // Tokens that hit the same expert are batched so that the expert's projection is a GEMM
 // (KTransformers article, 2.2).  Each expert's rows are cut into 128-row m-tiles; a workgroup
-// computes one m-tile against 128 weight rows over the whole K:
-//   phase 1: 64 gate rows + the same 64 up rows -> 64 columns of h = SiLU(gate) * up
-//   phase 2: 128 down rows -> 128 columns of y
+// computes one m-tile against a tile of weight rows over the whole K:
+//   phase 1: gate rows + the same up rows -> columns of h = SiLU(gate) * up
+//   phase 2: down rows -> columns of y
+// Weights are expanded exactly from FP8 to bf16 as they leave LDS and multiplied on MFMA
+// 32x32x16 (bf16 in, fp32 accumulate); each 128-long K block is one FP8 scale block, applied to
+// that block's MFMA sum (the post-scaling of the OSDI'26 article's FP8 GEMV, section "native
+// FP8 GEMV", Figures 9-10).
 //
-// Per 128-long K block (= one FP8 scale block) the workgroup stages in LDS the activation tile
-// (128 rows x 128 bf16, gathered through the grouping in phase 1) and the weight tile (128 rows
-// x 128 FP8 codes, kept as codes), both loaded as whole 128-byte lines.  Four waves (2 x 2) then
-// run MFMA 32x32x16 chains: each wave owns 2 of the 4 32-row m-subtiles (interleaved, so a
-// partly filled tile still spreads over both wave rows) and 2 32-row weight subtiles (phase 1:
-// matching gate and up rows, so SiLU(gate)*up is formed in registers).  k-steps go in pairs
-// whose lane halves cover 16 consecutive K each, so one 16-byte LDS read of FP8 codes feeds two
-// MFMAs.  Weight fragments are expanded exactly from FP8 to bf16 as they leave LDS (the row
-// stride of 144 bytes keeps those reads free of bank conflicts); each block's chain goes into a partial
-// sum that is multiplied by the block's scale into the fp32 accumulator (the post-scaling of
-// the OSDI'26 article's FP8 GEMV, section "native FP8 GEMV", Figures 9-10).  Subtiles past the
-// last row are skipped.  Two workgroups share a CU, so one computes while the other stages.
+// Two kernels, picked by launch_gemm:
+//   gemm_fp8_wide_kernel  FP8, weight-row count a multiple of 256 (phase 2) / 128 (phase 1):
+//                         one 8-wave workgroup per CU, 128 x 256 tiles, all loads direct to LDS;
+//   gemm_kernel           bf16 weights and the other FP8 shapes (H an odd multiple of 128, or
+//                         more than 64 GB of activations): register-staged 128 x 128 tiles.
+// In every kernel a wave owns 2 of the 4 32-row m-subtiles (interleaved, so a partly filled
+// tile still spreads over both wave rows) and 2 32-row weight subtiles (phase 1: matching gate
+// and up rows, so SiLU(gate)*up is formed in registers); subtiles past the last row are skipped.
 #include "libmoe.h"
 #include "moe_device.h"
 #include "moe_ffn.h"
@@ -218,24 +218,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
     }
 }
 
-// ------------------------------------------------------------------ FP8 weights
-//
-// Same tile and wave layout, with the loads restructured so that the HBM weight stream runs
-// two blocks ahead of the MFMAs and the activation rows one block ahead:
-//   * activations go global -> LDS directly (16 bytes per lane per instruction, whole 256-byte
-//     row slices) into a 2-stage ring; no registers, no LDS store instructions;
-//   * weights (FP8 codes) go through two alternating register sets into one LDS tile.
-// LDS: 2 x 32 KB activations + 16 KB weights = 80 KB, so two workgroups share a CU.  Both
-// tiles are unpadded; a 16-byte chunk sits at a slot XORed with a function of its row, which
-// keeps the 16-byte fragment reads free of bank conflicts.
-//
-// Wait counts.  Per iteration each thread issues, in this order: the block's scale loads, the
-// activation loads of the next block (inline assembly, so the compiler's own wait counting
-// does not see them and never waits for them before LDS reads), and exactly kBPer weight loads
-// for two blocks ahead.  At the top of the next iteration `vmcnt(kBPer)` therefore means that
-// everything but those weight loads has landed.
-
-constexpr int kBPer8 = kBN * kBK / 256 / 16;  // 16-byte weight chunks per thread per block (4)
+// ------------------------------------------------------------------ helpers of the direct-to-LDS loads
 
 // s_waitcnt immediate that waits until at most n vector-memory loads are outstanding (gfx9
 // encoding: vmcnt in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
@@ -250,84 +233,112 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* lds) {
                  : "memory", "m0");
 }
 
-template <int kPhase, bool kGrouped>
-__global__ __launch_bounds__(256, 2) void gemm_fp8_kernel(GemmArgs a) {
-    constexpr int kAStage = kBM * kBK * 2;  // 32 KB
-    __shared__ __attribute__((aligned(1024))) uint8_t sA[2][kAStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t sB[kBN * kBK];
+// ------------------------------------------------------------------ FP8 weights, wide tiles
+//
+// One workgroup of 8 waves per CU computes a 128-row m-tile against 256 weight rows (phase 1:
+// 128 gate + the same 128 up rows -> 128 h columns; phase 2: 256 y columns), so each activation
+// byte brought through the cache feeds twice as many weight rows as in the 128-row tiles above.
+// Both operands go global -> LDS directly into a 2-stage ring (32 KB activations + 32 KB FP8
+// codes per stage); the block scales of the tile are staged once.  One barrier per 128-long K
+// block: wait for this thread's loads of block kb, barrier (all of block kb has landed and every
+// wave is done with block kb - 1), issue the loads of block kb + 1 into the other stage,
+// multiply block kb.  Waves: 2 (rows) x 4 (weight rows), 64 x 64 outputs each.
+constexpr int kWBN = 256;  // weight rows per wide tile
 
-    constexpr int kCols = kPhase == 1 ? kBN / 2 : kBN;
+template <int kPhase, bool kGrouped>
+__global__ __launch_bounds__(512, 1) void gemm_fp8_wide_kernel(GemmArgs a) {
+    constexpr int kStage = kBM * kBK * 2;  // 32 KB: activations (bf16) or weights (FP8, 256 rows)
+    __shared__ __attribute__((aligned(1024))) uint8_t sA[2][kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB[2][kStage];
+    __shared__ float sScale[2][kMaxKBlocks];
+
+    constexpr int kCols = kPhase == 1 ? kWBN / 2 : kWBN;
     Tile tile;
     const int n_tiles = a.N / kCols;
     if (!find_tile(kGrouped ? a.offsets : nullptr, a.n_groups, a.rows, kBM, n_tiles, tile)) return;
 
     const int tid = (int)threadIdx.x, lane = lane_id(), wave = uniform(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int e = tile.group;
     const int c0 = tile.nt * kCols;
     const int K = a.K, kblocks = K / kBK;
     const int fr = lane & 31, half = lane >> 5;
 
-    // ---- activation loads: instruction i (0..7) of wave w fills tile rows 4 (8 w + i) + lane/16,
-    // slot lane % 16 of the row holding logical chunk slot ^ (row & 15).  Rows past the end of
-    // the m-tile load the tile's first row (never stored), so every load is in bounds.
-    uint32_t aoff[8];  // 16-byte chunk index of each loaded row slice (rows * K / 8 < 2^32)
+    // activation loads: instruction i (0..3) of wave w fills tile rows 4 (4 w + i) + lane/16,
+    // slot lane % 16 holding logical chunk slot ^ (row & 15); rows past the m-tile load its
+    // first row (never stored)
+    uint32_t aoff[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = 4 * (8 * wave + i) + (lane >> 4);
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * (4 * wave + i) + (lane >> 4);
         const int p = tile.row0 + r < tile.row1 ? tile.row0 + r : tile.row0;
         const uint32_t src = (kPhase == 1 && kGrouped) ? (uint32_t)(a.perm[p] / a.k) : (uint32_t)p;
         aoff[i] = src * (uint32_t)(K / 8) + (uint32_t)((lane & 15) ^ (r & 15));
     }
-    auto dma_a = [&](int kb, int st) {
+    // weight loads: instruction i of wave w fills tile rows 8 (4 w + i) + lane/8, slot lane % 8
+    // holding logical chunk slot ^ ((row >> 1) & 7); phase 1 rows 0..127 gate, 128..255 up
+    const uint8_t* bsrc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 8 * (4 * wave + i) + (lane >> 3);
+        const uint8_t* base;
+        int wr;
+        if (kPhase == 1) {
+            base = (const uint8_t*)(r < 128 ? a.w0 : a.w1);
+            wr = c0 + (r & 127);
+        } else {
+            base = (const uint8_t*)a.w0;
+            wr = c0 + r;
+        }
+        bsrc[i] = base + ((size_t)e * a.N + wr) * (size_t)K + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+    }
+    auto issue = [&](int kb, int st) {
         const uint8_t* act = (const uint8_t*)a.act + (size_t)kb * (kBK * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            lds_dma16(act + (size_t)aoff[i] * 16, &sA[st][4 * (8 * wave + i) * kBK * 2]);
-    };
-    // ---- weight loads: chunk tid % 8 of tile rows tid / 8 + 32 i; phase 1 rows 0..63 gate,
-    // 64..127 up.  Every row of a thread has the same swizzle ((row >> 1) & 7 = (tid >> 4) & 7).
-    const uint8_t* bsrc0;
-    const uint8_t* bsrc1;
-    {
-        const size_t row = (size_t)e * a.N + c0 + (tid >> 3);
-        bsrc0 = (const uint8_t*)a.w0 + row * K + (tid & 7) * 16;
-        bsrc1 = (kPhase == 1 ? (const uint8_t*)a.w1 + row * K : bsrc0 + (size_t)64 * K) + (kPhase == 1 ? (tid & 7) * 16 : 0);
-    }
-    const int bdst = (tid >> 3) * kBK + (((tid & 7) ^ ((tid >> 4) & 7)) << 4);
-    u32x4 rb0[kBPer8], rb1[kBPer8];
-    auto load_b = [&](int kb, u32x4 (&rb)[kBPer8]) {
-        const size_t o = (size_t)kb * kBK, step = (size_t)32 * K;
-        rb[0] = __builtin_nontemporal_load((const u32x4*)(bsrc0 + o));
-        rb[1] = __builtin_nontemporal_load((const u32x4*)(bsrc0 + o + step));
-        rb[2] = __builtin_nontemporal_load((const u32x4*)(bsrc1 + o));
-        rb[3] = __builtin_nontemporal_load((const u32x4*)(bsrc1 + o + step));
-    };
-    auto store_b = [&](const u32x4 (&rb)[kBPer8]) {
+        for (int i = 0; i < 4; ++i)
+            lds_dma16(act + (size_t)aoff[i] * 16, &sA[st][4 * (4 * wave + i) * kBK * 2]);
 #pragma unroll
-        for (int i = 0; i < kBPer8; ++i) *(u32x4*)&sB[bdst + i * 32 * kBK] = rb[i];
+        for (int i = 0; i < 4; ++i)
+            lds_dma16(bsrc[i] + (size_t)kb * kBK, &sB[st][8 * (4 * wave + i) * kBK]);
     };
-    // block scales of the tile's weight rows: phase 1 gate and up of block-row c0/128; phase 2
-    // one block-row (the 128 rows of the tile)
-    const size_t srow = ((size_t)e * (a.N / 128) + c0 / 128) * kblocks;
-    const float* sc0 = a.s0 + srow;
-    const float* sc1 = (kPhase == 1 ? a.s1 : a.s0) + srow;
+
+    // block scales: phase 1 [0] gate, [1] up of block-row c0/128; phase 2 block-rows c0/128 and
+    // c0/128 + 1 (the tile's 256 rows)
+    if (tid < kblocks) {
+        const size_t srow = ((size_t)e * (a.N / 128) + c0 / 128) * kblocks;
+        sScale[0][tid] = a.s0[srow + tid];
+        sScale[1][tid] = kPhase == 1 ? a.s1[srow + tid] : a.s0[srow + kblocks + tid];
+    }
+    const int srow0 = kPhase == 1 ? 0 : (wn >> 1);
+    const int srow1 = kPhase == 1 ? 1 : (wn >> 1);
 
     const int nvalid = (tile.row1 - tile.row0 + 31) >> 5;
     const int mine = (nvalid > wm) + (nvalid > wm + 2);
-    // fragment addresses: chunk c of row r sits at slot c ^ swz(r), so a read address is a
-    // per-lane base XOR a per-step constant
-    int abase[2], bbase[2];
+    // LDS fragment addresses (stage 0; stage 1 is +kStage, an immediate offset).  Chunk c of row
+    // r sits at slot c ^ swz(r).  A: m-subtile mi, k-pair j, step t -> logical chunk 4j + 2h + t;
+    // B: weight subtile ni, k-pair j -> logical chunk 2j + h.
+    int aaddr[2][8], baddr[2][4];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
         const int r = (wm + 2 * mi) * 32 + fr;
-        abase[mi] = r * (kBK * 2) + (((r & 15) << 4) ^ (half << 5));
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int c = 4 * (q >> 1) + 2 * half + (q & 1);
+            aaddr[mi][q] = r * (kBK * 2) + ((c ^ (r & 15)) << 4);
+        }
     }
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
-        const int r = (kPhase == 1 ? ni * 64 + wn * 32 : wn * 64 + ni * 32) + fr;
-        bbase[ni] = r * kBK + ((((r >> 1) & 7) ^ half) << 4);
+        const int r = (kPhase == 1 ? ni * 128 + wn * 32 : wn * 64 + ni * 32) + fr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) baddr[ni][j] = r * kBK + (((2 * j + half) ^ ((r >> 1) & 7)) << 4);
     }
+    // a zero block scale anywhere in the tile selects the variant that masks that block's codes
+    bool any_zero = false;
+    __syncthreads();  // scales staged
+    for (int b = lane; b < kblocks; b += kWave)
+        any_zero |= sScale[srow0][b] == 0.0f || sScale[srow1][b] == 0.0f;
+    any_zero = __ballot(any_zero) != 0;
 
     f32x16 acc[2][2];
 #pragma unroll
@@ -335,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void gemm_fp8_kernel(GemmArgs a) {
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+            for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.0f;
 
     // Block scales are applied by keeping each accumulator in units of the scale of the block
     // being multiplied: before block b it is multiplied by u / s_b (u = the scale of the last
@@ -344,24 +355,57 @@ __global__ __launch_bounds__(256, 2) void gemm_fp8_kernel(GemmArgs a) {
     // no separate partial sums.  A zero scale keeps the units and masks that block's codes, so
     // the block adds exactly nothing.
     float u0 = 0.0f, u1 = 0.0f;
-    auto compute = [&](int st, uint32_t m0, uint32_t m1, auto nsub_tag) {
-        constexpr int NS = decltype(nsub_tag)::value;
-        const uint8_t* A = sA[st];
-        // k-steps in pairs: for pair j, lane half h covers K elements [32j + 16h, +16) on both
-        // operands, so one 16-byte read of FP8 codes feeds two MFMAs
+    auto rescale = [&](float r0, float r1) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                acc[mi][0][q] *= r0;
+                acc[mi][1][q] *= r1;
+            }
+    };
+    // One K block from stage ST with NS filled m-subtiles; kMask: zero-scale blocks are masked.
+    auto block = [&](int kb, auto st_tag, auto ns_tag, auto mask_tag) {
+        constexpr int ST = decltype(st_tag)::value, NS = decltype(ns_tag)::value;
+        constexpr bool kMask = decltype(mask_tag)::value;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        if (kb + 1 < kblocks) issue(kb + 1, ST ^ 1);
+        if (NS == 0) return;
+        const float s0 = sScale[srow0][kb], s1 = sScale[srow1][kb];
+        uint32_t m0 = ~0u, m1 = ~0u;
+        float r0, r1;
+        if (kMask) {
+            const bool z0 = s0 == 0.0f, z1 = s1 == 0.0f;
+            r0 = z0 ? 1.0f : u0 * __builtin_amdgcn_rcpf(s0);
+            r1 = z1 ? 1.0f : u1 * __builtin_amdgcn_rcpf(s1);
+            u0 = z0 ? u0 : s0;
+            u1 = z1 ? u1 : s1;
+            m0 = z0 ? 0u : ~0u;
+            m1 = z1 ? 0u : ~0u;
+        } else {
+            r0 = u0 * __builtin_amdgcn_rcpf(s0);
+            r1 = u1 * __builtin_amdgcn_rcpf(s1);
+            u0 = s0;
+            u1 = s1;
+        }
+        rescale(r0, r1);
+        const uint8_t* A = sA[ST];
+        const uint8_t* B = sB[ST];
 #pragma unroll
         for (int j = 0; j < kBK / 32; ++j) {
-            bf16x8 fa[2][NS];
+            bf16x8 fa[2][NS > 0 ? NS : 1];
             u32x4 fbq[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int mi = 0; mi < NS; ++mi)
-                    fa[t][mi] = *(const bf16x8*)&A[abase[mi] ^ ((4 * j + t) << 4)];
+                for (int mi = 0; mi < NS; ++mi) fa[t][mi] = *(const bf16x8*)&A[aaddr[mi][2 * j + t]];
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) fbq[ni] = *(const u32x4*)&sB[bbase[ni] ^ (j << 5)];
-            fbq[0] &= m0;
-            fbq[1] &= m1;
+            for (int ni = 0; ni < 2; ++ni) fbq[ni] = *(const u32x4*)&B[baddr[ni][j]];
+            if (kMask) {
+                fbq[0] &= m0;
+                fbq[1] &= m1;
+            }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 bf16x8 fb[2];
@@ -376,124 +420,94 @@ __global__ __launch_bounds__(256, 2) void gemm_fp8_kernel(GemmArgs a) {
             }
         }
     };
-    auto rescale = [&](float r0, float r1) {
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                acc[mi][0][q] *= r0;
-                acc[mi][1][q] *= r1;
-            }
-    };
-
-    // One block.  kMode 2: the loads of block kb + 1 (scales, activations) and the weights of
-    // kb + 2 are issued; 1: only those of kb + 1 (the last weights are already in flight); 0:
-    // nothing (last block).  kWait: vmcnt at the top, kBPer8 while the weight loads of kb + 1
-    // may still be in flight, else 0.  Each call site has constant modes, so the loads are
-    // unconditional and the compiler's own wait counting stays exact.
-    float sn0 = sc0[0], sn1 = sc1[0];  // scales of the next block to multiply
-    auto iter = [&](int kb, u32x4 (&rb)[kBPer8], auto mode_tag, auto wait_tag) {
-        constexpr int kMode = decltype(mode_tag)::value;
-        constexpr int kWait = decltype(wait_tag)::value;
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWait));
-        __syncthreads();
-        store_b(rb);
-        const float s0 = sn0, s1 = sn1;
-        if (kMode >= 1) {
-            sn0 = sc0[kb + 1];
-            sn1 = sc1[kb + 1];
-            dma_a(kb + 1, (kb + 1) & 1);
+    // the whole K loop per (filled subtiles, masking): wave-uniform choice made once; every
+    // variant runs the same barriers
+    auto run = [&](auto ns_tag, auto mask_tag) {
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        int kb = 0;
+        for (; kb + 1 < kblocks; kb += 2) {
+            block(kb, S0{}, ns_tag, mask_tag);
+            block(kb + 1, S1{}, ns_tag, mask_tag);
         }
-        if (kMode == 2) load_b(kb + 2, rb);
-        __syncthreads();
-        if (mine == 0) return;
-        const bool z0 = s0 == 0.0f, z1 = s1 == 0.0f;
-        const float r0 = z0 ? 1.0f : u0 / s0, r1 = z1 ? 1.0f : u1 / s1;
-        u0 = z0 ? u0 : s0;
-        u1 = z1 ? u1 : s1;
-        rescale(r0, r1);
-        const uint32_t m0 = z0 ? 0u : ~0u, m1 = z1 ? 0u : ~0u;
-        if (mine == 2)
-            compute(kb & 1, m0, m1, std::integral_constant<int, 2>{});
-        else
-            compute(kb & 1, m0, m1, std::integral_constant<int, 1>{});
+        if (kb < kblocks) block(kb, S0{}, ns_tag, mask_tag);
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using IW = std::integral_constant<int, kBPer8>;
+    using N0 = std::integral_constant<int, 0>;
+    using N1 = std::integral_constant<int, 1>;
+    using N2 = std::integral_constant<int, 2>;
+    using MY = std::integral_constant<bool, true>;
+    using MN = std::integral_constant<bool, false>;
 
-    // prologue: weights of block 0, activations of block 0, weights of block 1 (this order, so
-    // that the first wait leaves only the last in flight)
-    // (with one block the second load re-reads block 0 into registers nobody uses: unconditional
-    // loads keep the compiler's wait counting exact)
-    load_b(0, rb0);
-    dma_a(0, 0);
-    load_b(kblocks > 1 ? 1 : 0, rb1);
-    int kb = 0;
-    for (; kb + 3 < kblocks; kb += 2) {
-        iter(kb, rb0, I2{}, IW{});
-        iter(kb + 1, rb1, I2{}, IW{});
-    }
-    // 1 to 3 blocks left; kb is even, so block kb's weights are in rb0
-    const int rem = kblocks - kb;
-    if (rem == 3) {
-        iter(kb, rb0, I2{}, IW{});
-        iter(kb + 1, rb1, I1{}, IW{});
-        iter(kb + 2, rb0, I0{}, I0{});
-    } else if (rem == 2) {
-        iter(kb, rb0, I1{}, IW{});
-        iter(kb + 1, rb1, I0{}, I0{});
-    } else {
-        iter(kb, rb0, I0{}, I0{});
-    }
+    issue(0, 0);
+    if (mine == 0)
+        run(N0{}, MN{});
+    else if (any_zero)
+        run(N2{}, MY{});  // rare: computes both subtiles (an unfilled one is never stored)
+    else if (mine == 2)
+        run(N2{}, MN{});
+    else
+        run(N1{}, MN{});
     rescale(u0, u1);
 
-    // D layout of the 32x32 MFMA: value r of a lane is row 8*(r/4) + 4*(lane/32) + r%4 of the
-    // subtile, column lane%32
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
         if (mi >= mine) break;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int p = tile.row0 + (wm + 2 * mi) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        for (int q = 0; q < 16; ++q) {
+            const int p = tile.row0 + (wm + 2 * mi) * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
             if (p >= tile.row1) continue;
             uint16_t* o = a.out + (size_t)p * a.N + c0 + fr;
             if (kPhase == 1) {
-                const float g = acc[mi][0][r], u = acc[mi][1][r];
+                const float g = acc[mi][0][q], u = acc[mi][1][q];
                 o[wn * 32] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
             } else {
-                o[wn * 64] = f32_to_bf16(acc[mi][0][r]);
-                o[wn * 64 + 32] = f32_to_bf16(acc[mi][1][r]);
+                o[wn * 64] = f32_to_bf16(acc[mi][0][q]);
+                o[wn * 64 + 32] = f32_to_bf16(acc[mi][1][q]);
             }
         }
     }
 }
 
+static moe_status launch_wide(int phase, const GemmArgs& a, hipStream_t st) {
+    const int cols = phase == 1 ? kWBN / 2 : kWBN;
+    const int groups = a.offsets ? a.n_groups : 1;
+    const int64_t mt = ((int64_t)a.rows + kBM - 1) / kBM + std::min<int64_t>(groups, a.rows);
+    const int64_t wgs = mt * (a.N / cols);
+    if (wgs > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    const dim3 grid((unsigned)((wgs + 7) & ~int64_t(7))), block(512);
+    const bool g = a.offsets != nullptr;
+    if (phase == 1) {
+        if (g) gemm_fp8_wide_kernel<1, true><<<grid, block, 0, st>>>(a);
+        else gemm_fp8_wide_kernel<1, false><<<grid, block, 0, st>>>(a);
+    } else {
+        if (g) gemm_fp8_wide_kernel<2, true><<<grid, block, 0, st>>>(a);
+        else gemm_fp8_wide_kernel<2, false><<<grid, block, 0, st>>>(a);
+    }
+    return launch_status();
+}
+
 moe_status launch_gemm(int phase, const GemmArgs& a, hipStream_t st) {
+    if (a.K / kBK > kMaxKBlocks) return MOE_ERR_UNSUPPORTED;
+    // the wide kernel addresses activation rows by 32-bit 16-byte chunk indices (up to 64 GB of
+    // activations); beyond that, and for other shapes, the register-staged kernel runs
+    const bool chunk32 = (int64_t)a.rows * (a.K / 8) < (int64_t(1) << 32);
+    if (a.fp8 && chunk32 && a.N % (phase == 1 ? kWBN / 2 : kWBN) == 0) return launch_wide(phase, a, st);
     const int cols = phase == 1 ? kBN / 2 : kBN;
     const int groups = a.offsets ? a.n_groups : 1;
     const int64_t mt = ((int64_t)a.rows + kBM - 1) / kBM + std::min<int64_t>(groups, a.rows);
     const int64_t wgs = mt * (a.N / cols);
-    if (wgs > INT32_MAX || a.K / kBK > kMaxKBlocks) return MOE_ERR_UNSUPPORTED;
+    if (wgs > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((wgs + 7) & ~int64_t(7))), block(256);
     const bool g = a.offsets != nullptr;
 #define MOE_GEMM(F, P, G) gemm_kernel<F, P, G><<<grid, block, 0, st>>>(a)
-#define MOE_GEMM8(P, G) gemm_fp8_kernel<P, G><<<grid, block, 0, st>>>(a)
-    // the FP8 kernel addresses activation rows by 32-bit 16-byte chunk indices (up to 64 GB of
-    // activations); beyond that the register-staged kernel, which uses 64-bit offsets, runs
-    const bool chunk32 = (int64_t)a.rows * (a.K / 8) < (int64_t(1) << 32);
     if (phase == 1) {
-        if (a.fp8 && chunk32) g ? MOE_GEMM8(1, true) : MOE_GEMM8(1, false);
-        else if (a.fp8) g ? MOE_GEMM(true, 1, true) : MOE_GEMM(true, 1, false);
+        if (a.fp8) g ? MOE_GEMM(true, 1, true) : MOE_GEMM(true, 1, false);
         else g ? MOE_GEMM(false, 1, true) : MOE_GEMM(false, 1, false);
     } else {
-        if (a.fp8 && chunk32) g ? MOE_GEMM8(2, true) : MOE_GEMM8(2, false);
-        else if (a.fp8) g ? MOE_GEMM(true, 2, true) : MOE_GEMM(true, 2, false);
+        if (a.fp8) g ? MOE_GEMM(true, 2, true) : MOE_GEMM(true, 2, false);
         else g ? MOE_GEMM(false, 2, true) : MOE_GEMM(false, 2, false);
     }
 #undef MOE_GEMM
-#undef MOE_GEMM8
     return launch_status();
 }
 

@@ -91,6 +91,7 @@ def test_tiny_layer(cfg):
     dict(T=1, E=24, k=4),                    # a single token
     dict(T=64, E=16, k=16, renorm=0),        # k = E (every expert), unnormalised sigmoid
     dict(T=96, E=40, k=3, score_fn="softmax", renorm=0, wdtype="bf16"),
+    dict(T=160, H=640, E=8, k=2),            # H an odd multiple of 128: register-staged GEMM
 ])
 def test_mid_layer(over):
     layer = layer_for(mid(**over), seed=1)
