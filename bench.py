@@ -68,21 +68,33 @@ def layer_flops(T, H, I, k, shared=True) -> int:
 
 # ------------------------------------------------------------------ counter-derived traffic
 
-def source_digest() -> str:
+def kernel_sources(kernel: str) -> list:
+    """Sources (relative to the repository root) that a libmoe kernel is built from: every file
+    of csrc/, less the other expert path's kernel file."""
+    files = sorted(os.path.relpath(p, ROOT) for p in
+                   glob.glob(os.path.join(ROOT, "routed_expert_grouped_amd", "csrc", "*")))
+    other = "moe_gemm.hip" if "gemv_kernel" in kernel else None
+    return [f for f in files if os.path.basename(f) != other]
+
+
+def source_digest(files) -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "routed_expert_grouped_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def counter_traffic(workload: str):
     """HBM bytes per launch of the gate/up kernel from the committed rocprofv3 counter summary,
-    or None when there is none or the kernel sources changed since it was taken."""
+    or None when there is none or the kernel's sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"gate_up_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_digest") != source_digest():
+    files = rec.get("source_files") or []
+    if not files or any(not os.path.exists(os.path.join(ROOT, f)) for f in files):
+        return None
+    if rec.get("source_digest") != source_digest(files):
         return None
     return rec.get("traffic_bytes")
 
