@@ -1,8 +1,8 @@
 // moe_gemm.hip -- grouped expert GEMMs for many rows per expert (prefill shapes).
 //
 // Tokens that hit the same expert are batched so that the expert's projection is a GEMM
-// (KTransformers article, 2.2).  Each expert's rows are cut into 128-row m-tiles; a workgroup
-// computes one m-tile against a tile of weight rows over the whole K:
+// (KTransformers article, 2.2).  Each expert's rows are cut into m-tiles; a workgroup computes
+// one m-tile against a tile of weight rows over the whole K:
 //   phase 1: gate rows + the same up rows -> columns of h = SiLU(gate) * up
 //   phase 2: down rows -> columns of y
 // Weights are expanded exactly from FP8 to bf16 as they leave LDS and multiplied on MFMA
@@ -11,13 +11,13 @@
 // FP8 GEMV", Figures 9-10).
 //
 // Two kernels, picked by launch_gemm:
-//   gemm_fp8_wide_kernel  FP8, weight-row count a multiple of 256 (phase 2) / 128 (phase 1):
-//                         one 8-wave workgroup per CU, 128 x 256 tiles, all loads direct to LDS;
+//   gemm_fp8_q256_kernel  FP8 weights, H a multiple of 256: one 8-wave workgroup per CU,
+//                         256-row m-tiles x 256 weight rows, all loads direct to LDS;
 //   gemm_kernel           bf16 weights and the other FP8 shapes (H an odd multiple of 128, or
 //                         more than 64 GB of activations): register-staged 128 x 128 tiles.
-// In every kernel a wave owns 2 of the 4 32-row m-subtiles (interleaved, so a partly filled
-// tile still spreads over both wave rows) and 2 32-row weight subtiles (phase 1: matching gate
-// and up rows, so SiLU(gate)*up is formed in registers); subtiles past the last row are skipped.
+// A wave owns interleaved 32-row m-subtiles (so a partly filled tile still spreads over both
+// wave rows) and 2 32-row weight subtiles (phase 1: matching gate and up rows, so SiLU(gate)*up
+// is formed in registers); subtiles past the last row are skipped.
 #include "libmoe.h"
 #include "moe_device.h"
 #include "moe_ffn.h"
@@ -233,54 +233,58 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* lds) {
                  : "memory", "m0");
 }
 
-// ------------------------------------------------------------------ FP8 weights, wide tiles
+constexpr int kHK = 64;  // K per stage of the direct-to-LDS kernel (half a scale block)
+
+// ------------------------------------------------------------------ FP8 weights, 256 x 256 tiles
 //
-// One workgroup of 8 waves per CU computes a 128-row m-tile against 256 weight rows (phase 1:
-// 128 gate + the same 128 up rows -> 128 h columns; phase 2: 256 y columns), so each activation
-// byte brought through the cache feeds twice as many weight rows as in the 128-row tiles above.
-// Both operands go global -> LDS directly into a 2-stage ring (32 KB activations + 32 KB FP8
-// codes per stage); the block scales of the tile are staged once.  One barrier per 128-long K
-// block: wait for this thread's loads of block kb, barrier (all of block kb has landed and every
-// wave is done with block kb - 1), issue the loads of block kb + 1 into the other stage,
-// multiply block kb.  Waves: 2 (rows) x 4 (weight rows), 64 x 64 outputs each.
-constexpr int kWBN = 256;  // weight rows per wide tile
+// One workgroup of 8 waves per CU computes a 256-row m-tile against 256 weight rows (phase 1:
+// 128 gate + the same 128 up rows -> 128 h columns; phase 2: 256 y columns).  Tiles of 256 rows
+// cover a whole expert at prefill sizes (about 128 rows per expert at T = 4096), so an expert's
+// weights are streamed once instead of once more for a short tail tile.  K goes in 64-long
+// stages through a 3-stage ring (32 KB activations + 16 KB FP8 codes per stage), loaded directly
+// to LDS two stages ahead.  Waves: 2 (rows) x 4 (weight rows); a wave owns the interleaved
+// m-subtiles wm, wm + 2, wm + 4, wm + 6 and 2 weight subtiles (phase 1: matching gate and up).
+constexpr int kQM = 256;  // rows per m-tile
+constexpr int kQN = 256;  // weight rows per tile
 
 template <int kPhase, bool kGrouped>
-__global__ __launch_bounds__(512, 1) void gemm_fp8_wide_kernel(GemmArgs a) {
-    constexpr int kStage = kBM * kBK * 2;  // 32 KB: activations (bf16) or weights (FP8, 256 rows)
-    __shared__ __attribute__((aligned(1024))) uint8_t sA[2][kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t sB[2][kStage];
+__global__ __launch_bounds__(512, 1) void gemm_fp8_q256_kernel(GemmArgs a) {
+    constexpr int kAStage = kQM * kHK * 2;  // 32 KB
+    constexpr int kBStage = kQN * kHK;      // 16 KB
+    constexpr int kStages = 3;
+    __shared__ __attribute__((aligned(1024))) uint8_t sA[kStages][kAStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB[kStages][kBStage];
     __shared__ float sScale[2][kMaxKBlocks];
 
-    constexpr int kCols = kPhase == 1 ? kWBN / 2 : kWBN;
+    constexpr int kCols = kPhase == 1 ? kQN / 2 : kQN;
     Tile tile;
     const int n_tiles = a.N / kCols;
-    if (!find_tile(kGrouped ? a.offsets : nullptr, a.n_groups, a.rows, kBM, n_tiles, tile)) return;
+    if (!find_tile(kGrouped ? a.offsets : nullptr, a.n_groups, a.rows, kQM, n_tiles, tile)) return;
 
     const int tid = (int)threadIdx.x, lane = lane_id(), wave = uniform(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const int e = tile.group;
     const int c0 = tile.nt * kCols;
-    const int K = a.K, kblocks = K / kBK;
+    const int K = a.K, kblocks = K / kBK, nq = 2 * kblocks;
     const int fr = lane & 31, half = lane >> 5;
 
-    // activation loads: instruction i (0..3) of wave w fills tile rows 4 (4 w + i) + lane/16,
-    // slot lane % 16 holding logical chunk slot ^ (row & 15); rows past the m-tile load its
-    // first row (never stored)
+    // activation loads: instruction i (0..3) of wave w fills stage rows 8 (4 w + i) + lane / 8,
+    // slot lane % 8 holding chunk slot ^ ((row >> 1) & 7); rows past the m-tile load its first
+    // row (never stored)
     uint32_t aoff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = 4 * (4 * wave + i) + (lane >> 4);
+        const int r = 8 * (4 * wave + i) + (lane >> 3);
         const int p = tile.row0 + r < tile.row1 ? tile.row0 + r : tile.row0;
         const uint32_t src = (kPhase == 1 && kGrouped) ? (uint32_t)(a.perm[p] / a.k) : (uint32_t)p;
-        aoff[i] = src * (uint32_t)(K / 8) + (uint32_t)((lane & 15) ^ (r & 15));
+        aoff[i] = src * (uint32_t)(K / 8) + (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
     }
-    // weight loads: instruction i of wave w fills tile rows 8 (4 w + i) + lane/8, slot lane % 8
-    // holding logical chunk slot ^ ((row >> 1) & 7); phase 1 rows 0..127 gate, 128..255 up
-    const uint8_t* bsrc[4];
+    // weight loads: instruction i (0..1) of wave w fills stage rows 16 (2 w + i) + lane / 4, slot
+    // lane % 4 holding chunk slot ^ ((row >> 2) & 3); phase 1 rows 0..127 gate, 128..255 up
+    const uint8_t* bsrc[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 8 * (4 * wave + i) + (lane >> 3);
+    for (int i = 0; i < 2; ++i) {
+        const int r = 16 * (2 * wave + i) + (lane >> 2);
         const uint8_t* base;
         int wr;
         if (kPhase == 1) {
@@ -290,17 +294,18 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_wide_kernel(GemmArgs a) {
             base = (const uint8_t*)a.w0;
             wr = c0 + r;
         }
-        bsrc[i] = base + ((size_t)e * a.N + wr) * (size_t)K + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+        bsrc[i] = base + ((size_t)e * a.N + wr) * (size_t)K + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
     }
-    auto issue = [&](int kb, int st) {
-        const uint8_t* act = (const uint8_t*)a.act + (size_t)kb * (kBK * 2);
+    auto issue = [&](int q, int st) {
+        const uint8_t* act = (const uint8_t*)a.act + (size_t)q * (kHK * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            lds_dma16(act + (size_t)aoff[i] * 16, &sA[st][4 * (4 * wave + i) * kBK * 2]);
+            lds_dma16(act + (size_t)aoff[i] * 16, &sA[st][8 * (4 * wave + i) * kHK * 2]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            lds_dma16(bsrc[i] + (size_t)kb * kBK, &sB[st][8 * (4 * wave + i) * kBK]);
+        for (int i = 0; i < 2; ++i)
+            lds_dma16(bsrc[i] + (size_t)q * kHK, &sB[st][16 * (2 * wave + i) * kHK]);
     };
+    constexpr int kIssued = 6;  // direct loads per thread per stage
 
     // block scales: phase 1 [0] gate, [1] up of block-row c0/128; phase 2 block-rows c0/128 and
     // c0/128 + 1 (the tile's 256 rows)
@@ -309,44 +314,40 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_wide_kernel(GemmArgs a) {
         sScale[0][tid] = a.s0[srow + tid];
         sScale[1][tid] = kPhase == 1 ? a.s1[srow + tid] : a.s0[srow + kblocks + tid];
     }
-    const int srow0 = kPhase == 1 ? 0 : (wn >> 1);
-    const int srow1 = kPhase == 1 ? 1 : (wn >> 1);
+    const int sg0 = kPhase == 1 ? 0 : (wn >> 1);
+    const int sg1 = kPhase == 1 ? 1 : (wn >> 1);
 
-    const int nvalid = (tile.row1 - tile.row0 + 31) >> 5;
-    const int mine = (nvalid > wm) + (nvalid > wm + 2);
-    // LDS fragment addresses (stage 0; stage 1 is +kStage, an immediate offset).  Chunk c of row
-    // r sits at slot c ^ swz(r).  A: m-subtile mi, k-pair j, step t -> logical chunk 4j + 2h + t;
-    // B: weight subtile ni, k-pair j -> logical chunk 2j + h.
-    int aaddr[2][8], baddr[2][4];
+    const int nvalid = (tile.row1 - tile.row0 + 31) >> 5;  // filled 32-row subtiles (1..8)
+    const int mine = (nvalid > wm) + (nvalid > wm + 2) + (nvalid > wm + 4) + (nvalid > wm + 6);
+    int aaddr[4][4], baddr[2][2];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
+    for (int mi = 0; mi < 4; ++mi) {
         const int r = (wm + 2 * mi) * 32 + fr;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < 4; ++q) {
             const int c = 4 * (q >> 1) + 2 * half + (q & 1);
-            aaddr[mi][q] = r * (kBK * 2) + ((c ^ (r & 15)) << 4);
+            aaddr[mi][q] = r * (kHK * 2) + ((c ^ ((r >> 1) & 7)) << 4);
         }
     }
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
         const int r = (kPhase == 1 ? ni * 128 + wn * 32 : wn * 64 + ni * 32) + fr;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) baddr[ni][j] = r * kBK + (((2 * j + half) ^ ((r >> 1) & 7)) << 4);
+        for (int j = 0; j < 2; ++j) baddr[ni][j] = r * kHK + (((2 * j + half) ^ ((r >> 2) & 3)) << 4);
     }
-    // a zero block scale anywhere in the tile selects the variant that masks that block's codes
     bool any_zero = false;
     __syncthreads();  // scales staged
     for (int b = lane; b < kblocks; b += kWave)
-        any_zero |= sScale[srow0][b] == 0.0f || sScale[srow1][b] == 0.0f;
+        any_zero |= sScale[sg0][b] == 0.0f || sScale[sg1][b] == 0.0f;
     any_zero = __ballot(any_zero) != 0;
 
-    f32x16 acc[2][2];
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.0f;
+            for (int x = 0; x < 16; ++x) acc[mi][ni][x] = 0.0f;
 
     // Block scales are applied by keeping each accumulator in units of the scale of the block
     // being multiplied: before block b it is multiplied by u / s_b (u = the scale of the last
@@ -355,143 +356,145 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_wide_kernel(GemmArgs a) {
     // no separate partial sums.  A zero scale keeps the units and masks that block's codes, so
     // the block adds exactly nothing.
     float u0 = 0.0f, u1 = 0.0f;
+    uint32_t m0 = ~0u, m1 = ~0u;
     auto rescale = [&](float r0, float r1) {
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                acc[mi][0][q] *= r0;
-                acc[mi][1][q] *= r1;
+            for (int x = 0; x < 16; ++x) {
+                acc[mi][0][x] *= r0;
+                acc[mi][1][x] *= r1;
             }
     };
-    // One K block from stage ST with NS filled m-subtiles; kMask: zero-scale blocks are masked.
-    auto block = [&](int kb, auto st_tag, auto ns_tag, auto mask_tag) {
+    // one 64-long stage from ring slot ST with NS filled m-subtiles
+    auto stage = [&](int q, auto st_tag, auto ns_tag, auto mask_tag) {
         constexpr int ST = decltype(st_tag)::value, NS = decltype(ns_tag)::value;
         constexpr bool kMask = decltype(mask_tag)::value;
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        if (q + 1 < nq)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
-        if (kb + 1 < kblocks) issue(kb + 1, ST ^ 1);
+        if (q + 2 < nq) issue(q + 2, (ST + 2) % kStages);
         if (NS == 0) return;
-        const float s0 = sScale[srow0][kb], s1 = sScale[srow1][kb];
-        uint32_t m0 = ~0u, m1 = ~0u;
-        float r0, r1;
-        if (kMask) {
-            const bool z0 = s0 == 0.0f, z1 = s1 == 0.0f;
-            r0 = z0 ? 1.0f : u0 * __builtin_amdgcn_rcpf(s0);
-            r1 = z1 ? 1.0f : u1 * __builtin_amdgcn_rcpf(s1);
-            u0 = z0 ? u0 : s0;
-            u1 = z1 ? u1 : s1;
-            m0 = z0 ? 0u : ~0u;
-            m1 = z1 ? 0u : ~0u;
-        } else {
-            r0 = u0 * __builtin_amdgcn_rcpf(s0);
-            r1 = u1 * __builtin_amdgcn_rcpf(s1);
-            u0 = s0;
-            u1 = s1;
+        if ((q & 1) == 0) {  // first half of scale block q / 2
+            const int kb = q >> 1;
+            const float s0 = sScale[sg0][kb], s1 = sScale[sg1][kb];
+            if (kMask) {
+                const bool z0 = s0 == 0.0f, z1 = s1 == 0.0f;
+                const float r0 = z0 ? 1.0f : u0 * __builtin_amdgcn_rcpf(s0);
+                const float r1 = z1 ? 1.0f : u1 * __builtin_amdgcn_rcpf(s1);
+                u0 = z0 ? u0 : s0;
+                u1 = z1 ? u1 : s1;
+                m0 = z0 ? 0u : ~0u;
+                m1 = z1 ? 0u : ~0u;
+                rescale(r0, r1);
+            } else {
+                rescale(u0 * __builtin_amdgcn_rcpf(s0), u1 * __builtin_amdgcn_rcpf(s1));
+                u0 = s0;
+                u1 = s1;
+            }
         }
-        rescale(r0, r1);
         const uint8_t* A = sA[ST];
         const uint8_t* B = sB[ST];
 #pragma unroll
-        for (int j = 0; j < kBK / 32; ++j) {
-            bf16x8 fa[2][NS > 0 ? NS : 1];
+        for (int j = 0; j < kHK / 32; ++j) {
             u32x4 fbq[2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int mi = 0; mi < NS; ++mi) fa[t][mi] = *(const bf16x8*)&A[aaddr[mi][2 * j + t]];
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni) fbq[ni] = *(const u32x4*)&B[baddr[ni][j]];
-            if (kMask) {
-                fbq[0] &= m0;
-                fbq[1] &= m1;
+            for (int ni = 0; ni < 2; ++ni) {
+                fbq[ni] = *(const u32x4*)&B[baddr[ni][j]];
+                if (kMask) fbq[ni] &= ni == 0 ? m0 : m1;
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                bf16x8 fb[2];
+                bf16x8 fa[NS > 0 ? NS : 1];
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) fb[ni] = fp8x8_to_bf16x8(fbq[ni][2 * t], fbq[ni][2 * t + 1]);
+                for (int mi = 0; mi < NS; ++mi) fa[mi] = *(const bf16x8*)&A[aaddr[mi][2 * j + t]];
 #pragma unroll
-                for (int mi = 0; mi < NS; ++mi)
+                for (int ni = 0; ni < 2; ++ni) {
+                    const bf16x8 fb = fp8x8_to_bf16x8(fbq[ni][2 * t], fbq[ni][2 * t + 1]);
 #pragma unroll
-                    for (int ni = 0; ni < 2; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            fa[t][mi], fb[ni], acc[mi][ni], 0, 0, 0);
+                    for (int mi = 0; mi < NS; ++mi)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb, acc[mi][ni], 0, 0, 0);
+                }
             }
         }
     };
-    // the whole K loop per (filled subtiles, masking): wave-uniform choice made once; every
-    // variant runs the same barriers
     auto run = [&](auto ns_tag, auto mask_tag) {
         using S0 = std::integral_constant<int, 0>;
         using S1 = std::integral_constant<int, 1>;
-        int kb = 0;
-        for (; kb + 1 < kblocks; kb += 2) {
-            block(kb, S0{}, ns_tag, mask_tag);
-            block(kb + 1, S1{}, ns_tag, mask_tag);
+        using S2 = std::integral_constant<int, 2>;
+        for (int q = 0; q < nq; q += 3) {
+            stage(q, S0{}, ns_tag, mask_tag);
+            if (q + 1 < nq) stage(q + 1, S1{}, ns_tag, mask_tag);
+            if (q + 2 < nq) stage(q + 2, S2{}, ns_tag, mask_tag);
         }
-        if (kb < kblocks) block(kb, S0{}, ns_tag, mask_tag);
     };
-    using N0 = std::integral_constant<int, 0>;
-    using N1 = std::integral_constant<int, 1>;
-    using N2 = std::integral_constant<int, 2>;
     using MY = std::integral_constant<bool, true>;
     using MN = std::integral_constant<bool, false>;
 
     issue(0, 0);
-    if (mine == 0)
-        run(N0{}, MN{});
-    else if (any_zero)
-        run(N2{}, MY{});  // rare: computes both subtiles (an unfilled one is never stored)
+    issue(1, 1);  // nq >= 2
+    if (any_zero && mine > 0)
+        run(std::integral_constant<int, 4>{}, MY{});  // rare: all 4 subtiles (unfilled ones are never stored)
+    else if (mine == 4)
+        run(std::integral_constant<int, 4>{}, MN{});
+    else if (mine == 3)
+        run(std::integral_constant<int, 3>{}, MN{});
     else if (mine == 2)
-        run(N2{}, MN{});
+        run(std::integral_constant<int, 2>{}, MN{});
+    else if (mine == 1)
+        run(std::integral_constant<int, 1>{}, MN{});
     else
-        run(N1{}, MN{});
+        run(std::integral_constant<int, 0>{}, MN{});
     rescale(u0, u1);
 
+    // D layout of the 32x32 MFMA: value x of a lane is row 8*(x/4) + 4*(lane/32) + x%4 of the
+    // subtile, column lane%32
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
+    for (int mi = 0; mi < 4; ++mi) {
         if (mi >= mine) break;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int p = tile.row0 + (wm + 2 * mi) * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
+        for (int x = 0; x < 16; ++x) {
+            const int p = tile.row0 + (wm + 2 * mi) * 32 + 8 * (x >> 2) + 4 * half + (x & 3);
             if (p >= tile.row1) continue;
             uint16_t* o = a.out + (size_t)p * a.N + c0 + fr;
             if (kPhase == 1) {
-                const float g = acc[mi][0][q], u = acc[mi][1][q];
+                const float g = acc[mi][0][x], u = acc[mi][1][x];
                 o[wn * 32] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
             } else {
-                o[wn * 64] = f32_to_bf16(acc[mi][0][q]);
-                o[wn * 64 + 32] = f32_to_bf16(acc[mi][1][q]);
+                o[wn * 64] = f32_to_bf16(acc[mi][0][x]);
+                o[wn * 64 + 32] = f32_to_bf16(acc[mi][1][x]);
             }
         }
     }
 }
 
-static moe_status launch_wide(int phase, const GemmArgs& a, hipStream_t st) {
-    const int cols = phase == 1 ? kWBN / 2 : kWBN;
+static moe_status launch_q256(int phase, const GemmArgs& a, hipStream_t st) {
+    const int cols = phase == 1 ? kQN / 2 : kQN;
     const int groups = a.offsets ? a.n_groups : 1;
-    const int64_t mt = ((int64_t)a.rows + kBM - 1) / kBM + std::min<int64_t>(groups, a.rows);
+    const int64_t mt = ((int64_t)a.rows + kQM - 1) / kQM + std::min<int64_t>(groups, a.rows);
     const int64_t wgs = mt * (a.N / cols);
     if (wgs > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((wgs + 7) & ~int64_t(7))), block(512);
     const bool g = a.offsets != nullptr;
     if (phase == 1) {
-        if (g) gemm_fp8_wide_kernel<1, true><<<grid, block, 0, st>>>(a);
-        else gemm_fp8_wide_kernel<1, false><<<grid, block, 0, st>>>(a);
+        if (g) gemm_fp8_q256_kernel<1, true><<<grid, block, 0, st>>>(a);
+        else gemm_fp8_q256_kernel<1, false><<<grid, block, 0, st>>>(a);
     } else {
-        if (g) gemm_fp8_wide_kernel<2, true><<<grid, block, 0, st>>>(a);
-        else gemm_fp8_wide_kernel<2, false><<<grid, block, 0, st>>>(a);
+        if (g) gemm_fp8_q256_kernel<2, true><<<grid, block, 0, st>>>(a);
+        else gemm_fp8_q256_kernel<2, false><<<grid, block, 0, st>>>(a);
     }
     return launch_status();
 }
 
 moe_status launch_gemm(int phase, const GemmArgs& a, hipStream_t st) {
     if (a.K / kBK > kMaxKBlocks) return MOE_ERR_UNSUPPORTED;
-    // the wide kernel addresses activation rows by 32-bit 16-byte chunk indices (up to 64 GB of
-    // activations); beyond that, and for other shapes, the register-staged kernel runs
+    // the direct-to-LDS kernel addresses activation rows by 32-bit 16-byte chunk indices (up to
+    // 64 GB of activations); beyond that, and for H an odd multiple of 128, the register-staged
+    // kernel runs
     const bool chunk32 = (int64_t)a.rows * (a.K / 8) < (int64_t(1) << 32);
-    if (a.fp8 && chunk32 && a.N % (phase == 1 ? kWBN / 2 : kWBN) == 0) return launch_wide(phase, a, st);
+    if (a.fp8 && chunk32 && a.N % (phase == 1 ? kQN / 2 : kQN) == 0) return launch_q256(phase, a, st);
     const int cols = phase == 1 ? kBN / 2 : kBN;
     const int groups = a.offsets ? a.n_groups : 1;
     const int64_t mt = ((int64_t)a.rows + kBM - 1) / kBM + std::min<int64_t>(groups, a.rows);

@@ -106,11 +106,13 @@ def test_skewed_routing_one_hot_expert():
     compare_with_oracle(layer, g)
 
 
-def test_block_scales_zero_and_wide_range():
+@pytest.mark.parametrize("I", [384, 512])
+def test_block_scales_zero_and_wide_range(I):
     """Weight blocks with zero scales and scales spread over six decades, on the grouped-GEMM
-    path (many rows per expert) of the routed and the shared experts; phase 2 has an odd number
-    of 128-long K blocks (I = 384).  A zero scale makes its whole block contribute nothing."""
-    layer = synth.make_layer(mid(T=200, E=8, k=2), seed=5)
+    path (many rows per expert) of the routed and the shared experts (I = 384: phase 2 has an
+    odd number of 128-long K blocks; I = 512: both phases on the 512-row tiles).  A zero scale
+    makes its whole block contribute nothing."""
+    layer = synth.make_layer(mid(T=200, E=8, k=2, I=I), seed=5)
     rng = np.random.default_rng(5)
     for ew in (layer.experts, layer.shared):
         for name in ("s_gate", "s_up", "s_down"):
