@@ -176,17 +176,13 @@ class MoeLayer:
     `experts` and `shared` are objects accepted by expert_weights(); `x` is bf16 bits [T, H]
     (torch.int16) and `scores` fp32 [T, E], all on the GPU.
 
-    overlap_shared: "auto" runs the shared expert on the second stream only when it is a
-    decode-sized matrix-vector pass (T <= 32, the row count up to which libmoe streams the
-    weights instead of running the GEMM); larger shared experts are GEMMs that fill the GPU, and
-    two GEMMs sharing the CUs finish later than the same two in sequence, so they run on the
-    caller's stream after the routed experts.  True / False force either placement.
+    overlap_shared=False runs the shared expert on the caller's stream after the routed experts
+    instead (measured equal or slower at every layer size: the side stream fills CUs left idle
+    by the routing kernels and by the routed GEMMs' last tiles).
     """
 
-    GEMV_MAX_ROWS = 32
-
     def __init__(self, T, H, I, E, k, experts, shared, score_fn="sigmoid", renorm=1, device="cuda",
-                 overlap_shared="auto"):
+                 overlap_shared=True):
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
         self.score_fn, self.renorm = score_fn, renorm
         self.w = expert_weights(experts)
@@ -204,8 +200,6 @@ class MoeLayer:
         self.sh_h = torch.empty((max(1, T), I), dtype=torch.int16, device=d)
         self.sh_y = torch.empty((max(1, T), H), dtype=torch.int16, device=d)
         self.out = torch.empty((max(1, T), H), dtype=torch.int16, device=d)
-        if overlap_shared == "auto":
-            overlap_shared = T <= self.GEMV_MAX_ROWS
         self.side = torch.cuda.Stream(device=d) if (overlap_shared and shared is not None) else None
 
     def forward(self, scores, x, stream=None, gate_up_events=None):
