@@ -15,9 +15,11 @@
 //           offsets[e] + (earlier waves' count of e) + (count of e in this wave's earlier
 //           chunks) + (lower peers in its chunk).
 // The result is the stable order by construction (ascending flat index within each expert).
+// Up to kSmallN assignments one wave does the same in order (moe_permute.h).
 #include "libmoe.h"
 #include "moe_device.h"
 #include "moe_host.h"
+#include "moe_permute.h"
 
 namespace moe {
 
@@ -118,6 +120,38 @@ __global__ __launch_bounds__(kPermWaves * kWave) void permute_kernel(
     }
 }
 
+constexpr int kSmallN = 2048;  // assignments up to which one wave groups them
+
+__global__ __launch_bounds__(kWave) void permute_small_kernel(
+    const int32_t* __restrict__ ids, int n, int E, int nbits, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    permute_wave(ids, n, E, nbits, cnt, counts, offsets, perm, inv);
+}
+
+static moe_status check_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                         const int32_t* counts, const int32_t* offsets, const int32_t* perm,
+                         const int32_t* inv) {
+    if (T < 0 || k < 1 || E < 1) return MOE_ERR_INVALID_ARG;
+    if (E > MOE_MAX_EXPERTS || (int64_t)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!topk_ids || !counts || !offsets || !perm || !inv) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+static moe_status launch_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv, hipStream_t st) {
+    const int n = T * k;
+    const int nbits = ceil_log2(E) > 0 ? ceil_log2(E) : 1;
+    if (n <= kSmallN)
+        permute_small_kernel<<<dim3(1), dim3(kWave), 0, st>>>(topk_ids, n, E, nbits, counts, offsets,
+                                                               perm, inv);
+    else
+        permute_kernel<<<dim3(1), dim3(kPermWaves * kWave), 0, st>>>(topk_ids, n, E, nbits, counts,
+                                                                     offsets, perm, inv);
+    return launch_status();
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -125,12 +159,7 @@ using namespace moe;
 extern "C" moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                                   int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                                   void* stream) {
-    if (T < 0 || k < 1 || E < 1) return MOE_ERR_INVALID_ARG;
-    if (E > MOE_MAX_EXPERTS || (int64_t)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
-    if (T == 0) return MOE_OK;
-    if (!topk_ids || !counts || !offsets || !perm || !inv) return MOE_ERR_INVALID_ARG;
-    const int n = T * k;
-    permute_kernel<<<dim3(1), dim3(kPermWaves * kWave), 0, as_stream(stream)>>>(
-        topk_ids, n, E, ceil_log2(E) > 0 ? ceil_log2(E) : 1, counts, offsets, perm, inv);
-    return launch_status();
+    const moe_status s = check_permute(topk_ids, T, k, E, counts, offsets, perm, inv);
+    if (s != MOE_OK || T == 0) return s;
+    return launch_permute(topk_ids, T, k, E, counts, offsets, perm, inv, as_stream(stream));
 }

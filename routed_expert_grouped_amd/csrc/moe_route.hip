@@ -1,27 +1,10 @@
-// moe_route.hip -- top-k routing: one wave64 per token.
-//
-// The router keeps, per token, the k experts with the largest score and turns their scores into
-// normalised gate weights (sparse MoE FFN with a few active experts per token: CMU 11-868
-// appendix A2 notes, 4.1; DeepSeek-V3 routes each token to 8 of 256 experts: KTransformers
-// article, 1.2; "gating" opens the expert-parallel flow in the OSDI'26 hybrid-inference article,
-// DSLP section).
-//
-// Each lane holds the scores e = lane + 64*i (coalesced loads).  The k winners are found by k
-// rounds of a wave-wide arg-max over (score, -id) -- exact fp32 comparisons, so the selection
-// is bit-identical to any correct top-k with the same tie rule (lower id wins; -0 == +0).
-// Slot j of the result ends up in lane j, which computes its weight in double.
+// moe_route.hip -- top-k routing: one wave64 per token (the routine is in moe_route.h).
 #include "libmoe.h"
 #include "moe_device.h"
 #include "moe_host.h"
+#include "moe_route.h"
 
 namespace moe {
-
-__device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
-    // is candidate a ranked before candidate b?  (an id < 0 marks "no candidate")
-    if (ea < 0) return false;
-    if (eb < 0) return true;
-    return va > vb || (va == vb && ea < eb);
-}
 
 template <int VPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ scores, int T, int E,
@@ -30,68 +13,30 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ sc
                                                     float* __restrict__ wts) {
     const int t = (int)(blockIdx.x * 4 + (threadIdx.x >> 6));
     if (t >= T) return;  // whole waves leave together
-    const int lane = lane_id();
-    const float* s = scores + (size_t)t * E;
-    float v[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int e = lane + kWave * i;
-        v[i] = e < E ? s[e] : 0.0f;
+    route_token<VPL>(scores + (size_t)t * E, E, k, score_fn, renorm, ids + (size_t)t * k,
+                     wts + (size_t)t * k);
+}
+
+static moe_status check_route(const float* scores, int32_t T, int32_t E, int32_t k, int32_t score_fn,
+                       const int32_t* topk_ids, const float* topk_w) {
+    if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+    if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!scores || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+static moe_status launch_route(const float* scores, int32_t T, int32_t E, int32_t k, int32_t score_fn,
+                        int32_t renorm, int32_t* topk_ids, float* topk_w, hipStream_t st) {
+    const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+    switch (route_vpl(E)) {
+#define MOE_ROUTE(V) \
+    case V: route_kernel<V><<<grid, block, 0, st>>>(scores, T, E, k, score_fn, renorm, topk_ids, topk_w); break;
+        MOE_ROUTE(1) MOE_ROUTE(2) MOE_ROUTE(4) MOE_ROUTE(8) MOE_ROUTE(16)
+#undef MOE_ROUTE
     }
-    uint32_t taken = 0;
-    int my_id = -1;
-    float my_s = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        float bv = 0.0f;
-        int be = -1;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int e = lane + kWave * i;
-            if (e < E && !((taken >> i) & 1u) && better(v[i], e, bv, be)) {
-                bv = v[i];
-                be = e;
-            }
-        }
-#pragma unroll
-        for (int off = kWave / 2; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, kWave);
-            const int oe = __shfl_xor(be, off, kWave);
-            if (better(ov, oe, bv, be)) {
-                bv = ov;
-                be = oe;
-            }
-        }
-        if ((be & (kWave - 1)) == lane) taken |= 1u << (be >> 6);
-        if (lane == j) {
-            my_id = be;
-            my_s = bv;
-        }
-    }
-    // gate weights, in double
-    const bool slot = lane < k;
-    double num = 0.0, den_part = 0.0;
-    if (score_fn == MOE_SCORE_SOFTMAX) {
-        const double mx = (double)__shfl(my_s, 0, kWave);  // slot 0 holds the maximum
-        if (slot) num = exp((double)my_s - mx);
-        if (renorm) {
-            den_part = num;
-        } else {
-#pragma unroll
-            for (int i = 0; i < VPL; ++i)
-                if (lane + kWave * i < E) den_part += exp((double)v[i] - mx);
-        }
-    } else {
-        if (slot) num = 1.0 / (1.0 + exp(-(double)my_s));
-        den_part = renorm ? num : 0.0;
-    }
-    double den = den_part;
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) den += __shfl_xor(den, off, kWave);
-    if (score_fn == MOE_SCORE_SIGMOID && !renorm) den = 1.0;
-    if (slot) {
-        ids[(size_t)t * k + lane] = my_id;
-        wts[(size_t)t * k + lane] = (float)(num / den);
-    }
+    return launch_status();
 }
 
 }  // namespace moe
@@ -101,23 +46,7 @@ using namespace moe;
 extern "C" moe_status moe_route(const float* scores, int32_t T, int32_t E, int32_t k,
                                 int32_t score_fn, int32_t renorm, int32_t* topk_ids, float* topk_w,
                                 void* stream) {
-    if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
-    if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
-    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
-    if (T == 0) return MOE_OK;
-    if (!scores || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
-    const dim3 grid((unsigned)((T + 3) / 4)), block(256);
-    hipStream_t st = as_stream(stream);
-    const int vpl = (E + kWave - 1) / kWave;
-    if (vpl <= 1)
-        route_kernel<1><<<grid, block, 0, st>>>(scores, T, E, k, score_fn, renorm, topk_ids, topk_w);
-    else if (vpl <= 2)
-        route_kernel<2><<<grid, block, 0, st>>>(scores, T, E, k, score_fn, renorm, topk_ids, topk_w);
-    else if (vpl <= 4)
-        route_kernel<4><<<grid, block, 0, st>>>(scores, T, E, k, score_fn, renorm, topk_ids, topk_w);
-    else if (vpl <= 8)
-        route_kernel<8><<<grid, block, 0, st>>>(scores, T, E, k, score_fn, renorm, topk_ids, topk_w);
-    else
-        route_kernel<16><<<grid, block, 0, st>>>(scores, T, E, k, score_fn, renorm, topk_ids, topk_w);
-    return launch_status();
+    const moe_status s = check_route(scores, T, E, k, score_fn, topk_ids, topk_w);
+    if (s != MOE_OK || T == 0) return s;
+    return launch_route(scores, T, E, k, score_fn, renorm, topk_ids, topk_w, as_stream(stream));
 }

@@ -110,7 +110,7 @@ def test_skewed_routing_one_hot_expert():
 def test_block_scales_zero_and_wide_range(I):
     """Weight blocks with zero scales and scales spread over six decades, on the grouped-GEMM
     path (many rows per expert) of the routed and the shared experts (I = 384: phase 2 has an
-    odd number of 128-long K blocks; I = 512: both phases on the 512-row tiles).  A zero scale
+    odd number of 128-long K blocks; I = 512: an even number).  A zero scale
     makes its whole block contribute nothing."""
     layer = synth.make_layer(mid(T=200, E=8, k=2, I=I), seed=5)
     rng = np.random.default_rng(5)
@@ -152,7 +152,8 @@ def test_route_ties_and_limits(T, E, k, fn):
 
 
 @pytest.mark.parametrize("T,E,k,skew", [(32768, 256, 8, 0.0), (20000, 256, 8, 2.0),
-                                        (3000, 1024, 4, 0.0), (1, 7, 7, 0.0), (999, 3, 1, 0.0)])
+                                        (3000, 1024, 4, 0.0), (1, 7, 7, 0.0), (999, 3, 1, 0.0),
+                                        (256, 256, 8, 1.0), (2049, 64, 1, 0.0)])
 def test_permute_large_and_skewed(T, E, k, skew):
     ids = synth.random_topk_ids(T, E, k, seed=11, skew=skew)
     c, o, p, i = moe.moe_permute(ids.to(DEV), E)
