@@ -112,7 +112,6 @@ moe_status moe_route(const float* scores, int32_t T, int32_t E, int32_t k, int32
 moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
                        int32_t* offsets, int32_t* perm, int32_t* inv, void* stream);
 
-
 /* Expert phase 1: gate and up projections with the activated product
  * [OSDI "CPU fine-grained parallelism" (gate and up feed act*mul before down), "native FP8
  * GEMV" (E4M3FN, 128-blocks, post-scaling); KT 2.2 (grouped GEMM)].
