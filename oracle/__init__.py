@@ -58,7 +58,13 @@ def lib():
         L.oracle_moe_layer.restype = i32
         L.oracle_moe_layer.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32,
                                        ctypes.POINTER(_Weights), P, ctypes.POINTER(_Weights),
-                                       P, i32, P, P, P, P, P, P, i32]
+                                       P, i32, P, P, P, P, P, P, i32, i32]
+        L.oracle_float_to_e4m3fn.restype = ctypes.c_uint8
+        L.oracle_float_to_e4m3fn.argtypes = [ctypes.c_float]
+        L.oracle_act_scale_exp.restype = i32
+        L.oracle_act_scale_exp.argtypes = [ctypes.c_double]
+        L.oracle_quantize_rows.restype = None
+        L.oracle_quantize_rows.argtypes = [P, i32, i32, P, P]
         L.oracle_max_threads.restype = i32
         L.oracle_max_threads.argtypes = [i32]
         _lib = L
@@ -131,14 +137,33 @@ def _weights(ew, keep):
     return _Weights(wd, n, H, I, *[_ptr(m) for m in mats], *[_ptr(s) for s in scales])
 
 
+def float_to_e4m3fn(v: float) -> int:
+    return lib().oracle_float_to_e4m3fn(float(v))
+
+
+def act_scale_exp(amax: float) -> int:
+    return lib().oracle_act_scale_exp(float(amax))
+
+
+def quantize_rows(x, K: int):
+    """bf16 bits [rows][K] -> (E4M3FN codes uint8 [rows][K], scale exponents int8 [rows][K/128])."""
+    x = _np(x, np.uint16).reshape(-1, K)
+    codes = np.zeros(x.shape, np.uint8)
+    exps = np.zeros((x.shape[0], K // 128), np.int8)
+    lib().oracle_quantize_rows(_ptr(x), x.shape[0], K, _ptr(codes), _ptr(exps))
+    return codes, exps
+
+
 def moe_layer(layer, rows=None, routed=None, expert_slot=None, with_shared=True, want_h=False,
-              want_y=False, n_threads: int = 0):
+              want_y=False, n_threads: int = 0, act_fp8: bool = False):
     """Oracle of the whole layer for token rows `rows` (default: all).
 
     `layer` is a synth.Layer (its tensors may live on any device; they are copied to host).
     `routed` overrides layer.experts with a subset of experts (e.g. the ones the sampled rows
     select, copied from the device), in which case `expert_slot` maps expert id -> slot.
     Returns a dict with ids, w, out (bf16 bits, uint16) and optionally h (uint16), y, S (float64).
+    act_fp8: quantise the activations x and h to E4M3FN in 1x128 blocks first (the FP8 MFMA
+    mode's arithmetic); h is reported before its quantisation.
     """
     keep = []
     scores = _np(layer.scores, np.float32)
@@ -160,7 +185,7 @@ def moe_layer(layer, rows=None, routed=None, expert_slot=None, with_shared=True,
         _ptr(scores), _ptr(x), T, H, I, E, k, SCORE_FN[layer.score_fn], int(layer.renorm),
         ctypes.byref(rw), _ptr(slot), ctypes.byref(sw) if sw is not None else None,
         _ptr(r), n, _ptr(res["ids"]), _ptr(res["w"]), _ptr(res["out"]), _ptr(res.get("h")),
-        _ptr(res.get("y")), _ptr(res.get("S")), int(n_threads))
+        _ptr(res.get("y")), _ptr(res.get("S")), int(n_threads), int(bool(act_fp8)))
     if rc:
         raise ValueError("oracle_moe_layer: invalid arguments (row, k or expert slot)")
     return res

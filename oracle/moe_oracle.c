@@ -36,6 +36,14 @@
  *     sigmoid weights are divided by their sum over the selected k (renorm=1) or used as is;
  *   - the activation is SiLU(g) = g / (1 + exp(-g));
  *   - the permutation is stable: within an expert, assignments keep ascending flat index t*k+j.
+ *
+ * Optional FP8 activations (act_fp8 != 0; the FP8 MFMA mode).  The pages quantise weights in
+ * 128-blocks with a scale per block (the article's "native FP8 GEMV" section); activations are
+ * quantised the same way along the input dimension: per token, per 128 consecutive channels, a
+ * power-of-two scale 2^e with e the smallest integer such that the block's largest magnitude is
+ * at most 448 * 2^e (e clamped to [-127, 127]), codes = E4M3FN round-to-nearest-even of
+ * x * 2^-e computed in fp32.  The gate/up input x and the bf16-rounded h feeding down are both
+ * quantised; everything after dequantisation is exact in double as above.
  */
 #include <math.h>
 #include <stdint.h>
@@ -98,6 +106,64 @@ uint16_t oracle_double_to_bf16(double v) {
 /* Top-k routing of T tokens over E experts.  scores [T][E] fp32 row-major.
  * Outputs ids [T][k] (descending key, ties to the lower id) and weights w [T][k] fp32.
  * score_fn 0 = softmax, 1 = sigmoid. */
+/* E4M3FN code of a float with |v| <= 448, round to nearest, ties to even (OCP definition:
+ * normals 1.m x 2^E for E in [-6, 8] with 3 mantissa bits, subnormals m x 2^-9).  The sign of a
+ * zero is kept (0x80 is -0). */
+uint8_t oracle_float_to_e4m3fn(float v) {
+    const uint8_t sign = signbit(v) ? 0x80 : 0;
+    const double a = fabs((double)v);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);                       /* a in [2^(e2-1), 2^e2) */
+    const int E = e2 - 1;
+    const double q = E < -6 ? ldexp(1.0, -9) : ldexp(1.0, E - 3); /* grid step of a's binade */
+    const double val = rint(a / q) * q;  /* a / q is exact; rint rounds half to even */
+    if (val == 0.0) return sign;
+    if (val < ldexp(1.0, -6)) return sign | (uint8_t)(val / ldexp(1.0, -9));
+    frexp(val, &e2);
+    const int Ev = e2 - 1;
+    const int mant = (int)(val / ldexp(1.0, Ev - 3)) - 8; /* 8..15 -> 0..7 */
+    return sign | (uint8_t)(((Ev + 7) << 3) | mant);
+}
+
+/* Exponent e of the power-of-two scale of an activation block with largest magnitude amax:
+ * the smallest e with amax <= 448 * 2^e = 1.75 * 2^(8+e), clamped to [-127, 127]; 0 for amax 0. */
+int oracle_act_scale_exp(double amax) {
+    if (!(amax > 0.0)) return 0;
+    int e2;
+    const double m = frexp(amax, &e2); /* amax = m 2^e2, m in [0.5, 1) */
+    int e = (m <= 0.875) ? e2 - 9 : e2 - 8;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* Quantises n values (exact in fp32) in place to their dequantised FP8 values, one scale for the
+ * block; returns the scale's exponent.  codes (optional) receives the n codes. */
+static int quantize_block(double* v, int n, uint8_t* codes) {
+    double amax = 0.0;
+    for (int i = 0; i < n; ++i) amax = fmax(amax, fabs(v[i]));
+    const int e = oracle_act_scale_exp(amax);
+    for (int i = 0; i < n; ++i) {
+        const uint8_t c = oracle_float_to_e4m3fn(ldexpf((float)v[i], -e));
+        if (codes) codes[i] = c;
+        v[i] = ldexp(oracle_fp8_e4m3fn_to_double(c), e);
+    }
+    return e;
+}
+
+/* Rows of bf16 values [rows][K] (K a multiple of 128) -> E4M3FN codes [rows][K] and scale
+ * exponents [rows][K/128] (the activation quantisation above). */
+void oracle_quantize_rows(const uint16_t* x, int rows, int K, uint8_t* codes, int8_t* exps) {
+    double v[128];
+    for (int r = 0; r < rows; ++r)
+        for (int b = 0; b < K / 128; ++b) {
+            for (int i = 0; i < 128; ++i) v[i] = oracle_bf16_to_double(x[(size_t)r * K + b * 128 + i]);
+            exps[(size_t)r * (K / 128) + b] =
+                (int8_t)quantize_block(v, 128, codes + (size_t)r * K + b * 128);
+        }
+}
+
 int oracle_route(const float* scores, int T, int E, int k, int score_fn, int renorm,
                  int32_t* ids, float* w) {
     if (k < 1 || k > E) return ORACLE_ERR;
@@ -198,9 +264,11 @@ static double weight(const oracle_weights* W, const void* mat, const float* sc, 
 /* One expert (slot x) on one token row xrow (bf16 bits, length H):
  * h[n] = bf16(SiLU(g_n) * u_n) with g = Wg x, u = Wu x; y = Wd h (double). */
 static void expert_on_token(const oracle_weights* W, int x, const uint16_t* xrow, uint16_t* h_out,
-                            double* y_out, double* xd, double* hd) {
+                            double* y_out, double* xd, double* hd, int act_fp8) {
     const int H = W->H, I = W->I;
     for (int c = 0; c < H; ++c) xd[c] = oracle_bf16_to_double(xrow[c]);
+    if (act_fp8)
+        for (int b = 0; b < H / 128; ++b) quantize_block(xd + b * 128, 128, NULL);
     for (int n = 0; n < I; ++n) {
         double g = 0.0, u = 0.0;
         for (int c = 0; c < H; ++c) {
@@ -212,6 +280,8 @@ static void expert_on_token(const oracle_weights* W, int x, const uint16_t* xrow
         if (h_out) h_out[n] = hb;
         hd[n] = oracle_bf16_to_double(hb);
     }
+    if (act_fp8)
+        for (int b = 0; b < I / 128; ++b) quantize_block(hd + b * 128, 128, NULL);
     for (int c = 0; c < H; ++c) {
         double y = 0.0;
         for (int n = 0; n < I; ++n) y += hd[n] * weight(W, W->down, W->s_down, x, H, I, c, n);
@@ -240,7 +310,7 @@ int oracle_moe_layer(const float* scores, const uint16_t* x, int T, int H, int I
                      const int32_t* expert_slot, const oracle_weights* shared,
                      const int32_t* rows, int n_rows, int32_t* ids_out, float* w_out,
                      uint16_t* out, uint16_t* h_out, double* y_out, double* S_out,
-                     int n_threads) {
+                     int n_threads, int act_fp8) {
     if (routed->H != H || routed->I != I) return ORACLE_ERR;
     if (shared && (shared->H != H || shared->I != I)) return ORACLE_ERR;
     if (rows == NULL) n_rows = T;
@@ -270,11 +340,11 @@ int oracle_moe_layer(const float* scores, const uint16_t* x, int T, int H, int I
             const uint16_t* xrow = x + (size_t)t * H;
             double* S = y + (size_t)k * H;
             for (int c = 0; c < H; ++c) S[c] = 0.0;
-            if (shared) expert_on_token(shared, 0, xrow, NULL, S, xd, hd);
+            if (shared) expert_on_token(shared, 0, xrow, NULL, S, xd, hd, act_fp8);
             for (int j = 0; j < k; ++j) {
                 int slot = expert_slot ? expert_slot[id[j]] : id[j];
                 if (slot < 0 || slot >= routed->n) { set_error(&err); break; }
-                expert_on_token(routed, slot, xrow, hb, y + (size_t)j * H, xd, hd);
+                expert_on_token(routed, slot, xrow, hb, y + (size_t)j * H, xd, hd, act_fp8);
                 if (h_out) memcpy(h_out + ((size_t)i * k + j) * I, hb, sizeof(uint16_t) * I);
             }
             for (int c = 0; c < H; ++c) {

@@ -8,8 +8,13 @@
   and the lecture notes' worked answer for the mean number of tokens per expert;
 * expert FFN + combine: a dense brute force (every expert on every token, masked by its gate
   weight, numpy float64 matrix products, torch's FP8 decode, numpy-expanded scale blocks);
-  the E=1, k=1 textbook SwiGLU case; the identical-experts closed form; k=1 combine.
+  the E=1, k=1 textbook SwiGLU case; the identical-experts closed form; k=1 combine;
+* FP8 activations (the FP8 MFMA mode): the E4M3FN encoder against torch's float8_e4m3fn cast
+  (random values, exact ties, subnormals), the power-of-two block-scale exponent against exact
+  rational arithmetic, the row quantiser against a numpy/torch re-implementation, and the
+  quantised-activation layer against the dense brute force fed with torch-quantised activations.
 """
+from fractions import Fraction
 import numpy as np
 import pytest
 import scipy.special
@@ -183,17 +188,20 @@ def _to_bf16_f64(a):
     return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
 
 
-def _dense_brute_force(layer, ids, w):
-    """Every expert on every token (float64), masked by its gate weight, plus the shared expert."""
+def _dense_brute_force(layer, ids, w, act_fp8=False):
+    """Every expert on every token (float64), masked by its gate weight, plus the shared expert.
+    act_fp8: x and the bf16 h are quantised in 1x128 blocks first (_ref_quantize)."""
     x = torch.from_numpy(oracle._np(layer.x, np.uint16).view(np.int16)).view(torch.bfloat16)
     x = x.to(torch.float64).numpy()
+    if act_fp8:
+        x = _ref_quantize(x)
     Wg, Wu, Wd = _dense_weights(layer.experts, layer.H, layer.I)
     Sg, Su, Sd = _dense_weights(layer.shared, layer.H, layer.I)
 
     def ffn(g, u, d):
         G, U = x @ g.T, x @ u.T
         h = _to_bf16_f64(scipy.special.expit(G) * G * U)  # note: h is exact within fp32 first
-        return h, h @ d.T
+        return h, (_ref_quantize(h) if act_fp8 else h) @ d.T
 
     _, S = ffn(Sg[0], Su[0], Sd[0])
     gate = np.zeros((layer.T, layer.E))
@@ -208,9 +216,9 @@ def _dense_brute_force(layer, ids, w):
     return acc, np.stack(hs, 1), np.stack(ys, 1), S
 
 
-def _check_layer_against_dense(layer):
-    res = oracle.moe_layer(layer, want_h=True, want_y=True)
-    acc, hs, ys, S = _dense_brute_force(layer, res["ids"], res["w"])
+def _check_layer_against_dense(layer, act_fp8=False):
+    res = oracle.moe_layer(layer, want_h=True, want_y=True, act_fp8=act_fp8)
+    acc, hs, ys, S = _dense_brute_force(layer, res["ids"], res["w"], act_fp8)
     T = layer.T
     y_sel = ys[np.arange(T)[:, None], res["ids"]]  # [T, k, H]
     h_sel = hs[np.arange(T)[:, None], res["ids"]]
@@ -302,3 +310,109 @@ def test_layer_row_subset_and_expert_slots_agree_with_full_run():
         slot2 = slot.copy()
         slot2[used[0]] = -1
         oracle.moe_layer(layer, rows=rows, routed=layer.experts.select(used), expert_slot=slot2)
+
+
+# ----------------------------------------------------------------------------- FP8 activations
+
+
+def _e4m3_grid():
+    """All finite non-negative E4M3FN values (float64, ascending), from torch's decode."""
+    v = torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    return np.unique(v.numpy())
+
+
+def _torch_e4m3_codes(v32):
+    return torch.from_numpy(np.ascontiguousarray(v32, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_encoder_matches_torch_cast():
+    grid = _e4m3_grid()
+    mids = (grid[:-1] + grid[1:]) / 2  # exact ties between neighbours
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([grid, mids, rng.uniform(-448, 448, 4000),
+                           rng.uniform(-1, 1, 2000) * 2.0 ** rng.integers(-12, 0, 2000),
+                           -grid, -mids, [0.0, -0.0, 2.0 ** -10, 2.0 ** -11 * 3]]).astype(np.float32)
+    vals = vals[np.abs(vals) <= 448]
+    ours = np.array([oracle.float_to_e4m3fn(float(v)) for v in vals], np.uint8)
+    np.testing.assert_array_equal(ours, _torch_e4m3_codes(vals))
+    # ties go to the even code (the grid step halves at each binade, so check on the codes)
+    t = np.array([oracle.float_to_e4m3fn(float(v)) for v in mids.astype(np.float32)], np.uint8)
+    assert np.all(t % 2 == 0)
+
+
+def _ref_scale_exp(amax):
+    """Smallest integer e with amax <= 448 * 2^e, by exact rational comparison (clamped)."""
+    if amax == 0:
+        return 0
+    a = Fraction(amax)
+    e = -200
+    while a > 448 * Fraction(2) ** e:
+        e += 1
+    return max(-127, min(127, e))
+
+
+def test_activation_scale_exponent_exact():
+    rng = np.random.default_rng(1)
+    cases = [0.0, 448.0, 448.0 * 2 ** -20, 448.0 * 2 ** 30, 1.0, 1e-30, 1e-45, 3e38]
+    cases += list(np.nextafter(np.float32(448.0), np.float32(1e9)) * 2.0 ** np.arange(-5, 5))
+    cases += list(np.nextafter(np.float32(448.0), np.float32(0)) * 2.0 ** np.arange(-5, 5))
+    cases += list(rng.uniform(0, 1, 300) * 10.0 ** rng.integers(-30, 30, 300))
+    for a in cases:
+        a = float(np.float32(a))
+        assert oracle.act_scale_exp(a) == _ref_scale_exp(a), a
+
+
+def _ref_quantize(x, codes_out=None, exps_out=None):
+    """[rows][K] float64 (exact in bf16) -> dequantised values, one power-of-two scale per 1x128
+    block, codes from torch's float8_e4m3fn cast of x * 2^-e computed in float32."""
+    rows, K = x.shape
+    out = np.empty_like(x)
+    for r in range(rows):
+        for b in range(K // 128):
+            blk = x[r, b * 128:(b + 1) * 128]
+            e = _ref_scale_exp(float(np.max(np.abs(blk))))
+            v = np.ldexp(blk.astype(np.float32), np.int32(-e)).astype(np.float32)
+            c = _torch_e4m3_codes(v)
+            out[r, b * 128:(b + 1) * 128] = np.ldexp(
+                torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy(), e)
+            if codes_out is not None:
+                codes_out[r, b * 128:(b + 1) * 128] = c
+                exps_out[r, b] = e
+    return out
+
+
+def test_quantize_rows_matches_reference():
+    rng = np.random.default_rng(2)
+    rows, K = 6, 512
+    x = rng.standard_normal((rows, K)) * 10.0 ** rng.integers(-8, 8, (rows, K // 128)).repeat(128, 1)
+    x[1, 128:256] = 0.0                       # an all-zero block
+    x[2, 256:384] = 0.0
+    x[2, 300] = -3.5                          # a single nonzero
+    x[3, :128] = 448.0 * 2.0 ** 3             # amax exactly at a scale boundary
+    bits = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    xb = oracle.bf16_bits_to_float(bits)
+    codes, exps = oracle.quantize_rows(bits, K)
+    rc = np.zeros((rows, K), np.uint8)
+    re = np.zeros((rows, K // 128), np.int64)
+    deq = _ref_quantize(xb, rc, re)
+    np.testing.assert_array_equal(codes, rc)
+    np.testing.assert_array_equal(exps.astype(np.int64), re)
+    # round to nearest: within half a grid step, i.e. 2^-4 relative for normal codes
+    nz = np.abs(xb) >= 2.0 ** -6 * 2.0 ** re.repeat(128, 1)
+    assert np.all(np.abs(deq - xb)[nz] <= 2.0 ** -4 * np.abs(xb)[nz])
+    # every nonzero block's largest magnitude lands in (224, 448] after scaling
+    for r in range(rows):
+        for b in range(K // 128):
+            m = np.max(np.abs(xb[r, b * 128:(b + 1) * 128]))
+            if m > 0:
+                assert 224 < m * 2.0 ** -re[r, b] <= 448
+
+
+def test_ffn_fp8_activations_dense_brute_force():
+    layer = synth.make_layer(dict(T=24, H=384, I=256, E=6, k=3, score_fn="sigmoid", scores="uniform",
+                                  wdtype="fp8"), seed=4)
+    res = _check_layer_against_dense(layer, act_fp8=True)
+    # the quantisation changes the result (it is not silently skipped)
+    plain = oracle.moe_layer(layer, act_fp8=False)
+    assert np.any(plain["out"] != res["out"])
