@@ -17,7 +17,6 @@ host.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -69,12 +68,14 @@ def layer_flops(T, H, I, k, shared=True) -> int:
 # ------------------------------------------------------------------ counter-derived traffic
 
 def kernel_sources(kernel: str) -> list:
-    """Sources (relative to the repository root) that a libmoe kernel is built from: every file
-    of csrc/, less the other expert path's kernel file."""
-    files = sorted(os.path.relpath(p, ROOT) for p in
-                   glob.glob(os.path.join(ROOT, "routed_expert_grouped_amd", "csrc", "*")))
-    other = "moe_gemm.hip" if "gemv_kernel" in kernel else None
-    return [f for f in files if os.path.basename(f) != other]
+    """Sources (relative to the repository root) of the translation units a libmoe gate/up
+    kernel is compiled in: moe_ffn.hip (GEMV kernels and the launches) and, for the GEMM
+    kernels, moe_gemm.hip, with the headers both include."""
+    names = ["moe_device.h", "moe_ffn.h", "moe_ffn.hip", "moe_host.h"]
+    if "gemv_kernel" not in kernel:
+        names.append("moe_gemm.hip")
+    return sorted(os.path.join("routed_expert_grouped_amd", "csrc", n) for n in names) + \
+        [os.path.join("include", "libmoe.h")]
 
 
 def source_digest(files) -> str:

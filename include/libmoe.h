@@ -153,6 +153,39 @@ moe_status moe_expert_ffn(const uint16_t* x, int32_t T, int32_t k, const int32_t
                           const int32_t* offsets, const moe_expert_weights* w, uint16_t* y,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- FP8 activation mode (A8W8)
+ * [OSDI "native FP8 GEMV", Figures 9-10] quantises weights to E4M3FN with one scale per
+ * 128-element block.  This opt-in mode quantises the activations the same way along the
+ * contraction dimension, so that both operands of each expert GEMM are E4M3FN (the form the
+ * gfx950 FP8 matrix instructions take):
+ *   per row, per 128 consecutive values v: e = the smallest integer with max|v| <= 448 * 2^e,
+ *   clamped to [-127, 127] (e = 0 for an all-zero block); code = E4M3FN(v * 2^-e), rounded to
+ *   nearest even in fp32; the block then stands for code * 2^e exactly.
+ * Scales are powers of two (E8M0 numbers), so the codes never overflow and dequantisation is
+ * exact; only the rounding to a 3-bit mantissa differs from the bf16 path. */
+
+/* Quantise a bf16 [rows][K] matrix row by row in 128-blocks (as above).
+ *   codes : uint8 [rows][K] out, E4M3FN bit patterns (same layout as x).
+ *   exps  : int8 [rows][K/128] out, the block exponents e (scale = 2^e).
+ * Errors: INVALID_ARG for rows < 0, K < 1, null or unaligned pointers; UNSUPPORTED when K is
+ * not a multiple of 128 or rows * K/128 >= 2^31.  rows == 0 enqueues nothing. */
+moe_status moe_quantize_act(const uint16_t* x, int32_t rows, int32_t K, uint8_t* codes,
+                            int8_t* exps, void* stream);
+
+/* Bytes of workspace moe_expert_ffn_a8 needs (host output). */
+moe_status moe_expert_ffn_a8_workspace_size(int32_t T, int32_t k, const moe_expert_weights* w,
+                                            size_t* bytes);
+
+/* Both expert phases with FP8 activations: x is quantised per token before the gate/up
+ * projection and h (after its bf16 rounding) per assignment before the down projection, as
+ * above; everything else is as in moe_expert_ffn (same arguments, same y layout, same errors).
+ * The workspace holds the quantised x, then h (bf16 [T*k][I], before its quantisation,
+ * starting at byte (T*H*2 rounded up to 256)), then the quantised h.  Only FP8 weights
+ * (MOE_W_FP8_E4M3_B128) are accepted (UNSUPPORTED otherwise). */
+moe_status moe_expert_ffn_a8(const uint16_t* x, int32_t T, int32_t k, const int32_t* perm,
+                             const int32_t* offsets, const moe_expert_weights* w, uint16_t* y,
+                             void* ws, size_t ws_bytes, void* stream);
+
 /* Weighted combine [OSDI DSLP section "weighted reduction"; KT 1.2 shared expert]:
  *     out[t][c] = bf16_rne( S[t][c] + sum_{j=0..k-1} w[t][j] * y[inv[t*k+j]][c] )
  * accumulated in fp32 in that order (S first, then j ascending).

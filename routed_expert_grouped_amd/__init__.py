@@ -21,7 +21,8 @@ MOE_W_FP8_E4M3_B128, MOE_W_BF16 = 0, 1
 SCORE_FN = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
 
 EXPORTS = ("moe_route", "moe_permute", "moe_expert_gate_up", "moe_expert_down",
-           "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine", "moe_status_string")
+           "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine", "moe_quantize_act",
+           "moe_expert_ffn_a8_workspace_size", "moe_expert_ffn_a8", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -58,6 +59,10 @@ def lib():
         L.moe_expert_ffn_workspace_size.argtypes = [i32, i32, W, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_expert_ffn.argtypes = [P, i32, i32, P, P, W, P, P, ctypes.c_size_t, P]
         L.moe_combine.argtypes = [P, P, P, P, i32, i32, i32, P, P]
+        L.moe_quantize_act.argtypes = [P, i32, i32, P, P, P]
+        L.moe_expert_ffn_a8_workspace_size.argtypes = [i32, i32, W,
+                                                       ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_expert_ffn_a8.argtypes = [P, i32, i32, P, P, W, P, P, ctypes.c_size_t, P]
         for name in EXPORTS[:-1]:
             getattr(L, name).restype = st
         L.moe_status_string.argtypes = [st]
@@ -168,6 +173,45 @@ def moe_combine(y, inv, topk_w, shared_y, T: int, k: int, H: int, out=None, stre
     return out
 
 
+def moe_quantize_act(x, codes=None, exps=None, stream=None):
+    """FP8 activation quantisation of bf16 bits x [rows, K]: (codes uint8 [rows, K], exps int8
+    [rows, K/128])."""
+    rows, K = x.shape
+    if codes is None:
+        codes = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    if exps is None:
+        exps = torch.empty((rows, max(1, K // 128)), dtype=torch.int8, device=x.device)
+    _check("moe_quantize_act", lib().moe_quantize_act(_p(x), rows, K, _p(codes), _p(exps),
+                                                      _s(stream)))
+    return codes, exps
+
+
+def moe_expert_ffn_a8_workspace_size(T: int, k: int, w: MoeExpertWeights) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_expert_ffn_a8_workspace_size",
+           lib().moe_expert_ffn_a8_workspace_size(T, k, ctypes.byref(w), ctypes.byref(n)))
+    return n.value
+
+
+def a8_h_offset(T: int, H: int) -> int:
+    """Byte offset of h (before its quantisation) in moe_expert_ffn_a8's workspace."""
+    return (T * H * 2 + 255) // 256 * 256
+
+
+def moe_expert_ffn_a8(x, k: int, perm, offsets, w: MoeExpertWeights, y=None, ws=None,
+                      stream=None):
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T * k, w.H), dtype=torch.int16, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(1, moe_expert_ffn_a8_workspace_size(T, k, w)), dtype=torch.uint8,
+                         device=x.device)
+    _check("moe_expert_ffn_a8", lib().moe_expert_ffn_a8(
+        _p(x), T, k, _p(perm), _p(offsets), ctypes.byref(w), _p(y), _p(ws), ws.numel(),
+        _s(stream)))
+    return y, ws
+
+
 class MoeLayer:
     """Buffers and the call sequence of one MoE layer forward: route -> permute -> routed
     gate/up -> routed down -> combine on the caller's stream, and the shared expert (which only
@@ -179,11 +223,17 @@ class MoeLayer:
     overlap_shared=False runs the shared expert on the caller's stream after the routed experts
     instead (measured equal or slower at every layer size: the side stream fills CUs left idle
     by the routing kernels and by the routed GEMMs' last tiles).
+
+    act="fp8" selects the FP8 activation mode (moe_expert_ffn_a8) for the routed and the shared
+    experts; `h` then views the routed h inside the workspace, before its quantisation.
     """
 
     def __init__(self, T, H, I, E, k, experts, shared, score_fn="sigmoid", renorm=1, device="cuda",
-                 overlap_shared=True):
+                 overlap_shared=True, act="bf16"):
+        if act not in ("bf16", "fp8"):
+            raise ValueError(f"act must be 'bf16' or 'fp8', not {act!r}")
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
+        self.act = act
         self.score_fn, self.renorm = score_fn, renorm
         self.w = expert_weights(experts)
         self.ws_ = expert_weights(shared) if shared is not None else None
@@ -195,36 +245,52 @@ class MoeLayer:
         self.offsets = torch.empty(E + 1, dtype=i32, device=d)
         self.perm = torch.empty(max(1, T * k), dtype=i32, device=d)
         self.inv = torch.empty(max(1, T * k), dtype=i32, device=d)
-        self.h = torch.empty((max(1, T * k), I), dtype=torch.int16, device=d)
+        if act == "fp8":
+            self.ws = torch.empty(max(1, moe_expert_ffn_a8_workspace_size(T, k, self.w)),
+                                  dtype=torch.uint8, device=d)
+            self.sh_ws = (torch.empty(max(1, moe_expert_ffn_a8_workspace_size(T, 1, self.ws_)),
+                                      dtype=torch.uint8, device=d) if shared is not None else None)
+            at = a8_h_offset(T, H)
+            self.h = self.ws[at:at + max(1, T * k) * I * 2].view(torch.int16).view(-1, I)
+        else:
+            self.h = torch.empty((max(1, T * k), I), dtype=torch.int16, device=d)
         self.y = torch.empty((max(1, T * k), H), dtype=torch.int16, device=d)
         self.sh_h = torch.empty((max(1, T), I), dtype=torch.int16, device=d)
         self.sh_y = torch.empty((max(1, T), H), dtype=torch.int16, device=d)
         self.out = torch.empty((max(1, T), H), dtype=torch.int16, device=d)
         self.side = torch.cuda.Stream(device=d) if (overlap_shared and shared is not None) else None
 
+    def _shared(self, x, st):
+        if self.act == "fp8":
+            moe_expert_ffn_a8(x, 1, None, None, self.ws_, self.sh_y, self.sh_ws, st)
+        else:
+            moe_expert_gate_up(x, 1, None, None, self.ws_, self.sh_h, st)
+            moe_expert_down(self.sh_h, self.T, 1, None, self.ws_, self.sh_y, st)
+
     def forward(self, scores, x, stream=None, gate_up_events=None):
         """Enqueue the layer; returns `out` (bf16 bits [T, H]).  gate_up_events=(start, stop)
-        records torch events around the routed gate/up kernel (for timing)."""
+        records torch events around the routed gate/up kernel (for timing; bf16 mode only)."""
         T, k = self.T, self.k
         main = torch.cuda.current_stream() if stream is None else stream
         shared_y = None
         if self.ws_ is not None and self.side is not None:
             # shared expert on the side stream, ordered after everything already on `main`
             self.side.wait_stream(main)
-            moe_expert_gate_up(x, 1, None, None, self.ws_, self.sh_h, self.side)
-            moe_expert_down(self.sh_h, T, 1, None, self.ws_, self.sh_y, self.side)
+            self._shared(x, self.side)
             shared_y = self.sh_y
         moe_route(scores, k, self.score_fn, self.renorm, self.topk_ids, self.topk_w, stream)
         moe_permute(self.topk_ids, self.E, self.counts, self.offsets, self.perm, self.inv, stream)
-        if gate_up_events is not None:
-            gate_up_events[0].record(stream)
-        moe_expert_gate_up(x, k, self.perm, self.offsets, self.w, self.h, stream)
-        if gate_up_events is not None:
-            gate_up_events[1].record(stream)
-        moe_expert_down(self.h, T, k, self.offsets, self.w, self.y, stream)
+        if self.act == "fp8":
+            moe_expert_ffn_a8(x, k, self.perm, self.offsets, self.w, self.y, self.ws, stream)
+        else:
+            if gate_up_events is not None:
+                gate_up_events[0].record(stream)
+            moe_expert_gate_up(x, k, self.perm, self.offsets, self.w, self.h, stream)
+            if gate_up_events is not None:
+                gate_up_events[1].record(stream)
+            moe_expert_down(self.h, T, k, self.offsets, self.w, self.y, stream)
         if self.ws_ is not None and self.side is None:
-            moe_expert_gate_up(x, 1, None, None, self.ws_, self.sh_h, stream)
-            moe_expert_down(self.sh_h, T, 1, None, self.ws_, self.sh_y, stream)
+            self._shared(x, stream)
             shared_y = self.sh_y
         elif self.side is not None:
             main.wait_stream(self.side)

@@ -6,15 +6,38 @@ import torch
 
 import oracle
 import routed_expert_grouped_amd as moe
+import synth
 
 ROW_TOL = 1e-2  # per-row relative L2 bound on float outputs (h, y, shared, out)
 W_TOL = 1e-6  # absolute bound on the routing weights
+DEV = "cuda"
+
+_layers = {}
 
 
-def run_gpu(layer, stream=None):
+def layer_for(cfg, seed=0, **over):
+    """Layers are cached per session (the large ones share their weights across configs)."""
+    key = (cfg if isinstance(cfg, str) else tuple(sorted(cfg.items())), seed, tuple(sorted(over.items())))
+    if key not in _layers:
+        c = synth.CONFIGS[cfg] if isinstance(cfg, str) else cfg
+        big = c["H"] * c["I"] * c["E"] > 1 << 26
+        if big:
+            _layers[key] = synth.make_layer(cfg, seed=seed, device=DEV, **over)
+        else:  # small layers are drawn on the host, then copied
+            _layers[key] = synth.make_layer(cfg, seed=seed, **over).to(DEV)
+    return _layers[key]
+
+
+def mid(**over):
+    c = dict(T=200, H=512, I=384, E=24, k=4, score_fn="sigmoid", scores="uniform", wdtype="fp8")
+    c.update(over)
+    return c
+
+
+def run_gpu(layer, stream=None, act="bf16"):
     """Run the full layer through the C ABI; return host copies of every intermediate."""
     L = moe.MoeLayer(layer.T, layer.H, layer.I, layer.E, layer.k, layer.experts, layer.shared,
-                     layer.score_fn, layer.renorm)
+                     layer.score_fn, layer.renorm, act=act)
     L.forward(layer.scores, layer.x, stream)
     torch.cuda.synchronize()
     T, k = layer.T, layer.k
@@ -41,10 +64,11 @@ def assert_rows_close(name, got, ref, tol=ROW_TOL):
     return float(r.max())
 
 
-def compare_with_oracle(layer, g, rows=None, routed=None, expert_slot=None, n_threads=0):
+def compare_with_oracle(layer, g, rows=None, routed=None, expert_slot=None, n_threads=0,
+                        act_fp8=False):
     """Check GPU results `g` against the oracle on token rows `rows` (default all)."""
     ref = oracle.moe_layer(layer, rows=rows, routed=routed, expert_slot=expert_slot,
-                           want_h=True, want_y=True, n_threads=n_threads)
+                           want_h=True, want_y=True, n_threads=n_threads, act_fp8=act_fp8)
     T, k = layer.T, layer.k
     r = np.arange(T) if rows is None else np.asarray(rows)
     # routing: ids bit-exact, weights within W_TOL
@@ -72,10 +96,10 @@ def touched_experts(layer, g, rows):
     return sorted(set(g["ids"][np.asarray(rows)].ravel().tolist()))
 
 
-def compare_sampled(layer, g, rows, n_threads=0):
+def compare_sampled(layer, g, rows, n_threads=0, act_fp8=False):
     """Oracle on a few token rows of a large layer: only the experts they select are copied."""
     used = touched_experts(layer, g, rows)
     slot = np.full(layer.E, -1, np.int32)
     slot[used] = np.arange(len(used), dtype=np.int32)
     return compare_with_oracle(layer, g, rows=rows, routed=layer.experts.select(used),
-                               expert_slot=slot, n_threads=n_threads)
+                               expert_slot=slot, n_threads=n_threads, act_fp8=act_fp8)

@@ -113,6 +113,47 @@ def test_ffn_workspace():
     assert L.moe_expert_ffn(FAKE, 0, 2, FAKE, FAKE, ctypes.byref(w), FAKE, None, 0, None) == moe.MOE_OK
 
 
+def test_quantize_act_validation():
+    q = moe.lib().moe_quantize_act
+    assert q(None, 4, 256, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(FAKE, 4, 256, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(FAKE, 4, 256, FAKE, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(ctypes.c_void_p(0x1002), 4, 256, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(FAKE, -1, 256, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(FAKE, 4, 0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(FAKE, 4, 200, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert q(FAKE, 1 << 30, 1024, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert q(None, 0, 256, None, None, None) == moe.MOE_OK
+
+
+def test_ffn_a8_validation():
+    L = moe.lib()
+    w = _w(H=256, I=384)
+    n = ctypes.c_size_t()
+    assert L.moe_expert_ffn_a8_workspace_size(16, 2, ctypes.byref(w), ctypes.byref(n)) == moe.MOE_OK
+    # quantised x [T][H], h and quantised h [T*k][I], bf16, each part 256-byte aligned
+    assert n.value == 16 * 256 * 2 + 2 * (32 * 384 * 2)
+    assert moe.a8_h_offset(16, 256) == 16 * 256 * 2
+    assert moe.a8_h_offset(3, 128) == 768
+    f = L.moe_expert_ffn_a8
+    assert f(FAKE, 16, 2, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, n.value - 1,
+             None) == moe.MOE_ERR_WORKSPACE
+    assert f(FAKE, 16, 2, FAKE, FAKE, ctypes.byref(w), FAKE, None, n.value,
+             None) == moe.MOE_ERR_WORKSPACE
+    assert f(FAKE, 16, 2, FAKE, FAKE, ctypes.byref(w), None, FAKE, n.value,
+             None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 16, 2, FAKE, FAKE, ctypes.byref(w), FAKE, ctypes.c_void_p(0x1008), n.value,
+             None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 16, 2, None, FAKE, ctypes.byref(w), FAKE, FAKE, n.value,
+             None) == moe.MOE_ERR_INVALID_ARG
+    bf16 = _w(dtype=1, scales=False)
+    assert f(FAKE, 16, 2, FAKE, FAKE, ctypes.byref(bf16), FAKE, FAKE, 1 << 30,
+             None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(FAKE, 16, 0, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, n.value,
+             None) == moe.MOE_ERR_INVALID_ARG
+    assert f(None, 0, 2, None, None, None, None, None, 0, None) == moe.MOE_OK
+
+
 def test_combine_validation():
     L = moe.lib()
     c = L.moe_combine

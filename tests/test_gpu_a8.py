@@ -1,0 +1,111 @@
+"""GPU parity of the FP8 activation mode (E4M3FN activations in 1x128 blocks with power-of-two
+scales) against the oracle's model of the same arithmetic.
+
+Bars: codes and block exponents bit-exact; h, y, the shared expert's output and the layer output
+within the same 1e-2 relative L2 per row as the bf16 mode.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routed_expert_grouped_amd as moe
+from gpu_util import (DEV, compare_sampled, compare_with_oracle, layer_for, mid, rel_l2_rows,
+                      run_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_bits(v):
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.bfloat16).view(torch.int16)
+
+
+def _quant_inputs():
+    """Rows of 512 values (4 blocks) that reach every branch of the quantiser."""
+    rng = np.random.default_rng(7)
+    rows = []
+    # magnitudes over the whole bf16 range, one decade per row
+    for p in range(-130, 128, 6):
+        rows.append(rng.standard_normal(512) * 2.0 ** p)
+    # heavy tails inside a block: small values become E4M3 subnormals or zero
+    rows.append(rng.standard_normal(512) * np.exp2(rng.integers(-30, 4, 512)))
+    b = np.zeros(512)  # an all-zero block, a single nonzero, signed zeros, the 448 boundary
+    b[128] = 3.0
+    b[256:384] = -0.0
+    b[384], b[385], b[386] = 448.0, -1.0, 0.01
+    rows.append(b)
+    c = np.zeros(512)
+    c[0:128] = 450.0  # just above 448: the next exponent
+    c[128:256] = np.linspace(-448, 448, 128)
+    c[256:384] = 2.0 ** -133  # bf16's smallest subnormal: the exponent clamps at -127
+    c[384:512] = 3.0e38  # near bf16's largest finite value
+    rows.append(c)
+    # values halfway between two E4M3 codes (ties to even), of both signs
+    m = rng.integers(0, 8, 512)
+    e = rng.integers(-6, 9, 512)
+    t = (1 + (2 * m + 1) / 16.0) * 2.0 ** e * rng.choice([-1.0, 1.0], 512)
+    t[::128] = 448.0  # fixes the block scale at 2^0
+    rows.append(t)
+    return _bf16_bits(np.stack(rows))
+
+
+def test_quantize_act_bit_exact():
+    x = _quant_inputs()
+    codes, exps = moe.moe_quantize_act(x.to(DEV))
+    torch.cuda.synchronize()
+    rc, re_ = oracle.quantize_rows(x.numpy().view(np.uint16), x.shape[1])
+    np.testing.assert_array_equal(exps.cpu().numpy(), re_)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    assert re_.min() == -127 and (rc == 0x80).any()  # the clamp and a signed zero were reached
+
+
+def test_quantize_act_ragged_row_counts():
+    """Row counts that leave the last workgroup partly idle (4 blocks per workgroup)."""
+    rng = np.random.default_rng(3)
+    for rows, K in ((1, 128), (3, 384), (5, 7168), (37, 2048)):
+        x = _bf16_bits(rng.standard_normal((rows, K)) * 10)
+        codes, exps = moe.moe_quantize_act(x.to(DEV))
+        torch.cuda.synchronize()
+        rc, re_ = oracle.quantize_rows(x.numpy().view(np.uint16), K)
+        np.testing.assert_array_equal(exps.cpu().numpy(), re_)
+        np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
+@pytest.mark.parametrize("cfg", ["tiny_fp8", mid(), mid(T=37, E=64, k=8),
+                                 mid(T=160, H=640, E=8, k=2), mid(T=300, E=4, k=1,
+                                                                  score_fn="softmax")])
+def test_a8_layer(cfg):
+    layer = layer_for(cfg, seed=1)
+    g = run_gpu(layer, act="fp8")
+    compare_with_oracle(layer, g, act_fp8=True)
+
+
+def test_a8_is_not_the_bf16_path():
+    """The FP8 mode's outputs sit much closer to the oracle's FP8 model than to its bf16 one."""
+    layer = layer_for(mid(), seed=1)
+    g = run_gpu(layer, act="fp8")
+    f = oracle.bf16_bits_to_float
+    a8 = oracle.moe_layer(layer, act_fp8=True)
+    bf = oracle.moe_layer(layer, act_fp8=False)
+    d_a8 = np.median(rel_l2_rows(f(g["out"]), f(a8["out"])))
+    d_bf = np.median(rel_l2_rows(f(g["out"]), f(bf["out"])))
+    assert d_bf > 1e-2 and d_a8 < d_bf / 10, (d_a8, d_bf)
+
+
+def test_a8_dsv3_decode_full():
+    layer = layer_for("dsv3_decode")
+    g = run_gpu(layer, act="fp8")
+    compare_sampled(layer, g, rows=list(range(layer.T)), act_fp8=True)
+
+
+def test_a8_dsv3_prefill_sampled_rows():
+    layer = layer_for("dsv3_prefill")
+    g = run_gpu(layer, act="fp8")
+    compare_sampled(layer, g, rows=[0, 1, 2048, 4095], act_fp8=True)
+
+
+def test_a8_rejects_bf16_weights():
+    layer = layer_for("tiny")
+    with pytest.raises(moe.MoeError) as ei:
+        run_gpu(layer, act="fp8")
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED

@@ -10,33 +10,9 @@ import torch
 import oracle
 import routed_expert_grouped_amd as moe
 import synth
-from gpu_util import compare_sampled, compare_with_oracle, run_gpu
+from gpu_util import DEV, compare_sampled, compare_with_oracle, layer_for, mid, run_gpu
 
 pytestmark = pytest.mark.gpu
-
-DEV = "cuda"
-
-_layers = {}
-
-
-def layer_for(cfg, seed=0, **over):
-    """Layers are cached per session (the large ones share their weights across configs)."""
-    key = (cfg if isinstance(cfg, str) else tuple(sorted(cfg.items())), seed, tuple(sorted(over.items())))
-    if key not in _layers:
-        c = synth.CONFIGS[cfg] if isinstance(cfg, str) else cfg
-        big = c["H"] * c["I"] * c["E"] > 1 << 26
-        if big:
-            _layers[key] = synth.make_layer(cfg, seed=seed, device=DEV, **over)
-        else:  # small layers are drawn on the host, then copied
-            _layers[key] = synth.make_layer(cfg, seed=seed, **over).to(DEV)
-    return _layers[key]
-
-
-def mid(**over):
-    c = dict(T=200, H=512, I=384, E=24, k=4, score_fn="sigmoid", scores="uniform", wdtype="fp8")
-    c.update(over)
-    return c
-
 
 # ------------------------------------------------------------------ number formats and layouts
 
