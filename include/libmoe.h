@@ -179,9 +179,11 @@ moe_status moe_expert_ffn_a8_workspace_size(int32_t T, int32_t k, const moe_expe
 /* Both expert phases with FP8 activations: x is quantised per token before the gate/up
  * projection and h (after its bf16 rounding) per assignment before the down projection, as
  * above; everything else is as in moe_expert_ffn (same arguments, same y layout, same errors).
- * The workspace holds the quantised x, then h (bf16 [T*k][I], before its quantisation,
- * starting at byte (T*H*2 rounded up to 256)), then the quantised h.  Only FP8 weights
- * (MOE_W_FP8_E4M3_B128) are accepted (UNSUPPORTED otherwise). */
+ * With many rows per expert both operands of each expert GEMM are FP8 codes and the activation
+ * scales are applied by the matrix instruction; otherwise the activations are dequantised
+ * exactly to bf16 first (same values up to the order of fp32 sums).  The workspace begins with
+ * h (bf16 [T*k][I], before its quantisation); the rest holds the quantised activations.  Only
+ * FP8 weights (MOE_W_FP8_E4M3_B128) are accepted (UNSUPPORTED otherwise). */
 moe_status moe_expert_ffn_a8(const uint16_t* x, int32_t T, int32_t k, const int32_t* perm,
                              const int32_t* offsets, const moe_expert_weights* w, uint16_t* y,
                              void* ws, size_t ws_bytes, void* stream);

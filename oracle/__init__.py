@@ -58,7 +58,7 @@ def lib():
         L.oracle_moe_layer.restype = i32
         L.oracle_moe_layer.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32,
                                        ctypes.POINTER(_Weights), P, ctypes.POINTER(_Weights),
-                                       P, i32, P, P, P, P, P, P, i32, i32]
+                                       P, i32, P, P, P, P, P, P, i32, i32, P]
         L.oracle_float_to_e4m3fn.restype = ctypes.c_uint8
         L.oracle_float_to_e4m3fn.argtypes = [ctypes.c_float]
         L.oracle_act_scale_exp.restype = i32
@@ -161,7 +161,8 @@ def moe_layer(layer, rows=None, routed=None, expert_slot=None, with_shared=True,
     `layer` is a synth.Layer (its tensors may live on any device; they are copied to host).
     `routed` overrides layer.experts with a subset of experts (e.g. the ones the sampled rows
     select, copied from the device), in which case `expert_slot` maps expert id -> slot.
-    Returns a dict with ids, w, out (bf16 bits, uint16) and optionally h (uint16), y, S (float64).
+    Returns a dict with ids, w, out (bf16 bits, uint16) and optionally h and, with a shared
+    expert, hS (its h) (uint16), y, S (float64).
     act_fp8: quantise the activations x and h to E4M3FN in 1x128 blocks first (the FP8 MFMA
     mode's arithmetic); h is reported before its quantisation.
     """
@@ -178,6 +179,8 @@ def moe_layer(layer, rows=None, routed=None, expert_slot=None, with_shared=True,
                out=np.zeros((n, H), np.uint16))
     if want_h:
         res["h"] = np.zeros((n, k, I), np.uint16)
+        if sw is not None:
+            res["hS"] = np.zeros((n, I), np.uint16)
     if want_y:
         res["y"] = np.zeros((n, k, H), np.float64)
         res["S"] = np.zeros((n, H), np.float64)
@@ -185,7 +188,8 @@ def moe_layer(layer, rows=None, routed=None, expert_slot=None, with_shared=True,
         _ptr(scores), _ptr(x), T, H, I, E, k, SCORE_FN[layer.score_fn], int(layer.renorm),
         ctypes.byref(rw), _ptr(slot), ctypes.byref(sw) if sw is not None else None,
         _ptr(r), n, _ptr(res["ids"]), _ptr(res["w"]), _ptr(res["out"]), _ptr(res.get("h")),
-        _ptr(res.get("y")), _ptr(res.get("S")), int(n_threads), int(bool(act_fp8)))
+        _ptr(res.get("y")), _ptr(res.get("S")), int(n_threads), int(bool(act_fp8)),
+        _ptr(res.get("hS")))
     if rc:
         raise ValueError("oracle_moe_layer: invalid arguments (row, k or expert slot)")
     return res

@@ -303,14 +303,14 @@ static void set_error(int* err) {
  *   shared: the shared expert (slot 0, gate weight 1) or NULL.
  * Outputs for row i (all optional except out):
  *   ids [i][k], w [i][k], out [i][H] bf16 bits, h [i][k][I] bf16 bits, y [i][k][H] double,
- *   S [i][H] double (shared expert output).
+ *   S [i][H] double (shared expert output), hS [i][I] bf16 bits (the shared expert's h).
  * out = bf16( S + sum_j w_j * y_j ), accumulated in double in the order S, j = 0..k-1. */
 int oracle_moe_layer(const float* scores, const uint16_t* x, int T, int H, int I, int E, int k,
                      int score_fn, int renorm, const oracle_weights* routed,
                      const int32_t* expert_slot, const oracle_weights* shared,
                      const int32_t* rows, int n_rows, int32_t* ids_out, float* w_out,
                      uint16_t* out, uint16_t* h_out, double* y_out, double* S_out,
-                     int n_threads, int act_fp8) {
+                     int n_threads, int act_fp8, uint16_t* hS_out) {
     if (routed->H != H || routed->I != I) return ORACLE_ERR;
     if (shared && (shared->H != H || shared->I != I)) return ORACLE_ERR;
     if (rows == NULL) n_rows = T;
@@ -340,7 +340,9 @@ int oracle_moe_layer(const float* scores, const uint16_t* x, int T, int H, int I
             const uint16_t* xrow = x + (size_t)t * H;
             double* S = y + (size_t)k * H;
             for (int c = 0; c < H; ++c) S[c] = 0.0;
-            if (shared) expert_on_token(shared, 0, xrow, NULL, S, xd, hd, act_fp8);
+            if (shared)
+                expert_on_token(shared, 0, xrow, hS_out ? hS_out + (size_t)i * I : NULL, S, xd, hd,
+                                act_fp8);
             for (int j = 0; j < k; ++j) {
                 int slot = expert_slot ? expert_slot[id[j]] : id[j];
                 if (slot < 0 || slot >= routed->n) { set_error(&err); break; }

@@ -193,11 +193,6 @@ def moe_expert_ffn_a8_workspace_size(T: int, k: int, w: MoeExpertWeights) -> int
     return n.value
 
 
-def a8_h_offset(T: int, H: int) -> int:
-    """Byte offset of h (before its quantisation) in moe_expert_ffn_a8's workspace."""
-    return (T * H * 2 + 255) // 256 * 256
-
-
 def moe_expert_ffn_a8(x, k: int, perm, offsets, w: MoeExpertWeights, y=None, ws=None,
                       stream=None):
     T = x.shape[0]
@@ -248,14 +243,17 @@ class MoeLayer:
         if act == "fp8":
             self.ws = torch.empty(max(1, moe_expert_ffn_a8_workspace_size(T, k, self.w)),
                                   dtype=torch.uint8, device=d)
-            self.sh_ws = (torch.empty(max(1, moe_expert_ffn_a8_workspace_size(T, 1, self.ws_)),
-                                      dtype=torch.uint8, device=d) if shared is not None else None)
-            at = a8_h_offset(T, H)
-            self.h = self.ws[at:at + max(1, T * k) * I * 2].view(torch.int16).view(-1, I)
+            # h (before its quantisation) opens the workspace
+            self.h = self.ws[:max(1, T * k) * I * 2].view(torch.int16).view(-1, I)
+            self.sh_ws = self.sh_h = None
+            if shared is not None:
+                self.sh_ws = torch.empty(max(1, moe_expert_ffn_a8_workspace_size(T, 1, self.ws_)),
+                                         dtype=torch.uint8, device=d)
+                self.sh_h = self.sh_ws[:max(1, T) * I * 2].view(torch.int16).view(-1, I)
         else:
             self.h = torch.empty((max(1, T * k), I), dtype=torch.int16, device=d)
+            self.sh_h = torch.empty((max(1, T), I), dtype=torch.int16, device=d)
         self.y = torch.empty((max(1, T * k), H), dtype=torch.int16, device=d)
-        self.sh_h = torch.empty((max(1, T), I), dtype=torch.int16, device=d)
         self.sh_y = torch.empty((max(1, T), H), dtype=torch.int16, device=d)
         self.out = torch.empty((max(1, T), H), dtype=torch.int16, device=d)
         self.side = torch.cuda.Stream(device=d) if (overlap_shared and shared is not None) else None

@@ -25,6 +25,10 @@ struct GemmArgs {
     const float* s1;
     bool fp8;
     uint16_t* out;  // [rows][N]
+    // FP8 activation mode only: act holds E4M3FN codes [rows of act][K] (one byte each) and
+    // aexp their block scales as E8M0 bytes (127 + e), [rows of act][aexp_pitch]
+    const uint8_t* aexp;
+    int aexp_pitch;
 };
 
 // gemv shape: m-tiles of 16 rows; kGemvWaves waves per workgroup, each wave owning 16 h-columns
@@ -40,5 +44,11 @@ constexpr int kGemvWaves = MOE_GEMV_WAVES;
 inline bool use_gemv(int rows, int n_groups) { return rows <= 32 * n_groups; }
 
 moe_status launch_gemm(int phase, const GemmArgs& a, hipStream_t st);
+
+// FP8 activation mode: the GEMM on FP8 codes of both operands, for the shapes a8_gemm_fits
+// accepts (FP8 weights, many rows per expert, K <= kA8MaxK, N a multiple of the tile's columns).
+constexpr int kA8MaxK = 8192;
+bool a8_gemm_fits(int phase, const GemmArgs& a);
+moe_status launch_gemm_a8(int phase, const GemmArgs& a, hipStream_t st);
 
 }  // namespace moe

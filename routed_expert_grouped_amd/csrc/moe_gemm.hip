@@ -22,6 +22,7 @@
 #include "moe_device.h"
 #include "moe_ffn.h"
 #include "moe_host.h"
+#include "moe_lds.h"
 
 #include <type_traits>
 
@@ -216,21 +217,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
             }
         }
     }
-}
-
-// ------------------------------------------------------------------ helpers of the direct-to-LDS loads
-
-// s_waitcnt immediate that waits until at most n vector-memory loads are outstanding (gfx9
-// encoding: vmcnt in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
-// One direct global -> LDS load of 16 bytes per lane: lane l's bytes land at lds + 16 * l.
-__device__ __forceinline__ void lds_dma16(const void* src, const void* lds) {
-    const uint32_t addr = (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)lds;
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(addr))
-                 : "memory", "m0");
 }
 
 constexpr int kHK = 64;  // K per stage of the direct-to-LDS kernel (half a scale block)

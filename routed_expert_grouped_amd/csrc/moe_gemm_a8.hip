@@ -1,0 +1,320 @@
+// moe_gemm_a8.hip -- grouped expert GEMMs with FP8 activations, on gfx950's scaled FP8 matrix
+// instruction.
+//
+// Both operands are E4M3FN codes.  The weights carry one fp32 scale per 128x128 block (the
+// OSDI'26 hybrid-inference article, "native FP8 GEMV", Figures 9-10).  The activations carry one
+// power-of-two scale 2^e per row and 128-long K block, stored as the E8M0 byte 127 + e.
+// v_mfma_scale_f32_32x32x64_f8f6f4 multiplies 32x64 by 64x32 codes and applies an E8M0 scale per
+// row of A itself, so the activation scales cost no instructions.  The weight scales are
+// applied to each 128-long block's sum as in the bf16-operand GEMM: the accumulator is kept in
+// units of the current block's scale.
+//
+// Tiles as in the bf16-operand GEMM of moe_gemm.hip: one 8-wave workgroup per CU computes a
+// 256-row m-tile against 256 weight rows (phase 1: 128 gate + the same 128 up rows -> 128 h
+// columns; phase 2: 256 y columns).  K goes in 64-long stages (16 KB of activation codes +
+// 16 KB of weight codes) through a 4-stage ring.  Loads go directly to LDS three stages ahead.
+// The tile's activation exponents (256 rows x up to 64 blocks) are loaded to LDS once, ahead of
+// the first stage.
+//
+// MFMA operand layout (32x32x64, 32 bytes a lane): lane l supplies row l % 32 of A (column
+// l % 32 of B); its bytes 0-15 are K values [16 h, 16 h + 16) and bytes 16-31 are
+// [32 + 16 h, 48 + 16 h) of the 64-long step, h = l / 32.  Rows of a stage are 64 bytes in LDS,
+// four 16-byte chunks, chunk c at slot c ^ ((row >> 2) & 3), so the fragment reads (chunks h and
+// 2 + h of 32 consecutive rows) are free of bank conflicts.
+#include "libmoe.h"
+#include "moe_device.h"
+#include "moe_ffn.h"
+#include "moe_host.h"
+#include "moe_lds.h"
+
+#include <type_traits>
+
+namespace moe {
+
+typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));
+
+constexpr int kA8M = 256;                     // rows per m-tile
+constexpr int kA8N = 256;                     // weight rows per tile
+constexpr int kA8K = 64;                      // K per stage: one MFMA step, half a scale block
+constexpr int kA8Stages = 4;                  // ring depth
+constexpr int kA8MaxBlocks = kA8MaxK / 128;  // exponent bytes per row staged in LDS
+constexpr int kE8M0One = 127;                 // E8M0 encoding of 1.0
+
+__device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
+    i32x8 r = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    return r;
+}
+
+template <int kPhase, bool kGrouped>
+__global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
+    constexpr int kStage = kA8M * kA8K;  // 16 KB; the weight stage is the same size
+    static_assert(kA8N * kA8K == kStage, "A and B stages share one layout");
+    __shared__ __attribute__((aligned(1024))) uint8_t sA[kA8Stages][kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB[kA8Stages][kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t sE[kA8M * kA8MaxBlocks];  // [row][pitch]
+    __shared__ float sScale[2][kA8MaxBlocks];
+
+    constexpr int kCols = kPhase == 1 ? kA8N / 2 : kA8N;
+    Tile tile;
+    if (!find_tile(kGrouped ? a.offsets : nullptr, a.n_groups, a.rows, kA8M, a.N / kCols, tile))
+        return;
+
+    const int tid = (int)threadIdx.x, lane = lane_id(), wave = uniform(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int e = tile.group;
+    const int c0 = tile.nt * kCols;
+    const int K = a.K, kblocks = K / 128, nq = 2 * kblocks;
+    const int pitch = a.aexp_pitch;  // a multiple of 16 in [kblocks, kA8MaxBlocks]
+    const int fr = lane & 31, half = lane >> 5;
+    const uint8_t* act = (const uint8_t*)a.act;
+
+    // source row (token, or grouped row) of tile row r; rows past the m-tile read its first row
+    // (never stored), so every load is unconditional
+    auto src_row = [&](int r) -> uint32_t {
+        const int p = tile.row0 + r < tile.row1 ? tile.row0 + r : tile.row0;
+        return (kPhase == 1 && kGrouped) ? (uint32_t)(a.perm[p] / a.k) : (uint32_t)p;
+    };
+    // stage loads: instruction i (0..1) of wave w fills rows 16 (2 w + i) + lane / 4 of the A
+    // and the B stage, slot lane % 4 holding chunk slot ^ ((row >> 2) & 3); activation sources
+    // in 16-byte units (32 bits: the host keeps the codes below 64 GB)
+    uint32_t aoff[2];
+    const uint8_t* bsrc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = 16 * (2 * wave + i) + (lane >> 2);
+        const uint32_t chunk = (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
+        aoff[i] = src_row(r) * (uint32_t)(K / 16) + chunk;
+        const uint8_t* base;
+        int wr;
+        if (kPhase == 1) {
+            base = (const uint8_t*)(r < 128 ? a.w0 : a.w1);
+            wr = c0 + (r & 127);
+        } else {
+            base = (const uint8_t*)a.w0;
+            wr = c0 + r;
+        }
+        bsrc[i] = base + ((size_t)e * a.N + wr) * (size_t)K + (chunk << 4);
+    }
+    // exponent rows: 16-byte chunk c = tid + 512 j of the tile's 256 x pitch bytes (row c / cpr,
+    // part c % cpr) lands at sE + 16 c, i.e. row-major with the global pitch
+    const int cpr = pitch >> 4;
+    const int echunks = kA8M * cpr;  // a multiple of 256: whole waves issue or skip a load
+    uint32_t eoff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int c = tid + 512 * j;
+        const int r = c < echunks ? c / cpr : 0;
+        eoff[j] = src_row(r) * (uint32_t)cpr + (uint32_t)(c - r * cpr);
+    }
+    auto issue = [&](int q, int st) {
+        const uint8_t* aq = act + (size_t)q * kA8K;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            lds_dma16(aq + (size_t)aoff[i] * 16, &sA[st][16 * (2 * wave + i) * kA8K]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            lds_dma16(bsrc[i] + (size_t)q * kA8K, &sB[st][16 * (2 * wave + i) * kA8K]);
+    };
+    constexpr int kIssued = 4;  // direct loads per thread per stage
+
+    // weight block scales: phase 1 [0] gate, [1] up of block-row c0/128; phase 2 block-rows
+    // c0/128 and c0/128 + 1 (the tile's 256 rows)
+    if (tid < kblocks) {
+        const size_t srow = ((size_t)e * (a.N / 128) + c0 / 128) * kblocks;
+        sScale[0][tid] = a.s0[srow + tid];
+        sScale[1][tid] = kPhase == 1 ? a.s1[srow + tid] : a.s0[srow + kblocks + tid];
+    }
+    const int sg0 = kPhase == 1 ? 0 : (wn >> 1);
+    const int sg1 = kPhase == 1 ? 1 : (wn >> 1);
+
+    const int nvalid = (tile.row1 - tile.row0 + 31) >> 5;  // filled 32-row subtiles (1..8)
+    const int mine = (nvalid > wm) + (nvalid > wm + 2) + (nvalid > wm + 4) + (nvalid > wm + 6);
+    int aaddr[4][2], baddr[2][2], eaddr[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int r = (wm + 2 * mi) * 32 + fr;
+        eaddr[mi] = r * pitch;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) aaddr[mi][j] = r * kA8K + (((2 * j + half) ^ ((r >> 2) & 3)) << 4);
+    }
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+        const int r = (kPhase == 1 ? ni * 128 + wn * 32 : wn * 64 + ni * 32) + fr;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) baddr[ni][j] = r * kA8K + (((2 * j + half) ^ ((r >> 2) & 3)) << 4);
+    }
+    bool any_zero = false;
+    __syncthreads();  // weight scales staged
+    for (int b = lane; b < kblocks; b += kWave)
+        any_zero |= sScale[sg0][b] == 0.0f || sScale[sg1][b] == 0.0f;
+    any_zero = __ballot(any_zero) != 0;
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) acc[mi][ni][x] = 0.0f;
+
+    // Weight block scales by Horner (as in moe_gemm.hip): before block b the accumulator is
+    // multiplied by u / s_b (u = the scale of the last block with a nonzero scale), the block's
+    // MFMAs add into it, and the end multiplies by u.  A zero scale keeps the units and masks
+    // that block's weight codes, so the block adds exactly nothing.
+    float u0 = 0.0f, u1 = 0.0f;
+    uint32_t m0 = ~0u, m1 = ~0u;
+    int sc[4] = {kE8M0One, kE8M0One, kE8M0One, kE8M0One};  // E8M0 activation scales of the block
+    auto rescale = [&](float r0, float r1) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                acc[mi][0][x] *= r0;
+                acc[mi][1][x] *= r1;
+            }
+    };
+    // one 64-long stage from ring slot ST with NS filled m-subtiles
+    auto stage = [&](int q, auto st_tag, auto ns_tag, auto mask_tag) {
+        constexpr int ST = decltype(st_tag)::value, NS = decltype(ns_tag)::value;
+        constexpr bool kMask = decltype(mask_tag)::value;
+        if (q + 2 < nq)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kIssued));
+        else if (q + 1 < nq)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        if (q + 3 < nq) issue(q + 3, (ST + 3) % kA8Stages);
+        if (NS == 0) return;
+        if ((q & 1) == 0) {  // first half of scale block q / 2
+            const int kb = q >> 1;
+            const float s0 = sScale[sg0][kb], s1 = sScale[sg1][kb];
+            if (kMask) {
+                const bool z0 = s0 == 0.0f, z1 = s1 == 0.0f;
+                const float r0 = z0 ? 1.0f : u0 * __builtin_amdgcn_rcpf(s0);
+                const float r1 = z1 ? 1.0f : u1 * __builtin_amdgcn_rcpf(s1);
+                u0 = z0 ? u0 : s0;
+                u1 = z1 ? u1 : s1;
+                m0 = z0 ? 0u : ~0u;
+                m1 = z1 ? 0u : ~0u;
+                rescale(r0, r1);
+            } else {
+                rescale(u0 * __builtin_amdgcn_rcpf(s0), u1 * __builtin_amdgcn_rcpf(s1));
+                u0 = s0;
+                u1 = s1;
+            }
+#pragma unroll
+            for (int mi = 0; mi < NS; ++mi) sc[mi] = sE[eaddr[mi] + kb];
+        }
+        const uint8_t* A = sA[ST];
+        const uint8_t* B = sB[ST];
+        i32x8 fb[2];
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+            u32x4 lo = *(const u32x4*)&B[baddr[ni][0]];
+            u32x4 hi = *(const u32x4*)&B[baddr[ni][1]];
+            if (kMask) {
+                lo &= ni == 0 ? m0 : m1;
+                hi &= ni == 0 ? m0 : m1;
+            }
+            fb[ni] = join(lo, hi);
+        }
+#pragma unroll
+        for (int mi = 0; mi < NS; ++mi) {
+            const i32x8 fa = join(*(const u32x4*)&A[aaddr[mi][0]], *(const u32x4*)&A[aaddr[mi][1]]);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    fa, fb[ni], acc[mi][ni], 0, 0, 0, sc[mi], 0, kE8M0One);
+        }
+    };
+    auto run = [&](auto ns_tag, auto mask_tag) {
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        using S2 = std::integral_constant<int, 2>;
+        using S3 = std::integral_constant<int, 3>;
+        for (int q = 0; q < nq; q += 4) {
+            stage(q, S0{}, ns_tag, mask_tag);
+            if (q + 1 < nq) stage(q + 1, S1{}, ns_tag, mask_tag);
+            if (q + 2 < nq) stage(q + 2, S2{}, ns_tag, mask_tag);
+            if (q + 3 < nq) stage(q + 3, S3{}, ns_tag, mask_tag);
+        }
+    };
+    using MY = std::integral_constant<bool, true>;
+    using MN = std::integral_constant<bool, false>;
+
+    // exponents first (the first stage's wait covers them), then three stages
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        if (512 * j + 64 * wave < echunks)
+            lds_dma16(a.aexp + (size_t)eoff[j] * 16, &sE[16 * (512 * j + 64 * wave)]);
+    issue(0, 0);
+    issue(1, 1);  // nq >= 2
+    if (nq > 2) issue(2, 2);
+    if (any_zero && mine > 0)
+        run(std::integral_constant<int, 4>{}, MY{});  // rare: all 4 subtiles (unfilled ones are never stored)
+    else if (mine == 4)
+        run(std::integral_constant<int, 4>{}, MN{});
+    else if (mine == 3)
+        run(std::integral_constant<int, 3>{}, MN{});
+    else if (mine == 2)
+        run(std::integral_constant<int, 2>{}, MN{});
+    else if (mine == 1)
+        run(std::integral_constant<int, 1>{}, MN{});
+    else
+        run(std::integral_constant<int, 0>{}, MN{});
+    rescale(u0, u1);
+
+    // D layout of the 32x32 MFMA: value x of a lane is row 8*(x/4) + 4*(lane/32) + x%4 of the
+    // subtile, column lane%32
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        if (mi >= mine) break;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            const int p = tile.row0 + (wm + 2 * mi) * 32 + 8 * (x >> 2) + 4 * half + (x & 3);
+            if (p >= tile.row1) continue;
+            uint16_t* o = a.out + (size_t)p * a.N + c0 + fr;
+            if (kPhase == 1) {
+                const float g = acc[mi][0][x], u = acc[mi][1][x];
+                o[wn * 32] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+            } else {
+                o[wn * 64] = f32_to_bf16(acc[mi][0][x]);
+                o[wn * 64 + 32] = f32_to_bf16(acc[mi][1][x]);
+            }
+        }
+    }
+}
+
+bool a8_gemm_fits(int phase, const GemmArgs& a) {
+    if (!a.fp8 || use_gemv(a.rows, a.n_groups)) return false;
+    if (a.K % 128 != 0 || a.K > kA8MaxK) return false;
+    if (a.N % (phase == 1 ? kA8N / 2 : kA8N) != 0) return false;
+    if (a.aexp_pitch % 16 != 0 || a.aexp_pitch < a.K / 128 || a.aexp_pitch > kA8MaxBlocks)
+        return false;
+    // activation rows: tokens (phase 1) or grouped rows (phase 2), addressed in 16-byte units
+    const int64_t src_rows = phase == 1 ? a.rows / a.k : a.rows;
+    return src_rows * (a.K / 16) < (int64_t(1) << 32);
+}
+
+moe_status launch_gemm_a8(int phase, const GemmArgs& a, hipStream_t st) {
+    if (!a8_gemm_fits(phase, a)) return MOE_ERR_UNSUPPORTED;
+    const int cols = phase == 1 ? kA8N / 2 : kA8N;
+    const int groups = a.offsets ? a.n_groups : 1;
+    const int64_t mt = ((int64_t)a.rows + kA8M - 1) / kA8M + std::min<int64_t>(groups, a.rows);
+    const int64_t wgs = mt * (a.N / cols);
+    if (wgs > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    const dim3 grid((unsigned)((wgs + 7) & ~int64_t(7))), block(512);
+    const bool g = a.offsets != nullptr;
+    if (phase == 1) {
+        if (g) gemm_a8_kernel<1, true><<<grid, block, 0, st>>>(a);
+        else gemm_a8_kernel<1, false><<<grid, block, 0, st>>>(a);
+    } else {
+        if (g) gemm_a8_kernel<2, true><<<grid, block, 0, st>>>(a);
+        else gemm_a8_kernel<2, false><<<grid, block, 0, st>>>(a);
+    }
+    return launch_status();
+}
+
+}  // namespace moe

@@ -14,6 +14,8 @@
 
 namespace moe {
 
+constexpr int kE8M0Bias = 127;  // E8M0 byte of 2^e: 127 + e
+
 // exponent e of the block scale for largest magnitude amax (see the file comment)
 __device__ __forceinline__ int act_scale_exp(float amax) {
     if (!(amax > 0.0f)) return 0;
@@ -23,13 +25,13 @@ __device__ __forceinline__ int act_scale_exp(float amax) {
     return min(127, max(-127, e));
 }
 
-// One wave per (row, 128-block): lane l holds values 2l and 2l+1.  Writes the codes and the
-// exponent (either may be null) and, if deq is not null, the dequantised values as bf16 (exact:
+// One wave per (row, 128-block): lane l holds values 2l and 2l+1.  Writes any of: the codes, the
+// exponent (as exp_bias + e, exps[r * exp_pitch + b]) and the dequantised values as bf16 (exact:
 // a 4-bit significand times a power of two).
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int rows,
                                                        int K, uint8_t* __restrict__ codes,
-                                                       int8_t* __restrict__ exps,
-                                                       uint16_t* __restrict__ deq) {
+                                                       uint8_t* __restrict__ exps, int exp_pitch,
+                                                       int exp_bias, uint16_t* __restrict__ deq) {
     const uint32_t nb = (uint32_t)K / 128;  // the launch keeps rows * nb below 2^31
     const uint32_t blk = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (blk >= (uint32_t)rows * nb) return;  // whole waves leave together
@@ -44,20 +46,69 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     const int e = act_scale_exp(amax);
     const int c2 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v0, -e), ldexpf(v1, -e), 0, false);
     if (codes) *(uint16_t*)(codes + at) = (uint16_t)c2;
-    if (exps && lane == 0) exps[(size_t)r * nb + b] = (int8_t)e;
+    if (exps && lane == 0) exps[(size_t)r * exp_pitch + b] = (uint8_t)(exp_bias + e);
     if (deq) {
         const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c2, ldexpf(1.0f, e), false);
         *(bf16x2*)(deq + at) = d;
     }
 }
 
-moe_status launch_quantize(const uint16_t* x, int64_t rows, int K, uint8_t* codes, int8_t* exps,
-                           uint16_t* deq, hipStream_t st) {
+moe_status launch_quantize(const uint16_t* x, int64_t rows, int K, uint8_t* codes, uint8_t* exps,
+                           int exp_pitch, int exp_bias, uint16_t* deq, hipStream_t st) {
     const int64_t blocks = rows * (K / 128);
     if (blocks > INT32_MAX) return MOE_ERR_UNSUPPORTED;
-    quantize_kernel<<<dim3((unsigned)((blocks + 3) / 4)), dim3(256), 0, st>>>(x, (int)rows, K, codes,
-                                                                              exps, deq);
+    quantize_kernel<<<dim3((unsigned)((blocks + 3) / 4)), dim3(256), 0, st>>>(
+        x, (int)rows, K, codes, exps, exp_pitch, exp_bias, deq);
     return launch_status();
+}
+
+// The FP8 activation mode's expert FFN.  Each phase runs the FP8-code GEMM when its shape fits
+// (moe_gemm_a8.hip); otherwise (few rows per expert, or shapes outside that kernel) the
+// activations are dequantised exactly to bf16 and the bf16-operand kernels run, which gives the
+// same values up to the order of the fp32 sums.
+struct A8Plan {
+    int T, k, H, I;
+    bool fp8_1, fp8_2;   // phase runs on FP8 codes
+    int pitch_h, pitch_i;  // exponent row pitches (bytes)
+    size_t h, x1, x1e, h2, h2e, size;  // workspace offsets and total
+};
+
+static size_t a8_part(size_t bytes) { return (bytes + 255) & ~size_t(255); }
+
+static GemmArgs a8_args(int phase, int T, int k, const moe_expert_weights* w) {
+    GemmArgs a{};
+    a.k = k;
+    a.rows = T * k;
+    a.n_groups = w->n_groups;
+    a.N = phase == 1 ? w->I : w->H;
+    a.K = phase == 1 ? w->H : w->I;
+    a.fp8 = w->dtype == MOE_W_FP8_E4M3_B128;
+    a.aexp_pitch = (a.K / 128 + 15) & ~15;
+    return a;
+}
+
+static A8Plan a8_plan(int T, int k, const moe_expert_weights* w) {
+    A8Plan p{};
+    p.T = T, p.k = k, p.H = w->H, p.I = w->I;
+    const GemmArgs a1 = a8_args(1, T, k, w), a2 = a8_args(2, T, k, w);
+    p.fp8_1 = a8_gemm_fits(1, a1);
+    p.fp8_2 = a8_gemm_fits(2, a2);
+    p.pitch_h = a1.aexp_pitch;
+    p.pitch_i = a2.aexp_pitch;
+    const size_t rows = (size_t)T * k;
+    size_t at = 0;
+    p.h = at;
+    at += a8_part(rows * w->I * 2);
+    p.x1 = at;  // x as codes (+ exponents) or as dequantised bf16
+    at += p.fp8_1 ? a8_part((size_t)T * w->H) : a8_part((size_t)T * w->H * 2);
+    p.x1e = at;
+    at += p.fp8_1 ? a8_part((size_t)T * p.pitch_h) : 0;
+    p.h2 = at;  // h as codes (+ exponents) or as dequantised bf16
+    at += p.fp8_2 ? a8_part(rows * w->I) : a8_part(rows * w->I * 2);
+    p.h2e = at;
+    at += p.fp8_2 ? a8_part(rows * p.pitch_i) : 0;
+    p.size = at;
+    return p;
 }
 
 }  // namespace moe
@@ -72,12 +123,9 @@ extern "C" moe_status moe_quantize_act(const uint16_t* x, int32_t rows, int32_t 
     if ((int64_t)rows * (K / 128) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     if (!x || !codes || !exps || !aligned16(x) || !aligned16(codes) || !aligned16(exps))
         return MOE_ERR_INVALID_ARG;
-    return launch_quantize(x, rows, K, codes, exps, nullptr, as_stream(stream));
+    return launch_quantize(x, rows, K, codes, reinterpret_cast<uint8_t*>(exps), K / 128, 0,
+                           nullptr, as_stream(stream));
 }
-
-// Workspace of moe_expert_ffn_a8: dequantised x [T][H] bf16, h [T*k][I] bf16, dequantised h
-// [T*k][I] bf16, each part 256-byte aligned.
-static size_t a8_part(size_t bytes) { return (bytes + 255) & ~size_t(255); }
 
 extern "C" moe_status moe_expert_ffn_a8_workspace_size(int32_t T, int32_t k,
                                                        const moe_expert_weights* w, size_t* bytes) {
@@ -85,8 +133,8 @@ extern "C" moe_status moe_expert_ffn_a8_workspace_size(int32_t T, int32_t k,
     moe_status s = check_weights(w);
     if (s != MOE_OK) return s;
     if (T < 0 || k < 1) return MOE_ERR_INVALID_ARG;
-    const size_t rows = (size_t)T * k;
-    *bytes = a8_part((size_t)T * w->H * 2) + 2 * a8_part(rows * w->I * 2);
+    if ((int64_t)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    *bytes = a8_plan(T, k, w).size;
     return MOE_OK;
 }
 
@@ -106,15 +154,48 @@ extern "C" moe_status moe_expert_ffn_a8(const uint16_t* x, int32_t T, int32_t k,
     const int64_t rows = (int64_t)T * k;
     if (rows * (w->I / 128) > INT32_MAX || (int64_t)T * (w->H / 128) > INT32_MAX)
         return MOE_ERR_UNSUPPORTED;
+    const A8Plan p = a8_plan(T, k, w);
     hipStream_t st = as_stream(stream);
-    uint8_t* p = static_cast<uint8_t*>(ws);
-    uint16_t* xq = reinterpret_cast<uint16_t*>(p);
-    p += a8_part((size_t)T * w->H * 2);
-    uint16_t* h = reinterpret_cast<uint16_t*>(p);
-    p += a8_part((size_t)rows * w->I * 2);
-    uint16_t* hq = reinterpret_cast<uint16_t*>(p);
-    if ((s = launch_quantize(x, T, w->H, nullptr, nullptr, xq, st)) != MOE_OK) return s;
-    if ((s = moe_expert_gate_up(xq, T, k, perm, offsets, w, h, stream)) != MOE_OK) return s;
-    if ((s = launch_quantize(h, rows, w->I, nullptr, nullptr, hq, st)) != MOE_OK) return s;
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    uint16_t* h = reinterpret_cast<uint16_t*>(base + p.h);
+    // phase 1: x -> h
+    if (p.fp8_1) {
+        GemmArgs a = a8_args(1, T, k, w);
+        uint8_t* codes = base + p.x1;
+        uint8_t* e8 = base + p.x1e;
+        if ((s = launch_quantize(x, T, w->H, codes, e8, p.pitch_h, kE8M0Bias, nullptr, st)) != MOE_OK)
+            return s;
+        a.act = reinterpret_cast<const uint16_t*>(codes);
+        a.aexp = e8;
+        a.perm = perm;
+        a.offsets = offsets;
+        a.w0 = w->w_gate;
+        a.w1 = w->w_up;
+        a.s0 = w->s_gate;
+        a.s1 = w->s_up;
+        a.out = h;
+        if ((s = launch_gemm_a8(1, a, st)) != MOE_OK) return s;
+    } else {
+        uint16_t* xq = reinterpret_cast<uint16_t*>(base + p.x1);
+        if ((s = launch_quantize(x, T, w->H, nullptr, nullptr, 0, 0, xq, st)) != MOE_OK) return s;
+        if ((s = moe_expert_gate_up(xq, T, k, perm, offsets, w, h, stream)) != MOE_OK) return s;
+    }
+    // phase 2: h -> y
+    if (p.fp8_2) {
+        GemmArgs a = a8_args(2, T, k, w);
+        uint8_t* codes = base + p.h2;
+        uint8_t* e8 = base + p.h2e;
+        if ((s = launch_quantize(h, rows, w->I, codes, e8, p.pitch_i, kE8M0Bias, nullptr, st)) != MOE_OK)
+            return s;
+        a.act = reinterpret_cast<const uint16_t*>(codes);
+        a.aexp = e8;
+        a.offsets = offsets;
+        a.w0 = w->w_down;
+        a.s0 = w->s_down;
+        a.out = y;
+        return launch_gemm_a8(2, a, st);
+    }
+    uint16_t* hq = reinterpret_cast<uint16_t*>(base + p.h2);
+    if ((s = launch_quantize(h, rows, w->I, nullptr, nullptr, 0, 0, hq, st)) != MOE_OK) return s;
     return moe_expert_down(hq, T, k, offsets, w, y, stream);
 }

@@ -10,6 +10,12 @@ import synth
 
 ROW_TOL = 1e-2  # per-row relative L2 bound on float outputs (h, y, shared, out)
 W_TOL = 1e-6  # absolute bound on the routing weights
+# FP8 activation mode.  h is quantised to E4M3FN before the down projection, and h is itself a
+# rounded result: the GPU's (fp32 sums) and the oracle's (double) may differ by a bf16 ulp, and
+# where such an h value sits on an E4M3 rounding midpoint (or a block's largest magnitude on a
+# scale boundary) the two sides quantise it one step apart -- both correctly for their own h.
+# y is linear in the dequantised h, so the exact effect of those steps is added to the oracle's
+# y (and through it to S and out) before the usual per-row bound is applied; see a8_correction.
 DEV = "cuda"
 
 _layers = {}
@@ -45,7 +51,50 @@ def run_gpu(layer, stream=None, act="bf16"):
     return dict(ids=c(L.topk_ids), w=c(L.topk_w), counts=c(L.counts), offsets=c(L.offsets),
                 perm=c(L.perm[:T * k]), inv=c(L.inv[:T * k]),
                 h=c(L.h[:T * k]).view(np.uint16), y=c(L.y[:T * k]).view(np.uint16),
-                S=c(L.sh_y[:T]).view(np.uint16), out=c(L.out[:T]).view(np.uint16))
+                hS=c(L.sh_h[:T]).view(np.uint16), S=c(L.sh_y[:T]).view(np.uint16),
+                out=c(L.out[:T]).view(np.uint16))
+
+
+def block_exponents(h_bits, K):
+    """Scale exponent of every 128-block of bf16 rows (bits [n, K]): the smallest e with
+    max|v| <= 448 * 2^e, clamped to [-127, 127], 0 for an all-zero block; and the largest
+    magnitude's bit pattern."""
+    h = np.asarray(h_bits, np.uint16).reshape(-1, K // 128, 128)
+    amax_bits = (h & 0x7FFF).max(-1)
+    m, E = np.frexp(oracle.bf16_bits_to_float(amax_bits))  # exact: amax = m 2^E, m in [0.5, 1)
+    e = np.where(m <= 0.875, E - 9, E - 8)
+    e = np.where(amax_bits == 0, 0, np.clip(e, -127, 127))
+    return e, amax_bits.astype(np.int64)
+
+
+def quantise_dequantise(h_bits, K):
+    """bf16 rows (bits [n, K]) through the FP8 mode's quantiser and back, in float64: exponents
+    from block_exponents, codes from torch's E4M3FN cast (round to nearest even) of v * 2^-e in
+    float32."""
+    e, _ = block_exponents(h_bits, K)
+    v = oracle.bf16_bits_to_float(h_bits).reshape(-1, K // 128, 128)
+    s = np.exp2(-e.astype(np.float64))[..., None]
+    q = torch.from_numpy((v * s).astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64)
+    return (q.numpy() / s).reshape(-1, K)
+
+
+def down_columns(ew, e, cols):
+    """Columns `cols` of expert e's down matrix [H][I], dequantised (FP8 code x block scale)."""
+    idx = torch.as_tensor(cols, dtype=torch.long, device=ew.down.device)
+    q = ew.down[e].index_select(1, idx).cpu().view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    sc = ew.s_down[e].index_select(1, idx // 128).cpu().to(torch.float64).numpy()  # [H/128, n]
+    return q * np.repeat(sc, 128, axis=0)
+
+
+def a8_correction(ew, experts, h_gpu, h_ref, K):
+    """[n, H] change of y = Wd h between the GPU's h and the oracle's h after each is quantised:
+    Wd_e (deq(h_gpu) - deq(h_ref)), over the (few) positions where the two differ."""
+    d = quantise_dequantise(h_gpu, K) - quantise_dequantise(h_ref, K)
+    out = np.zeros((d.shape[0], ew.down.shape[1]))
+    for p in np.nonzero(np.any(d != 0, axis=1))[0]:
+        cols = np.nonzero(d[p])[0]
+        out[p] = down_columns(ew, int(experts[p]), cols) @ d[p, cols]
+    return out
 
 
 def rel_l2_rows(got, ref):
@@ -86,9 +135,27 @@ def compare_with_oracle(layer, g, rows=None, routed=None, expert_slot=None, n_th
     f = oracle.bf16_bits_to_float
     errs = {}
     errs["h"] = assert_rows_close("h", f(g["h"][pos.ravel()]), f(ref["h"]).reshape(-1, layer.I))
-    errs["y"] = assert_rows_close("y", f(g["y"][pos.ravel()]), ref["y"].reshape(-1, layer.H))
-    errs["S"] = assert_rows_close("shared", f(g["S"][r]), ref["S"])
-    errs["out"] = assert_rows_close("out", f(g["out"][r]), f(ref["out"]))
+    errs["hS"] = assert_rows_close("shared h", f(g["hS"][r]), f(ref["hS"]))
+    y_got, y_ref = f(g["y"][pos.ravel()]), ref["y"].reshape(-1, layer.H)
+    S_got, S_ref = f(g["S"][r]), ref["S"]
+    out_got, out_ref = f(g["out"][r]), f(ref["out"])
+    if not act_fp8:
+        errs["y"] = assert_rows_close("y", y_got, y_ref)
+        errs["S"] = assert_rows_close("shared", S_got, S_ref)
+        errs["out"] = assert_rows_close("out", out_got, out_ref)
+        return errs
+    # the exact effect of the two sides' h quantisations on y, S and out (see a8_correction)
+    jr = g["ids"][r].reshape(-1)  # expert of each checked (t, j)
+    slots = jr if expert_slot is None else np.asarray(expert_slot)[jr]
+    ew = routed if routed is not None else layer.experts
+    dy = a8_correction(ew, slots, g["h"][pos.ravel()], ref["h"].reshape(-1, layer.I), layer.I)
+    dS = a8_correction(layer.shared, np.zeros(len(r), np.int64), g["hS"][r], ref["hS"], layer.I)
+    w = ref["w"].astype(np.float64)
+    dout = dS + np.einsum("tj,tjh->th", w, dy.reshape(len(r), k, -1))
+    errs["y"] = assert_rows_close("y", y_got, y_ref + dy)
+    errs["S"] = assert_rows_close("shared", S_got, S_ref + dS)
+    errs["out"] = assert_rows_close("out", out_got, out_ref + dout)
+    errs["corrected_rows"] = float(np.mean(np.any(dy != 0, axis=1)))
     return errs
 
 

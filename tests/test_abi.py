@@ -130,11 +130,14 @@ def test_ffn_a8_validation():
     L = moe.lib()
     w = _w(H=256, I=384)
     n = ctypes.c_size_t()
+    # many rows per expert (FP8-code GEMMs): h, then codes and E8M0 exponent rows (16-byte
+    # pitch) of x and of h, each part 256-byte aligned
+    big = ctypes.c_size_t()
+    assert L.moe_expert_ffn_a8_workspace_size(1024, 2, ctypes.byref(w), ctypes.byref(big)) == moe.MOE_OK
+    assert big.value == 2048 * 384 * 2 + 1024 * 256 + 1024 * 16 + 2048 * 384 + 2048 * 16
+    # few rows per expert: h, then x and h dequantised to bf16
     assert L.moe_expert_ffn_a8_workspace_size(16, 2, ctypes.byref(w), ctypes.byref(n)) == moe.MOE_OK
-    # quantised x [T][H], h and quantised h [T*k][I], bf16, each part 256-byte aligned
-    assert n.value == 16 * 256 * 2 + 2 * (32 * 384 * 2)
-    assert moe.a8_h_offset(16, 256) == 16 * 256 * 2
-    assert moe.a8_h_offset(3, 128) == 768
+    assert n.value == 32 * 384 * 2 + 16 * 256 * 2 + 32 * 384 * 2
     f = L.moe_expert_ffn_a8
     assert f(FAKE, 16, 2, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, n.value - 1,
              None) == moe.MOE_ERR_WORKSPACE

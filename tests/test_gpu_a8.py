@@ -10,6 +10,7 @@ import torch
 
 import oracle
 import routed_expert_grouped_amd as moe
+import synth
 from gpu_util import (DEV, compare_sampled, compare_with_oracle, layer_for, mid, rel_l2_rows,
                       run_gpu)
 
@@ -71,13 +72,42 @@ def test_quantize_act_ragged_row_counts():
         np.testing.assert_array_equal(codes.cpu().numpy(), rc)
 
 
-@pytest.mark.parametrize("cfg", ["tiny_fp8", mid(), mid(T=37, E=64, k=8),
-                                 mid(T=160, H=640, E=8, k=2), mid(T=300, E=4, k=1,
-                                                                  score_fn="softmax")])
+@pytest.mark.parametrize("cfg", [
+    "tiny_fp8",                                   # few rows per expert: dequantise + GEMV
+    mid(),                                        # FP8-code GEMMs in both phases, ragged tails
+    mid(T=37, E=64, k=8),                         # mostly 1-row experts, some empty
+    mid(T=160, H=640, E=8, k=2),                  # phase 2 outside the FP8 GEMM's tiles
+    mid(T=300, E=4, k=1, score_fn="softmax"),     # few experts with many rows (m-tile stacks)
+    mid(T=200, H=2560, E=8, k=2),                 # 20 exponent blocks a row (32-byte pitch)
+    mid(T=150, H=5120, E=6, k=2),                 # 40 blocks (48-byte pitch)
+    mid(T=256, E=32, k=2, scores="zipf"),         # skewed routing
+])
 def test_a8_layer(cfg):
     layer = layer_for(cfg, seed=1)
     g = run_gpu(layer, act="fp8")
     compare_with_oracle(layer, g, act_fp8=True)
+
+
+def test_a8_block_scales_zero_and_wide_range():
+    """Weight blocks with zero scales and scales over six decades, on the FP8-code GEMMs."""
+    layer = synth.make_layer(mid(T=200, E=8, k=2, I=512), seed=5)
+    rng = np.random.default_rng(5)
+    for ew in (layer.experts, layer.shared):
+        for name in ("s_gate", "s_up", "s_down"):
+            s = getattr(ew, name)
+            f = rng.choice(np.array([0.0, 1e-3, 1.0, 1e3], np.float32), size=tuple(s.shape))
+            s.mul_(torch.from_numpy(f))
+    layer = layer.to(DEV)
+    g = run_gpu(layer, act="fp8")
+    assert g["counts"].max() > 32
+    compare_with_oracle(layer, g, act_fp8=True)
+
+
+def test_a8_repeat_runs_are_bit_identical():
+    layer = layer_for(mid(), seed=1)
+    a, b = run_gpu(layer, act="fp8"), run_gpu(layer, act="fp8")
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
 
 
 def test_a8_is_not_the_bf16_path():
@@ -98,10 +128,13 @@ def test_a8_dsv3_decode_full():
     compare_sampled(layer, g, rows=list(range(layer.T)), act_fp8=True)
 
 
-def test_a8_dsv3_prefill_sampled_rows():
-    layer = layer_for("dsv3_prefill")
+@pytest.mark.parametrize("cfg,rows", [("dsv3_prefill", [0, 1, 2048, 4095]),
+                                      ("kimi_k2", [0, 4097, 8191]),
+                                      ("dsv3_long_zipf", [0, 12345, 32767])])
+def test_a8_large_layers_sampled_rows(cfg, rows):
+    layer = layer_for(cfg)
     g = run_gpu(layer, act="fp8")
-    compare_sampled(layer, g, rows=[0, 1, 2048, 4095], act_fp8=True)
+    compare_sampled(layer, g, rows=rows, act_fp8=True)
 
 
 def test_a8_rejects_bf16_weights():

@@ -1,5 +1,5 @@
-"""Invariants of the compiled prefill GEMM that its hand-counted load waits rely on (CPU only:
-hipcc cross-compiles gfx950 device code without a GPU).
+"""Invariants of the compiled prefill GEMMs (bf16 and FP8 activations) that their hand-counted
+load waits rely on (CPU only: hipcc cross-compiles gfx950 device code without a GPU).
 
 The direct-to-LDS loads are issued from inline assembly, so the compiler neither knows that
 they write M0 nor counts them when it inserts its own load waits; the kernel waits for them
@@ -17,8 +17,8 @@ import pytest
 
 from routed_expert_grouped_amd import build
 
-SRC = os.path.join(build.CSRC, "moe_gemm.hip")
-KERNEL = "gemm_fp8_q256_kernel"
+SRCS = [os.path.join(build.CSRC, f) for f in ("moe_gemm.hip", "moe_gemm_a8.hip")]
+KERNELS = ("gemm_fp8_q256_kernel", "gemm_a8_kernel")  # the kernels with direct-to-LDS loads
 
 pytestmark = pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not available")
 
@@ -27,13 +27,14 @@ _VMEM = re.compile(r"^\s*(global_|buffer_|scratch_|flat_)\w*")
 
 @pytest.fixture(scope="module")
 def isa(tmp_path_factory):
-    out = tmp_path_factory.mktemp("isa") / "moe_gemm.s"
-    subprocess.run([build.HIPCC, *build.FLAGS, "-S", "--cuda-device-only", "-o", str(out), SRC],
-                   check=True, capture_output=True)
-    text = out.read_text()
     funcs = {}
-    for m in re.finditer(r"^(_Z\w+):[^\n]*\n(.*?)^\.Lfunc_end", text, re.S | re.M):
-        funcs[m.group(1)] = m.group(2).splitlines()
+    for src in SRCS:
+        out = tmp_path_factory.mktemp("isa") / (os.path.basename(src) + ".s")
+        subprocess.run([build.HIPCC, *build.FLAGS, "-S", "--cuda-device-only", "-o", str(out),
+                        src], check=True, capture_output=True)
+        text = out.read_text()
+        for m in re.finditer(r"^(_Z\w+):[^\n]*\n(.*?)^\.Lfunc_end", text, re.S | re.M):
+            funcs[m.group(1)] = m.group(2).splitlines()
     assert any("gemm" in n for n in funcs), "no kernels found in the assembly"
     return funcs
 
@@ -54,8 +55,9 @@ def _code(lines):
 
 
 def test_kernels_present(isa):
-    names = [n for n in isa if KERNEL in n]
-    assert len(names) == 4, names  # 2 phases x (grouped, identity)
+    for kernel in KERNELS:
+        names = [n for n in isa if kernel in n]
+        assert len(names) == 4, names  # 2 phases x (grouped, identity)
 
 
 def test_m0_only_in_inline_asm(isa):
@@ -66,13 +68,13 @@ def test_m0_only_in_inline_asm(isa):
         checked += 1
         bad = [t for t, inasm in _code(lines) if not inasm and re.search(r"\bm0\b", t)]
         assert not bad, (name, bad[:5])
-    assert checked >= 8
+    assert checked >= 12
 
 
 def test_no_other_vector_memory_between_direct_loads(isa):
     checked = 0
     for name, lines in isa.items():
-        if KERNEL not in name:
+        if not any(k in name for k in KERNELS):
             continue
         checked += 1
         code = list(_code(lines))
@@ -81,4 +83,4 @@ def test_no_other_vector_memory_between_direct_loads(isa):
         inside = [t for t, _ in code[dma[0]:dma[-1] + 1]
                   if _VMEM.match(t) and not t.startswith("global_load_lds")]
         assert not inside, (name, inside[:5])
-    assert checked == 4
+    assert checked == 8

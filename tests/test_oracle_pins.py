@@ -203,7 +203,7 @@ def _dense_brute_force(layer, ids, w, act_fp8=False):
         h = _to_bf16_f64(scipy.special.expit(G) * G * U)  # note: h is exact within fp32 first
         return h, (_ref_quantize(h) if act_fp8 else h) @ d.T
 
-    _, S = ffn(Sg[0], Su[0], Sd[0])
+    hS, S = ffn(Sg[0], Su[0], Sd[0])
     gate = np.zeros((layer.T, layer.E))
     np.put_along_axis(gate, ids, w.astype(np.float64), axis=1)
     acc = S.copy()
@@ -213,12 +213,12 @@ def _dense_brute_force(layer, ids, w, act_fp8=False):
         acc += gate[:, e:e + 1] * y
         hs.append(h)
         ys.append(y)
-    return acc, np.stack(hs, 1), np.stack(ys, 1), S
+    return acc, np.stack(hs, 1), np.stack(ys, 1), S, hS
 
 
 def _check_layer_against_dense(layer, act_fp8=False):
     res = oracle.moe_layer(layer, want_h=True, want_y=True, act_fp8=act_fp8)
-    acc, hs, ys, S = _dense_brute_force(layer, res["ids"], res["w"], act_fp8)
+    acc, hs, ys, S, hS = _dense_brute_force(layer, res["ids"], res["w"], act_fp8)
     T = layer.T
     y_sel = ys[np.arange(T)[:, None], res["ids"]]  # [T, k, H]
     h_sel = hs[np.arange(T)[:, None], res["ids"]]
@@ -231,7 +231,10 @@ def _check_layer_against_dense(layer, act_fp8=False):
     np.testing.assert_allclose(res["y"][same_h], y_sel[same_h], rtol=1e-9, atol=1e-14)
     d = np.linalg.norm(res["y"] - y_sel, axis=-1) / np.linalg.norm(y_sel, axis=-1)
     assert d.max() < 1e-3
-    # shared expert: same caveat (its h is not returned, so compare per row)
+    # shared expert: same caveat
+    hSb = oracle.bf16_bits_to_float(res["hS"])
+    assert np.mean(hSb == hS) > 0.999
+    np.testing.assert_allclose(hSb, hS, rtol=2.0 ** -7, atol=0)
     dS = np.linalg.norm(res["S"] - S, axis=-1) / np.linalg.norm(S, axis=-1)
     assert dS.max() < 1e-3 and np.mean(dS < 1e-12) > 0.8
     out = oracle.bf16_bits_to_float(res["out"])
