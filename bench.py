@@ -7,12 +7,14 @@ combine.
 
 The headline `value` is tokens/s of the DeepSeek-V3-shaped decode layer (T=16, 256 experts,
 top-8, FP8 block-scaled weights).  The same line carries the 4096-token prefill layer under
-"prefill", the roofline of the dominant kernel (the routed gate/up projection: its launch
+"prefill", the same layer in the opt-in FP8 activation mode under "prefill_a8" (its gate/up
+roofline against the FP8 MFMA peak), the roofline of the dominant kernel (the routed gate/up projection: its launch
 duration from HIP events around back-to-back launches on the main stream, plus the average of
 the per-step brackets inside the layer) and the CPU oracle timed on a bounded sample on the
 host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_decode] [--no-cpu]
+                    [--prefill dsv3_prefill] [--a8 dsv3_prefill]
 """
 from __future__ import annotations
 
@@ -49,6 +51,14 @@ def gate_up_bytes(T: int, k: int, H: int, I: int, touched: int, wdtype: str = "f
     return touched * w + T * H * 2 + T * k * I * 2
 
 
+def gate_up_a8_bytes(T: int, k: int, H: int, I: int, touched: int) -> int:
+    """Algorithmic bytes of the FP8-activation gate/up launch: the touched experts' gate and up
+    weights (+ scales) once, every token's FP8 codes and exponent row once, h written once."""
+    w = 2 * H * I + 2 * (H // 128) * (I // 128) * 4
+    pitch = (H // 128 + 15) // 16 * 16
+    return touched * w + T * (H + pitch) + T * k * I * 2
+
+
 def gate_up_flops(T: int, k: int, H: int, I: int) -> int:
     return 2 * 2 * T * k * H * I
 
@@ -68,12 +78,16 @@ def layer_flops(T, H, I, k, shared=True) -> int:
 # ------------------------------------------------------------------ counter-derived traffic
 
 def kernel_sources(kernel: str) -> list:
-    """Sources (relative to the repository root) of the translation units a libmoe gate/up
-    kernel is compiled in: moe_ffn.hip (GEMV kernels and the launches) and, for the GEMM
-    kernels, moe_gemm.hip, with the headers both include."""
-    names = ["moe_device.h", "moe_ffn.h", "moe_ffn.hip", "moe_host.h"]
-    if "gemv_kernel" not in kernel:
-        names.append("moe_gemm.hip")
+    """Sources (relative to the repository root) of the translation unit a libmoe gate/up kernel
+    is compiled in, with the headers it includes: moe_ffn.hip (GEMV kernels and the launches),
+    moe_gemm.hip (bf16-activation GEMM) or moe_gemm_a8.hip (FP8-activation GEMM)."""
+    if "gemv_kernel" in kernel:
+        names = ["moe_device.h", "moe_ffn.h", "moe_ffn.hip", "moe_host.h"]
+    elif "gemm_a8_kernel" in kernel:
+        names = ["moe_device.h", "moe_ffn.h", "moe_gemm_a8.hip", "moe_host.h", "moe_lds.h"]
+    else:
+        names = ["moe_device.h", "moe_ffn.h", "moe_ffn.hip", "moe_gemm.hip", "moe_host.h",
+                 "moe_lds.h"]
     return sorted(os.path.join("routed_expert_grouped_amd", "csrc", n) for n in names) + \
         [os.path.join("include", "libmoe.h")]
 
@@ -102,19 +116,21 @@ def counter_traffic(workload: str):
 
 # ------------------------------------------------------------------ timing
 
-def time_layer(layer, steps: int, warmup: int):
+def time_layer(layer, steps: int, warmup: int, act: str = "bf16"):
     import torch
 
     import routed_expert_grouped_amd as moe
 
     L = moe.MoeLayer(layer.T, layer.H, layer.I, layer.E, layer.k, layer.experts, layer.shared,
-                     layer.score_fn, layer.renorm)
+                     layer.score_fn, layer.renorm, act=act)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         L.forward(layer.scores, layer.x)
     torch.cuda.synchronize()
+    # per-step brackets around the routed gate/up launch (the FP8 mode runs both phases in one
+    # call, so it has none)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+          for _ in range(steps)] if act == "bf16" else [None] * steps
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -126,21 +142,30 @@ def time_layer(layer, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
-    gu_ms = [a.elapsed_time(b) for a, b in ev]
+    gu_ms = [e[0].elapsed_time(e[1]) for e in ev if e is not None]
     # The same routed gate/up launch, `steps` times back to back on the same stream between one
     # event pair: the average launch duration without the per-step event latency that the
     # brackets above add (the weights read per launch are far larger than the caches, so a
     # repeat gets no help from them).
+    if act == "fp8":  # the FP8-code gate/up launch on the layer's quantised x
+        codes, exps = moe.moe_quantize_act(layer.x)
+        launch = lambda: moe.moe_expert_gate_up_a8(codes, exps, layer.k, L.perm, L.offsets, L.w,
+                                                   L.h, stream)
+    else:
+        launch = lambda: moe.moe_expert_gate_up(layer.x, layer.k, L.perm, L.offsets, L.w, L.h,
+                                                stream)
+    launch()
+    torch.cuda.synchronize()
     k0 = torch.cuda.Event(enable_timing=True)
     k1 = torch.cuda.Event(enable_timing=True)
     k0.record(stream)
     for _ in range(steps):
-        moe.moe_expert_gate_up(layer.x, layer.k, L.perm, L.offsets, L.w, L.h, stream)
+        launch()
     k1.record(stream)
     torch.cuda.synchronize()
     counts = L.counts.cpu().numpy()
     return dict(total_ms=total_ms, wall_s=wall, gate_up_ms=k0.elapsed_time(k1) / steps,
-                gate_up_ms_in_layer=sum(gu_ms) / len(gu_ms), counts=counts)
+                gate_up_ms_in_layer=sum(gu_ms) / len(gu_ms) if gu_ms else None, counts=counts)
 
 
 def cpu_baseline(layer, rows, n_threads: int):
@@ -175,34 +200,41 @@ def cpu_model() -> str:
     return platform.processor()
 
 
-def run_workload(name: str, steps: int, warmup: int, seed: int = 0):
+def run_workload(name: str, steps: int, warmup: int, seed: int = 0, act: str = "bf16",
+                 layer=None):
     import synth
 
-    layer = synth.make_layer(name, seed=seed, device="cuda")
-    r = time_layer(layer, steps, warmup)
+    if layer is None:
+        layer = synth.make_layer(name, seed=seed, device="cuda")
+    r = time_layer(layer, steps, warmup, act)
     T, H, I, E, k = layer.T, layer.H, layer.I, layer.E, layer.k
     touched = int((r["counts"] > 0).sum())
     ms = r["total_ms"] / steps
     lb = layer_bytes(T, H, I, E, k, touched)
     lf = layer_flops(T, H, I, k)
-    gb = gate_up_bytes(T, k, H, I, touched)
+    a8 = act == "fp8"
+    gb = gate_up_a8_bytes(T, k, H, I, touched) if a8 else gate_up_bytes(T, k, H, I, touched)
     gf = gate_up_flops(T, k, H, I)
     gu_s = r["gate_up_ms"] * 1e-3
     bw = gb / gu_s / 1e9
     tf = gf / gu_s / 1e12
-    bound = "hbm" if gb / (HBM_PEAK_GBS * 1e9) >= gf / (BF16_PEAK_TFLOPS * 1e12) else "mfma"
+    mfma_peak = FP8_PEAK_TFLOPS if a8 else BF16_PEAK_TFLOPS  # the contraction's own operand type
+    bound = "hbm" if gb / (HBM_PEAK_GBS * 1e9) >= gf / (mfma_peak * 1e12) else "mfma"
     if bound == "hbm":
         roof = dict(bound="hbm", achieved=round(bw, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(bw / HBM_PEAK_GBS, 4))
     else:
-        roof = dict(bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(tf / BF16_PEAK_TFLOPS, 4))
-    roof.update(traffic=counter_traffic(name), kernel="gate_up (routed)",
+        roof = dict(bound="mfma", achieved=round(tf, 1), peak=mfma_peak, unit="TFLOP/s",
+                    frac=round(tf / mfma_peak, 4))
+    roof.update(traffic=counter_traffic(name + ("_a8" if a8 else "")),
+                kernel="gate_up_a8 (routed, FP8 activations)" if a8 else "gate_up (routed)",
                 kernel_ms=round(r["gate_up_ms"], 4),
-                kernel_ms_in_layer=round(r["gate_up_ms_in_layer"], 4),
+                kernel_ms_in_layer=(None if r["gate_up_ms_in_layer"] is None
+                                    else round(r["gate_up_ms_in_layer"], 4)),
                 algorithmic_bytes=gb, algorithmic_flops=gf)
     res = dict(
-        workload=name, T=T, H=H, I=I, E=E, k=k, tokens_per_s=T * steps / (r["total_ms"] * 1e-3), ms_per_step=ms,
+        workload=name, activations=act, T=T, H=H, I=I, E=E, k=k,
+        tokens_per_s=T * steps / (r["total_ms"] * 1e-3), ms_per_step=ms,
         touched_experts=touched, layer_bytes=lb, layer_flops=lf,
         layer_hbm_frac=round(lb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
         layer_bf16_mfma_frac=round(lf / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
@@ -218,6 +250,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_decode")
     ap.add_argument("--prefill", default="dsv3_prefill", help="second workload ('' to skip)")
+    ap.add_argument("--a8", default="dsv3_prefill",
+                    help="workload also run in the FP8 activation mode ('' to skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-threads", type=int, default=int(os.environ.get("OMP_NUM_THREADS", "0") or 0))
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -248,10 +282,17 @@ def main(argv=None):
                    sample=f"{len(rows)} tokens of the {a.workload} layer (all experts they select "
                           f"+ shared), {dt:.2f} s wall", cpu=cpu_model())
     del layer
-    prefill = None
+    prefill = a8 = None
     if a.prefill:
         torch.cuda.empty_cache()
-        _, prefill = run_workload(a.prefill, max(3, a.steps // 2), max(1, a.warmup // 2))
+        player, prefill = run_workload(a.prefill, max(3, a.steps // 2), max(1, a.warmup // 2))
+        if a.a8 == a.prefill:  # same layer, FP8 activations
+            _, a8 = run_workload(a.a8, max(3, a.steps // 2), max(1, a.warmup // 2), act="fp8",
+                                 layer=player)
+        del player
+    if a.a8 and a8 is None:
+        torch.cuda.empty_cache()
+        _, a8 = run_workload(a.a8, max(3, a.steps // 2), max(1, a.warmup // 2), act="fp8")
     line = {
         "metric": METRIC,
         "value": round(main_res["tokens_per_s"], 2),
@@ -276,6 +317,8 @@ def main(argv=None):
                                            "layer_fp8_mfma_frac")},
         "prefill": None if prefill is None else {
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in prefill.items()},
+        "prefill_a8": None if a8 is None else {
+            k: (round(v, 4) if isinstance(v, float) else v) for k, v in a8.items()},
     }
     print(json.dumps(line))
     return 0

@@ -165,12 +165,35 @@ moe_status moe_expert_ffn(const uint16_t* x, int32_t T, int32_t k, const int32_t
  * exact; only the rounding to a 3-bit mantissa differs from the bf16 path. */
 
 /* Quantise a bf16 [rows][K] matrix row by row in 128-blocks (as above).
- *   codes : uint8 [rows][K] out, E4M3FN bit patterns (same layout as x).
- *   exps  : int8 [rows][K/128] out, the block exponents e (scale = 2^e).
- * Errors: INVALID_ARG for rows < 0, K < 1, null or unaligned pointers; UNSUPPORTED when K is
- * not a multiple of 128 or rows * K/128 >= 2^31.  rows == 0 enqueues nothing. */
+ *   codes     : uint8 [rows][K] out, E4M3FN bit patterns (same layout as x).
+ *   exps      : int8 [rows][exp_pitch] out, the block exponents e (scale = 2^e) in the first
+ *               K/128 bytes of each row (the rest of the row is not written).
+ *   exp_pitch : bytes per exps row, >= K/128; a multiple of 16 for moe_expert_*_a8.
+ * Errors: INVALID_ARG for rows < 0, K < 1, exp_pitch < K/128, null or unaligned pointers;
+ * UNSUPPORTED when K is not a multiple of 128 or rows * K/128 >= 2^31.  rows == 0 enqueues
+ * nothing. */
 moe_status moe_quantize_act(const uint16_t* x, int32_t rows, int32_t K, uint8_t* codes,
-                            int8_t* exps, void* stream);
+                            int8_t* exps, int32_t exp_pitch, void* stream);
+
+/* Expert phase 1 on FP8 activations: moe_expert_gate_up with x given as moe_quantize_act writes
+ * it (x_codes [T][H], x_exps [T][exp_pitch]), i.e. with activations x = code * 2^e.  Both
+ * operands go to the scaled FP8 matrix instruction; fp32 accumulation, weight block scales
+ * after each 128-long partial sum, h as in moe_expert_gate_up.
+ * For the shapes of the FP8-code GEMM only: UNSUPPORTED when T*k <= 32*n_groups (few rows per
+ * expert: moe_expert_ffn_a8 covers those), H > 8192, exp_pitch not a multiple of 16 or above 64,
+ * or weights not MOE_W_FP8_E4M3_B128; INVALID_ARG for exp_pitch < H/128; other errors as for
+ * moe_expert_gate_up. */
+moe_status moe_expert_gate_up_a8(const uint8_t* x_codes, const int8_t* x_exps, int32_t exp_pitch,
+                                 int32_t T, int32_t k, const int32_t* perm,
+                                 const int32_t* offsets, const moe_expert_weights* w, uint16_t* h,
+                                 void* stream);
+
+/* Expert phase 2 on FP8 activations: moe_expert_down with h given quantised (h_codes [T*k][I],
+ * h_exps [T*k][exp_pitch], grouped order).  Same limits as moe_expert_gate_up_a8, with I in
+ * place of H, and H a multiple of 256. */
+moe_status moe_expert_down_a8(const uint8_t* h_codes, const int8_t* h_exps, int32_t exp_pitch,
+                              int32_t T, int32_t k, const int32_t* offsets,
+                              const moe_expert_weights* w, uint16_t* y, void* stream);
 
 /* Bytes of workspace moe_expert_ffn_a8 needs (host output). */
 moe_status moe_expert_ffn_a8_workspace_size(int32_t T, int32_t k, const moe_expert_weights* w,

@@ -65,6 +65,10 @@ def lib():
         L.oracle_act_scale_exp.argtypes = [ctypes.c_double]
         L.oracle_quantize_rows.restype = None
         L.oracle_quantize_rows.argtypes = [P, i32, i32, P, P]
+        L.oracle_expert_gate_up.restype = i32
+        L.oracle_expert_gate_up.argtypes = [P, i32, i32, P, P, ctypes.POINTER(_Weights), P, i32]
+        L.oracle_expert_down.restype = i32
+        L.oracle_expert_down.argtypes = [P, i32, P, ctypes.POINTER(_Weights), P, i32]
         L.oracle_max_threads.restype = i32
         L.oracle_max_threads.argtypes = [i32]
         _lib = L
@@ -193,6 +197,36 @@ def moe_layer(layer, rows=None, routed=None, expert_slot=None, with_shared=True,
     if rc:
         raise ValueError("oracle_moe_layer: invalid arguments (row, k or expert slot)")
     return res
+
+
+def expert_gate_up(x, token, slot, experts, n_threads: int = 0):
+    """Phase 1 alone: h[p] = bf16(SiLU(Wg x_t) * (Wu x_t)) of expert slot[p] (a slot of
+    `experts`, a synth.ExpertWeights) on token t = token[p] of x (bf16 bits [T][H]).  Returns
+    bf16 bits [n, I]."""
+    keep = []
+    xb = _np(x, np.uint16)
+    tok, sl = _np(np.asarray(token), np.int32), _np(np.asarray(slot), np.int32)
+    W = _weights(experts, keep)
+    h = np.zeros((len(tok), W.I), np.uint16)
+    rc = lib().oracle_expert_gate_up(_ptr(xb), xb.shape[0], len(tok), _ptr(tok), _ptr(sl),
+                                     ctypes.byref(W), _ptr(h), int(n_threads))
+    if rc:
+        raise ValueError("oracle_expert_gate_up: token or slot out of range")
+    return h
+
+
+def expert_down(h, slot, experts, n_threads: int = 0):
+    """Phase 2 alone: y[p] = Wd h[p] (double) of expert slot[p] for bf16 rows h (bits [n][I])."""
+    keep = []
+    hb = _np(h, np.uint16)
+    sl = _np(np.asarray(slot), np.int32)
+    W = _weights(experts, keep)
+    y = np.zeros((len(sl), W.H), np.float64)
+    rc = lib().oracle_expert_down(_ptr(hb), len(sl), _ptr(sl), ctypes.byref(W), _ptr(y),
+                                  int(n_threads))
+    if rc:
+        raise ValueError("oracle_expert_down: slot out of range")
+    return y
 
 
 def max_threads(n_threads: int = 0) -> int:

@@ -261,14 +261,12 @@ static double weight(const oracle_weights* W, const void* mat, const float* sc, 
     return fp8_table[((const uint8_t*)mat)[at]] * scale;
 }
 
-/* One expert (slot x) on one token row xrow (bf16 bits, length H):
- * h[n] = bf16(SiLU(g_n) * u_n) with g = Wg x, u = Wu x; y = Wd h (double). */
-static void expert_on_token(const oracle_weights* W, int x, const uint16_t* xrow, uint16_t* h_out,
-                            double* y_out, double* xd, double* hd, int act_fp8) {
+/* Gate and up of expert slot x on the activations xd (length H, double):
+ * h[n] = bf16(SiLU(g_n) * u_n) with g = Wg x, u = Wu x.  Writes the bf16 bits to h_out (if not
+ * NULL) and their values to hd. */
+static void gate_up_row(const oracle_weights* W, int x, const double* xd, uint16_t* h_out,
+                        double* hd) {
     const int H = W->H, I = W->I;
-    for (int c = 0; c < H; ++c) xd[c] = oracle_bf16_to_double(xrow[c]);
-    if (act_fp8)
-        for (int b = 0; b < H / 128; ++b) quantize_block(xd + b * 128, 128, NULL);
     for (int n = 0; n < I; ++n) {
         double g = 0.0, u = 0.0;
         for (int c = 0; c < H; ++c) {
@@ -280,13 +278,82 @@ static void expert_on_token(const oracle_weights* W, int x, const uint16_t* xrow
         if (h_out) h_out[n] = hb;
         hd[n] = oracle_bf16_to_double(hb);
     }
-    if (act_fp8)
-        for (int b = 0; b < I / 128; ++b) quantize_block(hd + b * 128, 128, NULL);
+}
+
+/* Down projection of expert slot x: y = Wd h (double, length H) for h of length I. */
+static void down_row(const oracle_weights* W, int x, const double* hd, double* y_out) {
+    const int H = W->H, I = W->I;
     for (int c = 0; c < H; ++c) {
         double y = 0.0;
         for (int n = 0; n < I; ++n) y += hd[n] * weight(W, W->down, W->s_down, x, H, I, c, n);
         y_out[c] = y;
     }
+}
+
+/* One expert (slot x) on one token row xrow (bf16 bits, length H): gate_up_row then down_row,
+ * with x and h quantised first in the FP8 activation mode. */
+static void expert_on_token(const oracle_weights* W, int x, const uint16_t* xrow, uint16_t* h_out,
+                            double* y_out, double* xd, double* hd, int act_fp8) {
+    const int H = W->H, I = W->I;
+    for (int c = 0; c < H; ++c) xd[c] = oracle_bf16_to_double(xrow[c]);
+    if (act_fp8)
+        for (int b = 0; b < H / 128; ++b) quantize_block(xd + b * 128, 128, NULL);
+    gate_up_row(W, x, xd, h_out, hd);
+    if (act_fp8)
+        for (int b = 0; b < I / 128; ++b) quantize_block(hd + b * 128, 128, NULL);
+    down_row(W, x, hd, y_out);
+}
+
+/* Expert phase 1 alone on rows p = 0..n_rows-1: h[p] = gate/up of expert slot[p] on the bf16
+ * activations x[token[p]] (bits, rows of length H), as in the layer (bf16 activations). */
+int oracle_expert_gate_up(const uint16_t* x, int n_tokens, int n_rows, const int32_t* token,
+                          const int32_t* slot, const oracle_weights* W, uint16_t* h, int n_threads) {
+    fill_fp8_table();
+    for (int p = 0; p < n_rows; ++p)
+        if (token[p] < 0 || token[p] >= n_tokens || slot[p] < 0 || slot[p] >= W->n) return ORACLE_ERR;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel
+#endif
+    {
+        double* xd = (double*)malloc(sizeof(double) * W->H);
+        double* hd = (double*)malloc(sizeof(double) * W->I);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int p = 0; p < n_rows; ++p) {
+            const uint16_t* xrow = x + (size_t)token[p] * W->H;
+            for (int c = 0; c < W->H; ++c) xd[c] = oracle_bf16_to_double(xrow[c]);
+            gate_up_row(W, slot[p], xd, h + (size_t)p * W->I, hd);
+        }
+        free(xd); free(hd);
+    }
+    return ORACLE_OK;
+}
+
+/* Expert phase 2 alone: y[p] = down projection of expert slot[p] on the bf16 row h[p] (bits,
+ * length I), in double. */
+int oracle_expert_down(const uint16_t* h, int n_rows, const int32_t* slot, const oracle_weights* W,
+                       double* y, int n_threads) {
+    fill_fp8_table();
+    for (int p = 0; p < n_rows; ++p)
+        if (slot[p] < 0 || slot[p] >= W->n) return ORACLE_ERR;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel
+#endif
+    {
+        double* hd = (double*)malloc(sizeof(double) * W->I);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int p = 0; p < n_rows; ++p) {
+            for (int n = 0; n < W->I; ++n) hd[n] = oracle_bf16_to_double(h[(size_t)p * W->I + n]);
+            down_row(W, slot[p], hd, y + (size_t)p * W->H);
+        }
+        free(hd);
+    }
+    return ORACLE_OK;
 }
 
 static void set_error(int* err) {

@@ -22,7 +22,8 @@ SCORE_FN = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
 
 EXPORTS = ("moe_route", "moe_permute", "moe_expert_gate_up", "moe_expert_down",
            "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine", "moe_quantize_act",
-           "moe_expert_ffn_a8_workspace_size", "moe_expert_ffn_a8", "moe_status_string")
+           "moe_expert_gate_up_a8", "moe_expert_down_a8", "moe_expert_ffn_a8_workspace_size",
+           "moe_expert_ffn_a8", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -59,7 +60,9 @@ def lib():
         L.moe_expert_ffn_workspace_size.argtypes = [i32, i32, W, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_expert_ffn.argtypes = [P, i32, i32, P, P, W, P, P, ctypes.c_size_t, P]
         L.moe_combine.argtypes = [P, P, P, P, i32, i32, i32, P, P]
-        L.moe_quantize_act.argtypes = [P, i32, i32, P, P, P]
+        L.moe_quantize_act.argtypes = [P, i32, i32, P, P, i32, P]
+        L.moe_expert_gate_up_a8.argtypes = [P, P, i32, i32, i32, P, P, W, P, P]
+        L.moe_expert_down_a8.argtypes = [P, P, i32, i32, i32, P, W, P, P]
         L.moe_expert_ffn_a8_workspace_size.argtypes = [i32, i32, W,
                                                        ctypes.POINTER(ctypes.c_size_t)]
         L.moe_expert_ffn_a8.argtypes = [P, i32, i32, P, P, W, P, P, ctypes.c_size_t, P]
@@ -173,17 +176,44 @@ def moe_combine(y, inv, topk_w, shared_y, T: int, k: int, H: int, out=None, stre
     return out
 
 
-def moe_quantize_act(x, codes=None, exps=None, stream=None):
+def exp_pitch(K: int) -> int:
+    """Exponent row pitch that the FP8-activation phase calls take: K/128 rounded up to 16."""
+    return (K // 128 + 15) // 16 * 16
+
+
+def moe_quantize_act(x, codes=None, exps=None, pitch=None, stream=None):
     """FP8 activation quantisation of bf16 bits x [rows, K]: (codes uint8 [rows, K], exps int8
-    [rows, K/128])."""
+    [rows, pitch]; the exponents of row r are exps[r, :K/128])."""
     rows, K = x.shape
+    pitch = exp_pitch(K) if pitch is None else pitch
     if codes is None:
         codes = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
     if exps is None:
-        exps = torch.empty((rows, max(1, K // 128)), dtype=torch.int8, device=x.device)
-    _check("moe_quantize_act", lib().moe_quantize_act(_p(x), rows, K, _p(codes), _p(exps),
+        exps = torch.empty((rows, max(1, pitch)), dtype=torch.int8, device=x.device)
+    _check("moe_quantize_act", lib().moe_quantize_act(_p(x), rows, K, _p(codes), _p(exps), pitch,
                                                       _s(stream)))
     return codes, exps
+
+
+def moe_expert_gate_up_a8(codes, exps, k: int, perm, offsets, w: MoeExpertWeights, h=None,
+                          stream=None):
+    T = codes.shape[0]
+    if h is None:
+        h = torch.empty((T * k, w.I), dtype=torch.int16, device=codes.device)
+    _check("moe_expert_gate_up_a8", lib().moe_expert_gate_up_a8(
+        _p(codes), _p(exps), exps.shape[1], T, k, _p(perm), _p(offsets), ctypes.byref(w), _p(h),
+        _s(stream)))
+    return h
+
+
+def moe_expert_down_a8(codes, exps, T: int, k: int, offsets, w: MoeExpertWeights, y=None,
+                       stream=None):
+    if y is None:
+        y = torch.empty((T * k, w.H), dtype=torch.int16, device=codes.device)
+    _check("moe_expert_down_a8", lib().moe_expert_down_a8(
+        _p(codes), _p(exps), exps.shape[1], T, k, _p(offsets), ctypes.byref(w), _p(y),
+        _s(stream)))
+    return y
 
 
 def moe_expert_ffn_a8_workspace_size(T: int, k: int, w: MoeExpertWeights) -> int:

@@ -26,8 +26,8 @@ struct GemmArgs {
     bool fp8;
     uint16_t* out;  // [rows][N]
     // FP8 activation mode only: act holds E4M3FN codes [rows of act][K] (one byte each) and
-    // aexp their block scales as E8M0 bytes (127 + e), [rows of act][aexp_pitch]
-    const uint8_t* aexp;
+    // aexp their block exponents e (scale 2^e), [rows of act][aexp_pitch]
+    const int8_t* aexp;
     int aexp_pitch;
 };
 
@@ -46,8 +46,10 @@ inline bool use_gemv(int rows, int n_groups) { return rows <= 32 * n_groups; }
 moe_status launch_gemm(int phase, const GemmArgs& a, hipStream_t st);
 
 // FP8 activation mode: the GEMM on FP8 codes of both operands, for the shapes a8_gemm_fits
-// accepts (FP8 weights, many rows per expert, K <= kA8MaxK, N a multiple of the tile's columns).
+// accepts (FP8 weights, many rows per expert, K <= kA8MaxK, N a multiple of the tile's columns,
+// an exponent pitch that is a multiple of 16 and at most kA8MaxPitch).
 constexpr int kA8MaxK = 8192;
+constexpr int kA8MaxPitch = kA8MaxK / 128;
 bool a8_gemm_fits(int phase, const GemmArgs& a);
 moe_status launch_gemm_a8(int phase, const GemmArgs& a, hipStream_t st);
 

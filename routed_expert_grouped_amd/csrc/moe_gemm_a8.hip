@@ -3,7 +3,7 @@
 //
 // Both operands are E4M3FN codes.  The weights carry one fp32 scale per 128x128 block (the
 // OSDI'26 hybrid-inference article, "native FP8 GEMV", Figures 9-10).  The activations carry one
-// power-of-two scale 2^e per row and 128-long K block, stored as the E8M0 byte 127 + e.
+// power-of-two scale 2^e per row and 128-long K block (int8 e; the E8M0 byte is 127 + e).
 // v_mfma_scale_f32_32x32x64_f8f6f4 multiplies 32x64 by 64x32 codes and applies an E8M0 scale per
 // row of A itself, so the activation scales cost no instructions.  The weight scales are
 // applied to each 128-long block's sum as in the bf16-operand GEMM: the accumulator is kept in
@@ -37,7 +37,7 @@ constexpr int kA8M = 256;                     // rows per m-tile
 constexpr int kA8N = 256;                     // weight rows per tile
 constexpr int kA8K = 64;                      // K per stage: one MFMA step, half a scale block
 constexpr int kA8Stages = 4;                  // ring depth
-constexpr int kA8MaxBlocks = kA8MaxK / 128;  // exponent bytes per row staged in LDS
+constexpr int kA8MaxBlocks = kA8MaxPitch;    // exponent bytes per row staged in LDS
 constexpr int kE8M0One = 127;                 // E8M0 encoding of 1.0
 
 __device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
     const int e = tile.group;
     const int c0 = tile.nt * kCols;
     const int K = a.K, kblocks = K / 128, nq = 2 * kblocks;
-    const int pitch = a.aexp_pitch;  // a multiple of 16 in [kblocks, kA8MaxBlocks]
+    const int pitch = a.aexp_pitch;  // a multiple of 16 in [kblocks, kA8MaxPitch]
     const int fr = lane & 31, half = lane >> 5;
     const uint8_t* act = (const uint8_t*)a.act;
 
@@ -165,9 +165,11 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
     float u0 = 0.0f, u1 = 0.0f;
     uint32_t m0 = ~0u, m1 = ~0u;
     int sc[4] = {kE8M0One, kE8M0One, kE8M0One, kE8M0One};  // E8M0 activation scales of the block
-    auto rescale = [&](float r0, float r1) {
+    // rescales the accumulators of the first NS m-subtiles (the others are never stored)
+    auto rescale = [&](float r0, float r1, auto ns_tag) {
+        constexpr int NS = decltype(ns_tag)::value;
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < NS; ++mi)
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
                 acc[mi][0][x] *= r0;
@@ -198,18 +200,19 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
                 u1 = z1 ? u1 : s1;
                 m0 = z0 ? 0u : ~0u;
                 m1 = z1 ? 0u : ~0u;
-                rescale(r0, r1);
+                rescale(r0, r1, ns_tag);
             } else {
-                rescale(u0 * __builtin_amdgcn_rcpf(s0), u1 * __builtin_amdgcn_rcpf(s1));
+                rescale(u0 * __builtin_amdgcn_rcpf(s0), u1 * __builtin_amdgcn_rcpf(s1), ns_tag);
                 u0 = s0;
                 u1 = s1;
             }
 #pragma unroll
-            for (int mi = 0; mi < NS; ++mi) sc[mi] = sE[eaddr[mi] + kb];
+            for (int mi = 0; mi < NS; ++mi) sc[mi] = kE8M0One + (int)(int8_t)sE[eaddr[mi] + kb];
         }
         const uint8_t* A = sA[ST];
         const uint8_t* B = sB[ST];
-        i32x8 fb[2];
+        // every fragment of the stage is read before the first MFMA
+        i32x8 fb[2], fa[NS > 0 ? NS : 1];
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
             u32x4 lo = *(const u32x4*)&B[baddr[ni][0]];
@@ -221,13 +224,14 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
             fb[ni] = join(lo, hi);
         }
 #pragma unroll
-        for (int mi = 0; mi < NS; ++mi) {
-            const i32x8 fa = join(*(const u32x4*)&A[aaddr[mi][0]], *(const u32x4*)&A[aaddr[mi][1]]);
+        for (int mi = 0; mi < NS; ++mi)
+            fa[mi] = join(*(const u32x4*)&A[aaddr[mi][0]], *(const u32x4*)&A[aaddr[mi][1]]);
+#pragma unroll
+        for (int mi = 0; mi < NS; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
                 acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    fa, fb[ni], acc[mi][ni], 0, 0, 0, sc[mi], 0, kE8M0One);
-        }
+                    fa[mi], fb[ni], acc[mi][ni], 0, 0, 0, sc[mi], 0, kE8M0One);
     };
     auto run = [&](auto ns_tag, auto mask_tag) {
         using S0 = std::integral_constant<int, 0>;
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
         if (512 * j + 64 * wave < echunks)
-            lds_dma16(a.aexp + (size_t)eoff[j] * 16, &sE[16 * (512 * j + 64 * wave)]);
+            lds_dma16((const uint8_t*)a.aexp + (size_t)eoff[j] * 16, &sE[16 * (512 * j + 64 * wave)]);
     issue(0, 0);
     issue(1, 1);  // nq >= 2
     if (nq > 2) issue(2, 2);
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
         run(std::integral_constant<int, 1>{}, MN{});
     else
         run(std::integral_constant<int, 0>{}, MN{});
-    rescale(u0, u1);
+    rescale(u0, u1, std::integral_constant<int, 4>{});
 
     // D layout of the 32x32 MFMA: value x of a lane is row 8*(x/4) + 4*(lane/32) + x%4 of the
     // subtile, column lane%32
@@ -291,7 +295,7 @@ bool a8_gemm_fits(int phase, const GemmArgs& a) {
     if (!a.fp8 || use_gemv(a.rows, a.n_groups)) return false;
     if (a.K % 128 != 0 || a.K > kA8MaxK) return false;
     if (a.N % (phase == 1 ? kA8N / 2 : kA8N) != 0) return false;
-    if (a.aexp_pitch % 16 != 0 || a.aexp_pitch < a.K / 128 || a.aexp_pitch > kA8MaxBlocks)
+    if (a.aexp_pitch % 16 != 0 || a.aexp_pitch < a.K / 128 || a.aexp_pitch > kA8MaxPitch)
         return false;
     // activation rows: tokens (phase 1) or grouped rows (phase 2), addressed in 16-byte units
     const int64_t src_rows = phase == 1 ? a.rows / a.k : a.rows;
@@ -318,3 +322,54 @@ moe_status launch_gemm_a8(int phase, const GemmArgs& a, hipStream_t st) {
 }
 
 }  // namespace moe
+
+using namespace moe;
+
+// The two public phase calls: validation, then the FP8-code GEMM.
+static moe_status a8_phase(int phase, const uint8_t* codes, const int8_t* exps, int32_t pitch,
+                           int32_t T, int32_t k, const int32_t* perm, const int32_t* offsets,
+                           const moe_expert_weights* w, uint16_t* out, void* stream) {
+    if (T < 0 || k < 1) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!codes || !exps || !out || !aligned16(codes) || !aligned16(exps) || !aligned16(out))
+        return MOE_ERR_INVALID_ARG;
+    moe_status s = check_weights(w);
+    if (s != MOE_OK) return s;
+    if (w->dtype != MOE_W_FP8_E4M3_B128) return MOE_ERR_UNSUPPORTED;
+    if ((s = check_grouping(T, k, perm, offsets, w, phase == 1)) != MOE_OK) return s;
+    GemmArgs a{};
+    a.act = reinterpret_cast<const uint16_t*>(codes);
+    a.aexp = exps;
+    a.aexp_pitch = pitch;
+    a.perm = phase == 1 ? perm : nullptr;
+    a.offsets = offsets;
+    a.k = k;
+    a.rows = T * k;
+    a.n_groups = w->n_groups;
+    a.N = phase == 1 ? w->I : w->H;
+    a.K = phase == 1 ? w->H : w->I;
+    if (pitch < a.K / 128) return MOE_ERR_INVALID_ARG;
+    a.w0 = phase == 1 ? w->w_gate : w->w_down;
+    a.w1 = phase == 1 ? w->w_up : nullptr;
+    a.s0 = phase == 1 ? w->s_gate : w->s_down;
+    a.s1 = phase == 1 ? w->s_up : nullptr;
+    a.fp8 = true;
+    a.out = out;
+    if (!a8_gemm_fits(phase, a)) return MOE_ERR_UNSUPPORTED;
+    return launch_gemm_a8(phase, a, as_stream(stream));
+}
+
+extern "C" moe_status moe_expert_gate_up_a8(const uint8_t* x_codes, const int8_t* x_exps,
+                                            int32_t exp_pitch, int32_t T, int32_t k,
+                                            const int32_t* perm, const int32_t* offsets,
+                                            const moe_expert_weights* w, uint16_t* h,
+                                            void* stream) {
+    return a8_phase(1, x_codes, x_exps, exp_pitch, T, k, perm, offsets, w, h, stream);
+}
+
+extern "C" moe_status moe_expert_down_a8(const uint8_t* h_codes, const int8_t* h_exps,
+                                         int32_t exp_pitch, int32_t T, int32_t k,
+                                         const int32_t* offsets, const moe_expert_weights* w,
+                                         uint16_t* y, void* stream) {
+    return a8_phase(2, h_codes, h_exps, exp_pitch, T, k, nullptr, offsets, w, y, stream);
+}

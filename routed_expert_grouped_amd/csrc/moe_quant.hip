@@ -14,8 +14,6 @@
 
 namespace moe {
 
-constexpr int kE8M0Bias = 127;  // E8M0 byte of 2^e: 127 + e
-
 // exponent e of the block scale for largest magnitude amax (see the file comment)
 __device__ __forceinline__ int act_scale_exp(float amax) {
     if (!(amax > 0.0f)) return 0;
@@ -26,12 +24,12 @@ __device__ __forceinline__ int act_scale_exp(float amax) {
 }
 
 // One wave per (row, 128-block): lane l holds values 2l and 2l+1.  Writes any of: the codes, the
-// exponent (as exp_bias + e, exps[r * exp_pitch + b]) and the dequantised values as bf16 (exact:
-// a 4-bit significand times a power of two).
+// exponent (exps[r * exp_pitch + b]) and the dequantised values as bf16 (exact: a 4-bit
+// significand times a power of two).
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int rows,
                                                        int K, uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ exps, int exp_pitch,
-                                                       int exp_bias, uint16_t* __restrict__ deq) {
+                                                       int8_t* __restrict__ exps, int exp_pitch,
+                                                       uint16_t* __restrict__ deq) {
     const uint32_t nb = (uint32_t)K / 128;  // the launch keeps rows * nb below 2^31
     const uint32_t blk = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (blk >= (uint32_t)rows * nb) return;  // whole waves leave together
@@ -46,19 +44,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     const int e = act_scale_exp(amax);
     const int c2 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v0, -e), ldexpf(v1, -e), 0, false);
     if (codes) *(uint16_t*)(codes + at) = (uint16_t)c2;
-    if (exps && lane == 0) exps[(size_t)r * exp_pitch + b] = (uint8_t)(exp_bias + e);
+    if (exps && lane == 0) exps[(size_t)r * exp_pitch + b] = (int8_t)e;
     if (deq) {
         const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c2, ldexpf(1.0f, e), false);
         *(bf16x2*)(deq + at) = d;
     }
 }
 
-moe_status launch_quantize(const uint16_t* x, int64_t rows, int K, uint8_t* codes, uint8_t* exps,
-                           int exp_pitch, int exp_bias, uint16_t* deq, hipStream_t st) {
+moe_status launch_quantize(const uint16_t* x, int64_t rows, int K, uint8_t* codes, int8_t* exps,
+                           int exp_pitch, uint16_t* deq, hipStream_t st) {
     const int64_t blocks = rows * (K / 128);
     if (blocks > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     quantize_kernel<<<dim3((unsigned)((blocks + 3) / 4)), dim3(256), 0, st>>>(
-        x, (int)rows, K, codes, exps, exp_pitch, exp_bias, deq);
+        x, (int)rows, K, codes, exps, exp_pitch, deq);
     return launch_status();
 }
 
@@ -116,15 +114,15 @@ static A8Plan a8_plan(int T, int k, const moe_expert_weights* w) {
 using namespace moe;
 
 extern "C" moe_status moe_quantize_act(const uint16_t* x, int32_t rows, int32_t K, uint8_t* codes,
-                                       int8_t* exps, void* stream) {
+                                       int8_t* exps, int32_t exp_pitch, void* stream) {
     if (rows < 0 || K < 1) return MOE_ERR_INVALID_ARG;
     if (K % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if (exp_pitch < K / 128) return MOE_ERR_INVALID_ARG;
     if (rows == 0) return MOE_OK;
     if ((int64_t)rows * (K / 128) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     if (!x || !codes || !exps || !aligned16(x) || !aligned16(codes) || !aligned16(exps))
         return MOE_ERR_INVALID_ARG;
-    return launch_quantize(x, rows, K, codes, reinterpret_cast<uint8_t*>(exps), K / 128, 0,
-                           nullptr, as_stream(stream));
+    return launch_quantize(x, rows, K, codes, exps, exp_pitch, nullptr, as_stream(stream));
 }
 
 extern "C" moe_status moe_expert_ffn_a8_workspace_size(int32_t T, int32_t k,
@@ -160,42 +158,25 @@ extern "C" moe_status moe_expert_ffn_a8(const uint16_t* x, int32_t T, int32_t k,
     uint16_t* h = reinterpret_cast<uint16_t*>(base + p.h);
     // phase 1: x -> h
     if (p.fp8_1) {
-        GemmArgs a = a8_args(1, T, k, w);
         uint8_t* codes = base + p.x1;
-        uint8_t* e8 = base + p.x1e;
-        if ((s = launch_quantize(x, T, w->H, codes, e8, p.pitch_h, kE8M0Bias, nullptr, st)) != MOE_OK)
-            return s;
-        a.act = reinterpret_cast<const uint16_t*>(codes);
-        a.aexp = e8;
-        a.perm = perm;
-        a.offsets = offsets;
-        a.w0 = w->w_gate;
-        a.w1 = w->w_up;
-        a.s0 = w->s_gate;
-        a.s1 = w->s_up;
-        a.out = h;
-        if ((s = launch_gemm_a8(1, a, st)) != MOE_OK) return s;
+        int8_t* e = reinterpret_cast<int8_t*>(base + p.x1e);
+        if ((s = launch_quantize(x, T, w->H, codes, e, p.pitch_h, nullptr, st)) != MOE_OK) return s;
+        s = moe_expert_gate_up_a8(codes, e, p.pitch_h, T, k, perm, offsets, w, h, stream);
     } else {
         uint16_t* xq = reinterpret_cast<uint16_t*>(base + p.x1);
-        if ((s = launch_quantize(x, T, w->H, nullptr, nullptr, 0, 0, xq, st)) != MOE_OK) return s;
-        if ((s = moe_expert_gate_up(xq, T, k, perm, offsets, w, h, stream)) != MOE_OK) return s;
+        if ((s = launch_quantize(x, T, w->H, nullptr, nullptr, 0, xq, st)) != MOE_OK) return s;
+        s = moe_expert_gate_up(xq, T, k, perm, offsets, w, h, stream);
     }
+    if (s != MOE_OK) return s;
     // phase 2: h -> y
     if (p.fp8_2) {
-        GemmArgs a = a8_args(2, T, k, w);
         uint8_t* codes = base + p.h2;
-        uint8_t* e8 = base + p.h2e;
-        if ((s = launch_quantize(h, rows, w->I, codes, e8, p.pitch_i, kE8M0Bias, nullptr, st)) != MOE_OK)
+        int8_t* e = reinterpret_cast<int8_t*>(base + p.h2e);
+        if ((s = launch_quantize(h, rows, w->I, codes, e, p.pitch_i, nullptr, st)) != MOE_OK)
             return s;
-        a.act = reinterpret_cast<const uint16_t*>(codes);
-        a.aexp = e8;
-        a.offsets = offsets;
-        a.w0 = w->w_down;
-        a.s0 = w->s_down;
-        a.out = y;
-        return launch_gemm_a8(2, a, st);
+        return moe_expert_down_a8(codes, e, p.pitch_i, T, k, offsets, w, y, stream);
     }
     uint16_t* hq = reinterpret_cast<uint16_t*>(base + p.h2);
-    if ((s = launch_quantize(h, rows, w->I, nullptr, nullptr, 0, 0, hq, st)) != MOE_OK) return s;
+    if ((s = launch_quantize(h, rows, w->I, nullptr, nullptr, 0, hq, st)) != MOE_OK) return s;
     return moe_expert_down(hq, T, k, offsets, w, y, stream);
 }

@@ -200,3 +200,14 @@ def random_topk_ids(T: int, E: int, k: int, seed: int, skew: float = 0.0) -> tor
     for t in range(T):
         ids[t] = rng.choice(E, size=k, replace=False, p=p)
     return torch.from_numpy(ids)
+
+
+def random_fp8_activations(rows: int, K: int, seed: int, exp_range=(-8, 8)):
+    """Quantised activations drawn directly: (codes uint8 [rows, K], every finite E4M3FN code
+    (the NaN codes 0x7F and 0xFF excluded) equally likely; exps int8 [rows, K/128], block
+    exponents uniform in exp_range)."""
+    rng = np.random.default_rng(_seed(seed, 11))
+    codes = rng.integers(0, 254, size=(rows, K), dtype=np.int64)
+    codes = codes + (codes >= 0x7F)  # skip 0x7F; 0xFF is beyond the range drawn
+    exps = rng.integers(exp_range[0], exp_range[1] + 1, size=(rows, K // 128))
+    return torch.from_numpy(codes.astype(np.uint8)), torch.from_numpy(exps.astype(np.int8))

@@ -115,15 +115,40 @@ def test_ffn_workspace():
 
 def test_quantize_act_validation():
     q = moe.lib().moe_quantize_act
-    assert q(None, 4, 256, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert q(FAKE, 4, 256, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert q(FAKE, 4, 256, FAKE, None, None) == moe.MOE_ERR_INVALID_ARG
-    assert q(ctypes.c_void_p(0x1002), 4, 256, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert q(FAKE, -1, 256, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert q(FAKE, 4, 0, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert q(FAKE, 4, 200, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
-    assert q(FAKE, 1 << 30, 1024, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
-    assert q(None, 0, 256, None, None, None) == moe.MOE_OK
+    assert q(None, 4, 256, FAKE, FAKE, 2, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(FAKE, 4, 256, None, FAKE, 2, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(FAKE, 4, 256, FAKE, None, 2, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(ctypes.c_void_p(0x1002), 4, 256, FAKE, FAKE, 2, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(FAKE, -1, 256, FAKE, FAKE, 2, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(FAKE, 4, 0, FAKE, FAKE, 2, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(FAKE, 4, 256, FAKE, FAKE, 1, None) == moe.MOE_ERR_INVALID_ARG  # pitch < K/128
+    assert q(FAKE, 4, 200, FAKE, FAKE, 2, None) == moe.MOE_ERR_UNSUPPORTED
+    assert q(FAKE, 1 << 30, 1024, FAKE, FAKE, 8, None) == moe.MOE_ERR_UNSUPPORTED
+    assert q(None, 0, 256, None, None, 2, None) == moe.MOE_OK
+    assert moe.exp_pitch(7168) == 64 and moe.exp_pitch(2048) == 16 and moe.exp_pitch(640) == 16
+
+
+def test_a8_phase_validation():
+    L = moe.lib()
+    gu, dn = L.moe_expert_gate_up_a8, L.moe_expert_down_a8
+    w = _w(n=4, H=256, I=384)
+    big = (1024, 2)  # T*k = 2048 > 32 * 4 rows: the FP8-code GEMM applies
+    assert gu(FAKE, FAKE, 16, *big, FAKE, FAKE, ctypes.byref(w), None, None) == moe.MOE_ERR_INVALID_ARG
+    assert gu(None, FAKE, 16, *big, FAKE, FAKE, ctypes.byref(w), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert gu(FAKE, FAKE, 1, *big, FAKE, FAKE, ctypes.byref(w), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert gu(FAKE, FAKE, 24, *big, FAKE, FAKE, ctypes.byref(w), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert gu(FAKE, FAKE, 80, *big, FAKE, FAKE, ctypes.byref(w), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert gu(FAKE, FAKE, 16, 16, 2, FAKE, FAKE, ctypes.byref(w), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    bf16 = _w(dtype=1, scales=False)
+    assert gu(FAKE, FAKE, 16, *big, FAKE, FAKE, ctypes.byref(bf16), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    wide = _w(n=4, H=8192 + 128, I=384)
+    assert gu(FAKE, FAKE, 80, *big, FAKE, FAKE, ctypes.byref(wide), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert gu(None, None, 0, 0, 2, None, None, None, None, None) == moe.MOE_OK
+    odd_h = _w(n=4, H=384, I=256)  # phase 2 needs H a multiple of 256
+    assert dn(FAKE, FAKE, 16, *big, FAKE, ctypes.byref(odd_h), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert dn(FAKE, FAKE, 16, *big, FAKE, ctypes.byref(w), None, None) == moe.MOE_ERR_INVALID_ARG
+    assert dn(FAKE, FAKE, 16, 1024, 0, FAKE, ctypes.byref(w), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert dn(None, None, 0, 0, 2, None, None, None, None) == moe.MOE_OK
 
 
 def test_ffn_a8_validation():

@@ -11,8 +11,8 @@ import torch
 import oracle
 import routed_expert_grouped_amd as moe
 import synth
-from gpu_util import (DEV, compare_sampled, compare_with_oracle, layer_for, mid, rel_l2_rows,
-                      run_gpu)
+from gpu_util import (DEV, assert_rows_close, compare_sampled, compare_with_oracle, layer_for, mid,
+                      rel_l2_rows, run_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,7 @@ def test_quantize_act_bit_exact():
     codes, exps = moe.moe_quantize_act(x.to(DEV))
     torch.cuda.synchronize()
     rc, re_ = oracle.quantize_rows(x.numpy().view(np.uint16), x.shape[1])
-    np.testing.assert_array_equal(exps.cpu().numpy(), re_)
+    np.testing.assert_array_equal(exps.cpu().numpy()[:, :x.shape[1] // 128], re_)
     np.testing.assert_array_equal(codes.cpu().numpy(), rc)
     assert re_.min() == -127 and (rc == 0x80).any()  # the clamp and a signed zero were reached
 
@@ -65,7 +65,7 @@ def test_quantize_act_ragged_row_counts():
     rng = np.random.default_rng(3)
     for rows, K in ((1, 128), (3, 384), (5, 7168), (37, 2048)):
         x = _bf16_bits(rng.standard_normal((rows, K)) * 10)
-        codes, exps = moe.moe_quantize_act(x.to(DEV))
+        codes, exps = moe.moe_quantize_act(x.to(DEV), pitch=K // 128)  # unpadded rows
         torch.cuda.synchronize()
         rc, re_ = oracle.quantize_rows(x.numpy().view(np.uint16), K)
         np.testing.assert_array_equal(exps.cpu().numpy(), re_)
@@ -135,6 +135,58 @@ def test_a8_large_layers_sampled_rows(cfg, rows):
     layer = layer_for(cfg)
     g = run_gpu(layer, act="fp8")
     compare_sampled(layer, g, rows=rows, act_fp8=True)
+
+
+def _dequant_bits(codes, exps):
+    """bf16 bits of code * 2^e, exactly: the activations that quantised rows stand for."""
+    v = codes.view(torch.float8_e4m3fn).to(torch.float32)
+    v = v * torch.exp2(exps.to(torch.float32)).repeat_interleave(128, dim=1)
+    return v.to(torch.bfloat16).view(torch.int16)
+
+
+def _padded(exps, pitch):
+    out = torch.zeros((exps.shape[0], pitch), dtype=torch.int8)
+    out[:, :exps.shape[1]] = exps
+    return out
+
+
+@pytest.mark.parametrize("cfg,rows", [
+    (mid(T=200, E=8, k=2), None),                      # every row; ragged m-tiles
+    (mid(T=300, H=2560, I=256, E=4, k=2), None),      # 32-byte exponent pitch, deep m-tile stacks
+    (mid(T=120, H=256, I=1152, E=3, k=1), None),      # odd number of 128-blocks in phase 2
+    ("dsv3_prefill", [0, 1, 777, 2048, 4095]),          # full size, sampled tokens
+])
+def test_a8_phases_exact_inputs(cfg, rows):
+    """The FP8-code GEMMs on quantised activations drawn directly (codes and exponents), against
+    the oracle's phases on the values they stand for: no quantisation on either side."""
+    layer = layer_for(cfg)
+    T, H, I, E, k = layer.T, layer.H, layer.I, layer.E, layer.k
+    ids = synth.random_topk_ids(T, E, k, seed=21)
+    counts, offsets, perm, inv = oracle.permute(ids.numpy(), E)
+    got = moe.moe_permute(ids.to(DEV), E)
+    for a, b in zip(got, (counts, offsets, perm, inv)):
+        np.testing.assert_array_equal(a.cpu().numpy(), b)
+    _, offsets_d, perm_d, _ = got
+    w = moe.expert_weights(layer.experts)
+    xc, xe = synth.random_fp8_activations(T, H, seed=22)
+    hc, he = synth.random_fp8_activations(T * k, I, seed=23)
+    h = moe.moe_expert_gate_up_a8(xc.to(DEV), _padded(xe, moe.exp_pitch(H)).to(DEV), k, perm_d,
+                                  offsets_d, w)
+    y = moe.moe_expert_down_a8(hc.to(DEV), _padded(he, moe.exp_pitch(I)).to(DEV), T, k,
+                               offsets_d, w)
+    torch.cuda.synchronize()
+    flat = np.arange(T * k) if rows is None else np.array([t * k + j for t in rows for j in range(k)])
+    experts = ids.numpy().reshape(-1)[flat]
+    used = sorted(set(experts.tolist()))
+    slot = np.searchsorted(used, experts)
+    sub = layer.experts.select(used)
+    f = oracle.bf16_bits_to_float
+    h_ref = oracle.expert_gate_up(_dequant_bits(xc, xe), flat // k, slot, sub)
+    assert_rows_close("h", f(h.cpu().numpy().view(np.uint16)[inv[flat]]), f(h_ref))
+    p = inv[flat]  # grouped rows of the checked assignments
+    y_ref = oracle.expert_down(_dequant_bits(hc[torch.from_numpy(p)], he[torch.from_numpy(p)]),
+                               slot, sub)
+    assert_rows_close("y", f(y.cpu().numpy().view(np.uint16)[p]), y_ref)
 
 
 def test_a8_rejects_bf16_weights():

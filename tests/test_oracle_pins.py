@@ -419,3 +419,44 @@ def test_ffn_fp8_activations_dense_brute_force():
     # the quantisation changes the result (it is not silently skipped)
     plain = oracle.moe_layer(layer, act_fp8=False)
     assert np.any(plain["out"] != res["out"])
+
+
+def test_expert_phases_dense_brute_force():
+    """The single-phase entry points against numpy float64 matrix products: arbitrary (token,
+    expert) lists, a rectangular H != I scale grid with random per-block scales."""
+    layer = synth.make_layer(dict(T=20, H=384, I=256, E=5, k=2, score_fn="sigmoid",
+                                  scores="uniform", wdtype="fp8"), seed=9)
+    g = torch.Generator().manual_seed(9)
+    for s in (layer.experts.s_gate, layer.experts.s_up, layer.experts.s_down):
+        s.mul_(torch.rand(s.shape, generator=g) * 4 + 0.25)
+    rng = np.random.default_rng(9)
+    token = rng.integers(0, layer.T, 60)
+    slot = rng.integers(0, layer.E, 60)
+    h = oracle.expert_gate_up(layer.x, token, slot, layer.experts)
+    Wg, Wu, Wd = _dense_weights(layer.experts, layer.H, layer.I)
+    x = oracle.bf16_bits_to_float(oracle._np(layer.x, np.uint16))
+    G = np.einsum("pnc,pc->pn", Wg[slot], x[token])
+    U = np.einsum("pnc,pc->pn", Wu[slot], x[token])
+    h_ref = _to_bf16_f64(scipy.special.expit(G) * G * U)
+    hb = oracle.bf16_bits_to_float(h)
+    assert np.mean(hb == h_ref) > 0.999  # (the dense path's fp32 detour may move a tie)
+    np.testing.assert_allclose(hb, h_ref, rtol=2.0 ** -7, atol=0)
+    # phase 2 on bf16 rows of every magnitude class, independent of phase 1
+    hrand = torch.from_numpy(rng.standard_normal((60, layer.I)).astype(np.float32) *
+                             np.exp2(rng.integers(-8, 8, (60, 1))).astype(np.float32))
+    hbits = hrand.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    y = oracle.expert_down(hbits, slot, layer.experts)
+    y_ref = np.einsum("pcn,pn->pc", Wd[slot], oracle.bf16_bits_to_float(hbits))
+    np.testing.assert_allclose(y, y_ref, rtol=1e-12, atol=1e-300)
+
+
+def test_expert_phases_reproduce_the_layer():
+    """Phase 1 then phase 2 on the layer's own (token, expert) pairs give the layer's h and y."""
+    layer = synth.make_layer("tiny_fp8", seed=4)
+    res = oracle.moe_layer(layer, want_h=True, want_y=True)
+    token = np.repeat(np.arange(layer.T), layer.k)
+    slot = res["ids"].reshape(-1)
+    h = oracle.expert_gate_up(layer.x, token, slot, layer.experts)
+    np.testing.assert_array_equal(h, res["h"].reshape(-1, layer.I))
+    y = oracle.expert_down(h, slot, layer.experts)
+    np.testing.assert_array_equal(y, res["y"].reshape(-1, layer.H))
