@@ -282,16 +282,20 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_q256_kernel(GemmArgs a) {
         }
         bsrc[i] = base + ((size_t)e * a.N + wr) * (size_t)K + (((lane & 3) ^ ((r >> 2) & 3)) << 4);
     }
-    auto issue = [&](int q, int st) {
-        const uint8_t* act = (const uint8_t*)a.act + (size_t)q * (kHK * 2);
+    // A wave whose 32 activation rows all lie past the m-tile's last row loads no activations
+    // (no filled m-subtile reads them); the load counts its waits assume follow from kA.
+    const bool load_a = 32 * wave < tile.row1 - tile.row0;
+    auto issue = [&](int q, int st, auto a_tag) {
+        if (decltype(a_tag)::value) {
+            const uint8_t* act = (const uint8_t*)a.act + (size_t)q * (kHK * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            lds_dma16(act + (size_t)aoff[i] * 16, &sA[st][8 * (4 * wave + i) * kHK * 2]);
+            for (int i = 0; i < 4; ++i)
+                lds_dma16(act + (size_t)aoff[i] * 16, &sA[st][8 * (4 * wave + i) * kHK * 2]);
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             lds_dma16(bsrc[i] + (size_t)q * kHK, &sB[st][16 * (2 * wave + i) * kHK]);
     };
-    constexpr int kIssued = 6;  // direct loads per thread per stage
 
     // block scales: phase 1 [0] gate, [1] up of block-row c0/128; phase 2 block-rows c0/128 and
     // c0/128 + 1 (the tile's 256 rows)
@@ -343,9 +347,11 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_q256_kernel(GemmArgs a) {
     // the block adds exactly nothing.
     float u0 = 0.0f, u1 = 0.0f;
     uint32_t m0 = ~0u, m1 = ~0u;
-    auto rescale = [&](float r0, float r1) {
+    // rescales the accumulators of the first NS m-subtiles (the others are never stored)
+    auto rescale = [&](float r0, float r1, auto ns_tag) {
+        constexpr int NS = decltype(ns_tag)::value;
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < NS; ++mi)
 #pragma unroll
             for (int x = 0; x < 16; ++x) {
                 acc[mi][0][x] *= r0;
@@ -353,15 +359,16 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_q256_kernel(GemmArgs a) {
             }
     };
     // one 64-long stage from ring slot ST with NS filled m-subtiles
-    auto stage = [&](int q, auto st_tag, auto ns_tag, auto mask_tag) {
+    auto stage = [&](int q, auto st_tag, auto ns_tag, auto mask_tag, auto a_tag) {
         constexpr int ST = decltype(st_tag)::value, NS = decltype(ns_tag)::value;
         constexpr bool kMask = decltype(mask_tag)::value;
+        constexpr int kIssued = decltype(a_tag)::value ? 6 : 2;  // direct loads per thread per stage
         if (q + 1 < nq)
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued));
         else
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
-        if (q + 2 < nq) issue(q + 2, (ST + 2) % kStages);
+        if (q + 2 < nq) issue(q + 2, (ST + 2) % kStages, a_tag);
         if (NS == 0) return;
         if ((q & 1) == 0) {  // first half of scale block q / 2
             const int kb = q >> 1;
@@ -374,9 +381,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_q256_kernel(GemmArgs a) {
                 u1 = z1 ? u1 : s1;
                 m0 = z0 ? 0u : ~0u;
                 m1 = z1 ? 0u : ~0u;
-                rescale(r0, r1);
+                rescale(r0, r1, ns_tag);
             } else {
-                rescale(u0 * __builtin_amdgcn_rcpf(s0), u1 * __builtin_amdgcn_rcpf(s1));
+                rescale(u0 * __builtin_amdgcn_rcpf(s0), u1 * __builtin_amdgcn_rcpf(s1), ns_tag);
                 u0 = s0;
                 u1 = s1;
             }
@@ -406,34 +413,40 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_q256_kernel(GemmArgs a) {
             }
         }
     };
-    auto run = [&](auto ns_tag, auto mask_tag) {
+    auto run = [&](auto ns_tag, auto mask_tag, auto a_tag) {
         using S0 = std::integral_constant<int, 0>;
         using S1 = std::integral_constant<int, 1>;
         using S2 = std::integral_constant<int, 2>;
+        issue(0, 0, a_tag);
+        issue(1, 1, a_tag);  // nq >= 2
         for (int q = 0; q < nq; q += 3) {
-            stage(q, S0{}, ns_tag, mask_tag);
-            if (q + 1 < nq) stage(q + 1, S1{}, ns_tag, mask_tag);
-            if (q + 2 < nq) stage(q + 2, S2{}, ns_tag, mask_tag);
+            stage(q, S0{}, ns_tag, mask_tag, a_tag);
+            if (q + 1 < nq) stage(q + 1, S1{}, ns_tag, mask_tag, a_tag);
+            if (q + 2 < nq) stage(q + 2, S2{}, ns_tag, mask_tag, a_tag);
         }
     };
     using MY = std::integral_constant<bool, true>;
     using MN = std::integral_constant<bool, false>;
-
-    issue(0, 0);
-    issue(1, 1);  // nq >= 2
-    if (any_zero && mine > 0)
-        run(std::integral_constant<int, 4>{}, MY{});  // rare: all 4 subtiles (unfilled ones are never stored)
-    else if (mine == 4)
-        run(std::integral_constant<int, 4>{}, MN{});
-    else if (mine == 3)
-        run(std::integral_constant<int, 3>{}, MN{});
-    else if (mine == 2)
-        run(std::integral_constant<int, 2>{}, MN{});
-    else if (mine == 1)
-        run(std::integral_constant<int, 1>{}, MN{});
+    // the K loop for this wave's filled-subtile count, zero-scale masking and activation loads
+    auto dispatch = [&](auto a_tag) {
+        if (any_zero && mine > 0)
+            run(std::integral_constant<int, 4>{}, MY{}, a_tag);  // rare: all 4 subtiles (unfilled ones are never stored)
+        else if (mine == 4)
+            run(std::integral_constant<int, 4>{}, MN{}, a_tag);
+        else if (mine == 3)
+            run(std::integral_constant<int, 3>{}, MN{}, a_tag);
+        else if (mine == 2)
+            run(std::integral_constant<int, 2>{}, MN{}, a_tag);
+        else if (mine == 1)
+            run(std::integral_constant<int, 1>{}, MN{}, a_tag);
+        else
+            run(std::integral_constant<int, 0>{}, MN{}, a_tag);
+    };
+    if (load_a)
+        dispatch(std::true_type{});
     else
-        run(std::integral_constant<int, 0>{}, MN{});
-    rescale(u0, u1);
+        dispatch(std::false_type{});
+    rescale(u0, u1, std::integral_constant<int, 4>{});
 
     // D layout of the 32x32 MFMA: value x of a lane is row 8*(x/4) + 4*(lane/32) + x%4 of the
     // subtile, column lane%32

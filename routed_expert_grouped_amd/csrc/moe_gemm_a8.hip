@@ -11,16 +11,19 @@
 //
 // Tiles as in the bf16-operand GEMM of moe_gemm.hip: one 8-wave workgroup per CU computes a
 // 256-row m-tile against 256 weight rows (phase 1: 128 gate + the same 128 up rows -> 128 h
-// columns; phase 2: 256 y columns).  K goes in 64-long stages (16 KB of activation codes +
-// 16 KB of weight codes) through a 4-stage ring.  Loads go directly to LDS three stages ahead.
-// The tile's activation exponents (256 rows x up to 64 blocks) are loaded to LDS once, ahead of
-// the first stage.
+// columns; phase 2: 256 y columns).  K goes in 64-long compute stages.  Operands are loaded
+// directly to LDS, in two rings:
+//   activations  16 KB stages of 64 K (256 rows x 64 bytes), 3 slots, two stages ahead;
+//   weights      32 KB slots of 128 K, one scale block (256 rows x 128 bytes: every row is read
+//                in whole 128-byte lines), 3 slots, two blocks (four stages) ahead;
+//   exponents    4 KB parts of 16 blocks (256 rows x 16 bytes), 2 slots, a part ahead.
 //
 // MFMA operand layout (32x32x64, 32 bytes a lane): lane l supplies row l % 32 of A (column
 // l % 32 of B); its bytes 0-15 are K values [16 h, 16 h + 16) and bytes 16-31 are
-// [32 + 16 h, 48 + 16 h) of the 64-long step, h = l / 32.  Rows of a stage are 64 bytes in LDS,
-// four 16-byte chunks, chunk c at slot c ^ ((row >> 2) & 3), so the fragment reads (chunks h and
-// 2 + h of 32 consecutive rows) are free of bank conflicts.
+// [32 + 16 h, 48 + 16 h) of the 64-long step, h = l / 32.  Activation rows are 64 bytes in LDS,
+// four 16-byte chunks, chunk c at slot c ^ ((row >> 2) & 3); weight rows are 128 bytes, eight
+// chunks, chunk c at slot c ^ ((row >> 1) & 7).  Either way the fragment reads (chunks h and
+// 2 + h of a step, for 32 consecutive rows) are free of bank conflicts.
 #include "libmoe.h"
 #include "moe_device.h"
 #include "moe_ffn.h"
@@ -33,12 +36,14 @@ namespace moe {
 
 typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));
 
-constexpr int kA8M = 256;                     // rows per m-tile
-constexpr int kA8N = 256;                     // weight rows per tile
-constexpr int kA8K = 64;                      // K per stage: one MFMA step, half a scale block
-constexpr int kA8Stages = 4;                  // ring depth
-constexpr int kA8MaxBlocks = kA8MaxPitch;    // exponent bytes per row staged in LDS
-constexpr int kE8M0One = 127;                 // E8M0 encoding of 1.0
+constexpr int kA8M = 256;    // rows per m-tile
+constexpr int kA8N = 256;    // weight rows per tile
+constexpr int kA8K = 64;     // K per compute stage: one MFMA step, half a scale block
+constexpr int kA8BK = 128;   // K per weight slot: one scale block
+constexpr int kARing = 3;    // activation slots
+constexpr int kBRing = 3;    // weight slots
+constexpr int kEPart = 16;   // scale blocks per exponent part
+constexpr int kE8M0One = 127;  // E8M0 encoding of 1.0
 
 __device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
     i32x8 r = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
@@ -48,12 +53,13 @@ __device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
 
 template <int kPhase, bool kGrouped>
 __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
-    constexpr int kStage = kA8M * kA8K;  // 16 KB; the weight stage is the same size
-    static_assert(kA8N * kA8K == kStage, "A and B stages share one layout");
-    __shared__ __attribute__((aligned(1024))) uint8_t sA[kA8Stages][kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t sB[kA8Stages][kStage];
-    __shared__ __attribute__((aligned(16))) uint8_t sE[kA8M * kA8MaxBlocks];  // [row][pitch]
-    __shared__ float sScale[2][kA8MaxBlocks];
+    constexpr int kAStage = kA8M * kA8K;   // 16 KB
+    constexpr int kBSlot = kA8N * kA8BK;   // 32 KB
+    constexpr int kEBytes = kA8M * 16;     // 4 KB
+    __shared__ __attribute__((aligned(1024))) uint8_t sA[kARing][kAStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB[kBRing][kBSlot];
+    __shared__ __attribute__((aligned(1024))) uint8_t sE[2][kEBytes];  // [row][16 blocks]
+    __shared__ float sScale[2][kA8MaxPitch];
 
     constexpr int kCols = kPhase == 1 ? kA8N / 2 : kA8N;
     Tile tile;
@@ -65,7 +71,7 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
     const int e = tile.group;
     const int c0 = tile.nt * kCols;
     const int K = a.K, kblocks = K / 128, nq = 2 * kblocks;
-    const int pitch = a.aexp_pitch;  // a multiple of 16 in [kblocks, kA8MaxPitch]
+    const int cpr = a.aexp_pitch >> 4;  // 16-byte parts of an exponent row (1..4)
     const int fr = lane & 31, half = lane >> 5;
     const uint8_t* act = (const uint8_t*)a.act;
 
@@ -75,16 +81,21 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
         const int p = tile.row0 + r < tile.row1 ? tile.row0 + r : tile.row0;
         return (kPhase == 1 && kGrouped) ? (uint32_t)(a.perm[p] / a.k) : (uint32_t)p;
     };
-    // stage loads: instruction i (0..1) of wave w fills rows 16 (2 w + i) + lane / 4 of the A
-    // and the B stage, slot lane % 4 holding chunk slot ^ ((row >> 2) & 3); activation sources
-    // in 16-byte units (32 bits: the host keeps the codes below 64 GB)
+    // activation loads: instruction i (0..1) of wave w fills stage rows 16 (2 w + i) + lane / 4,
+    // slot lane % 4 holding chunk slot ^ ((row >> 2) & 3); sources in 16-byte units (32 bits: the
+    // host keeps the codes below 64 GB)
     uint32_t aoff[2];
-    const uint8_t* bsrc[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int r = 16 * (2 * wave + i) + (lane >> 2);
-        const uint32_t chunk = (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
-        aoff[i] = src_row(r) * (uint32_t)(K / 16) + chunk;
+        aoff[i] = src_row(r) * (uint32_t)(K / 16) + (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
+    }
+    // weight loads: instruction i (0..3) of wave w fills slot rows 8 (4 w + i) + lane / 8, slot
+    // lane % 8 holding chunk slot ^ ((row >> 1) & 7); phase 1 rows 0..127 gate, 128..255 up
+    const uint8_t* bsrc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 8 * (4 * wave + i) + (lane >> 3);
         const uint8_t* base;
         int wr;
         if (kPhase == 1) {
@@ -94,29 +105,29 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
             base = (const uint8_t*)a.w0;
             wr = c0 + r;
         }
-        bsrc[i] = base + ((size_t)e * a.N + wr) * (size_t)K + (chunk << 4);
+        bsrc[i] = base + ((size_t)e * a.N + wr) * (size_t)K + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
     }
-    // exponent rows: 16-byte chunk c = tid + 512 j of the tile's 256 x pitch bytes (row c / cpr,
-    // part c % cpr) lands at sE + 16 c, i.e. row-major with the global pitch
-    const int cpr = pitch >> 4;
-    const int echunks = kA8M * cpr;  // a multiple of 256: whole waves issue or skip a load
-    uint32_t eoff[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int c = tid + 512 * j;
-        const int r = c < echunks ? c / cpr : 0;
-        eoff[j] = src_row(r) * (uint32_t)cpr + (uint32_t)(c - r * cpr);
-    }
-    auto issue = [&](int q, int st) {
+    // exponent parts: waves 0..3 each fill rows 64 w + lane (16 bytes: blocks 16 p .. 16 p + 15)
+    const uint32_t eoff = src_row((64 * wave + lane) & (kA8M - 1)) * (uint32_t)cpr;
+
+    // A wave whose 32 activation rows all lie past the m-tile's last row loads no activations
+    // (no filled m-subtile reads them); the load counts its waits assume follow from kA.
+    const bool load_a = 32 * wave < tile.row1 - tile.row0;
+    auto issue_a = [&](int q) {
         const uint8_t* aq = act + (size_t)q * kA8K;
+        uint8_t* dst = sA[q % kARing];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            lds_dma16(aq + (size_t)aoff[i] * 16, &sA[st][16 * (2 * wave + i) * kA8K]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            lds_dma16(bsrc[i] + (size_t)q * kA8K, &sB[st][16 * (2 * wave + i) * kA8K]);
+        for (int i = 0; i < 2; ++i) lds_dma16(aq + (size_t)aoff[i] * 16, dst + 16 * (2 * wave + i) * kA8K);
     };
-    constexpr int kIssued = 4;  // direct loads per thread per stage
+    auto issue_b = [&](int kb) {
+        uint8_t* dst = sB[kb % kBRing];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_dma16(bsrc[i] + (size_t)kb * kA8BK, dst + 8 * (4 * wave + i) * kA8BK);
+    };
+    auto issue_e = [&](int part) {  // waves 0..3 (whole waves)
+        if (wave < 4)
+            lds_dma16((const uint8_t*)a.aexp + ((size_t)eoff + part) * 16, &sE[part & 1][16 * 64 * wave]);
+    };
 
     // weight block scales: phase 1 [0] gate, [1] up of block-row c0/128; phase 2 block-rows
     // c0/128 and c0/128 + 1 (the tile's 256 rows)
@@ -130,11 +141,11 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
 
     const int nvalid = (tile.row1 - tile.row0 + 31) >> 5;  // filled 32-row subtiles (1..8)
     const int mine = (nvalid > wm) + (nvalid > wm + 2) + (nvalid > wm + 4) + (nvalid > wm + 6);
-    int aaddr[4][2], baddr[2][2], eaddr[4];
+    int aaddr[4][2], baddr[2][2][2], eaddr[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         const int r = (wm + 2 * mi) * 32 + fr;
-        eaddr[mi] = r * pitch;
+        eaddr[mi] = r * 16;
 #pragma unroll
         for (int j = 0; j < 2; ++j) aaddr[mi][j] = r * kA8K + (((2 * j + half) ^ ((r >> 2) & 3)) << 4);
     }
@@ -142,7 +153,10 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
     for (int ni = 0; ni < 2; ++ni) {
         const int r = (kPhase == 1 ? ni * 128 + wn * 32 : wn * 64 + ni * 32) + fr;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) baddr[ni][j] = r * kA8K + (((2 * j + half) ^ ((r >> 2) & 3)) << 4);
+        for (int hs = 0; hs < 2; ++hs)  // half of the 128-long weight slot
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                baddr[ni][hs][j] = r * kA8BK + (((4 * hs + 2 * j + half) ^ ((r >> 1) & 7)) << 4);
     }
     bool any_zero = false;
     __syncthreads();  // weight scales staged
@@ -176,21 +190,41 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
                 acc[mi][1][x] *= r1;
             }
     };
-    // one 64-long stage from ring slot ST with NS filled m-subtiles
-    auto stage = [&](int q, auto st_tag, auto ns_tag, auto mask_tag) {
+    // Loads in issue order: exponent part 0, weight blocks 0 and 1, activation stages 0 and 1
+    // (kA); then at stage q: (q even) exponent part q / 32 + 1 when q % 32 == 0, weight block
+    // q / 2 + 2; activation stage q + 2 (kA).  Stage q needs activation stage q and weight block
+    // q / 2 (and its exponent part, older than both); the wait allows the loads issued after the
+    // newest of those to stay in flight.  The exponent loads of waves 0..3 are not counted: an
+    // uncounted newer load only makes a wait stricter.
+    auto stage = [&](int q, auto st_tag, auto ns_tag, auto mask_tag, auto a_tag) {
         constexpr int ST = decltype(st_tag)::value, NS = decltype(ns_tag)::value;
-        constexpr bool kMask = decltype(mask_tag)::value;
-        if (q + 2 < nq)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kIssued));
-        else if (q + 1 < nq)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kIssued));
-        else
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        constexpr bool kMask = decltype(mask_tag)::value, kA = decltype(a_tag)::value;
+        constexpr int HS = ST & 1;  // half of the weight slot (q is congruent to ST mod 6)
+        const int kb = q >> 1;
+        const bool b1 = kb + 1 < kblocks, b2 = kb + 2 < kblocks, a1 = q + 1 < nq;
+        if (kA) {
+            if (HS == 0) {
+                if (a1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            } else {
+                if (b2 && a1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(6));
+                else if (b2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+                else if (a1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            }
+        } else {
+            if (HS == 1 && b1 && b2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+            else if (b1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
         __syncthreads();
-        if (q + 3 < nq) issue(q + 3, (ST + 3) % kA8Stages);
+        if (HS == 0) {
+            if ((q & (2 * kEPart - 1)) == 0 && kb + kEPart < kblocks) issue_e(kb / kEPart + 1);
+            if (b2) issue_b(kb + 2);
+        }
+        if (kA && q + 2 < nq) issue_a(q + 2);
         if (NS == 0) return;
-        if ((q & 1) == 0) {  // first half of scale block q / 2
-            const int kb = q >> 1;
+        if (HS == 0) {  // first half of scale block kb
             const float s0 = sScale[sg0][kb], s1 = sScale[sg1][kb];
             if (kMask) {
                 const bool z0 = s0 == 0.0f, z1 = s1 == 0.0f;
@@ -206,17 +240,18 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
                 u0 = s0;
                 u1 = s1;
             }
+            const uint8_t* E = sE[(kb / kEPart) & 1] + (kb & (kEPart - 1));
 #pragma unroll
-            for (int mi = 0; mi < NS; ++mi) sc[mi] = kE8M0One + (int)(int8_t)sE[eaddr[mi] + kb];
+            for (int mi = 0; mi < NS; ++mi) sc[mi] = kE8M0One + (int)(int8_t)E[eaddr[mi]];
         }
-        const uint8_t* A = sA[ST];
-        const uint8_t* B = sB[ST];
+        const uint8_t* A = sA[ST % kARing];
+        const uint8_t* B = sB[(ST >> 1) % kBRing];
         // every fragment of the stage is read before the first MFMA
         i32x8 fb[2], fa[NS > 0 ? NS : 1];
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
-            u32x4 lo = *(const u32x4*)&B[baddr[ni][0]];
-            u32x4 hi = *(const u32x4*)&B[baddr[ni][1]];
+            u32x4 lo = *(const u32x4*)&B[baddr[ni][HS][0]];
+            u32x4 hi = *(const u32x4*)&B[baddr[ni][HS][1]];
             if (kMask) {
                 lo &= ni == 0 ? m0 : m1;
                 hi &= ni == 0 ? m0 : m1;
@@ -233,41 +268,45 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
                 acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     fa[mi], fb[ni], acc[mi][ni], 0, 0, 0, sc[mi], 0, kE8M0One);
     };
-    auto run = [&](auto ns_tag, auto mask_tag) {
-        using S0 = std::integral_constant<int, 0>;
-        using S1 = std::integral_constant<int, 1>;
-        using S2 = std::integral_constant<int, 2>;
-        using S3 = std::integral_constant<int, 3>;
-        for (int q = 0; q < nq; q += 4) {
-            stage(q, S0{}, ns_tag, mask_tag);
-            if (q + 1 < nq) stage(q + 1, S1{}, ns_tag, mask_tag);
-            if (q + 2 < nq) stage(q + 2, S2{}, ns_tag, mask_tag);
-            if (q + 3 < nq) stage(q + 3, S3{}, ns_tag, mask_tag);
+    auto run = [&](auto ns_tag, auto mask_tag, auto a_tag) {
+        issue_e(0);
+        issue_b(0);
+        if (kblocks > 1) issue_b(1);
+        if (decltype(a_tag)::value) {
+            issue_a(0);
+            issue_a(1);  // nq >= 2
+        }
+        // the slots of stage q are q % 3 (activations) and (q / 2) % 3 (weights): period 6
+        for (int q = 0; q < nq; q += 6) {
+            stage(q, std::integral_constant<int, 0>{}, ns_tag, mask_tag, a_tag);
+            if (q + 1 < nq) stage(q + 1, std::integral_constant<int, 1>{}, ns_tag, mask_tag, a_tag);
+            if (q + 2 < nq) stage(q + 2, std::integral_constant<int, 2>{}, ns_tag, mask_tag, a_tag);
+            if (q + 3 < nq) stage(q + 3, std::integral_constant<int, 3>{}, ns_tag, mask_tag, a_tag);
+            if (q + 4 < nq) stage(q + 4, std::integral_constant<int, 4>{}, ns_tag, mask_tag, a_tag);
+            if (q + 5 < nq) stage(q + 5, std::integral_constant<int, 5>{}, ns_tag, mask_tag, a_tag);
         }
     };
     using MY = std::integral_constant<bool, true>;
     using MN = std::integral_constant<bool, false>;
-
-    // exponents first (the first stage's wait covers them), then three stages
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-        if (512 * j + 64 * wave < echunks)
-            lds_dma16((const uint8_t*)a.aexp + (size_t)eoff[j] * 16, &sE[16 * (512 * j + 64 * wave)]);
-    issue(0, 0);
-    issue(1, 1);  // nq >= 2
-    if (nq > 2) issue(2, 2);
-    if (any_zero && mine > 0)
-        run(std::integral_constant<int, 4>{}, MY{});  // rare: all 4 subtiles (unfilled ones are never stored)
-    else if (mine == 4)
-        run(std::integral_constant<int, 4>{}, MN{});
-    else if (mine == 3)
-        run(std::integral_constant<int, 3>{}, MN{});
-    else if (mine == 2)
-        run(std::integral_constant<int, 2>{}, MN{});
-    else if (mine == 1)
-        run(std::integral_constant<int, 1>{}, MN{});
+    // the K loop for this wave's filled-subtile count, zero-scale masking and activation loads
+    auto dispatch = [&](auto a_tag) {
+        if (any_zero && mine > 0)
+            run(std::integral_constant<int, 4>{}, MY{}, a_tag);  // rare: all 4 subtiles (unfilled ones are never stored)
+        else if (mine == 4)
+            run(std::integral_constant<int, 4>{}, MN{}, a_tag);
+        else if (mine == 3)
+            run(std::integral_constant<int, 3>{}, MN{}, a_tag);
+        else if (mine == 2)
+            run(std::integral_constant<int, 2>{}, MN{}, a_tag);
+        else if (mine == 1)
+            run(std::integral_constant<int, 1>{}, MN{}, a_tag);
+        else
+            run(std::integral_constant<int, 0>{}, MN{}, a_tag);
+    };
+    if (load_a)
+        dispatch(std::true_type{});
     else
-        run(std::integral_constant<int, 0>{}, MN{});
+        dispatch(std::false_type{});
     rescale(u0, u1, std::integral_constant<int, 4>{});
 
     // D layout of the 32x32 MFMA: value x of a lane is row 8*(x/4) + 4*(lane/32) + x%4 of the
