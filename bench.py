@@ -131,17 +131,17 @@ def time_layer(layer, steps: int, warmup: int, act: str = "bf16"):
     # call, so it has none)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)] if act == "bf16" else [None] * steps
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]  # step boundaries
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t0.record(stream)
+    marks[0].record(stream)
     for i in range(steps):
         L.forward(layer.scores, layer.x, gate_up_events=ev[i])
-    t1.record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t0.elapsed_time(t1)
+    total_ms = marks[0].elapsed_time(marks[-1])
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
     gu_ms = [e[0].elapsed_time(e[1]) for e in ev if e is not None]
     # The same routed gate/up launch, `steps` times back to back on the same stream between one
     # event pair: the average launch duration without the per-step event latency that the
@@ -164,7 +164,9 @@ def time_layer(layer, steps: int, warmup: int, act: str = "bf16"):
     k1.record(stream)
     torch.cuda.synchronize()
     counts = L.counts.cpu().numpy()
+    pick = lambda f: step_ms[min(steps - 1, int(round(f * (steps - 1))))]
     return dict(total_ms=total_ms, wall_s=wall, gate_up_ms=k0.elapsed_time(k1) / steps,
+                step_ms=dict(median=pick(0.5), p10=pick(0.1), p90=pick(0.9)),
                 gate_up_ms_in_layer=sum(gu_ms) / len(gu_ms) if gu_ms else None, counts=counts)
 
 
@@ -235,6 +237,8 @@ def run_workload(name: str, steps: int, warmup: int, seed: int = 0, act: str = "
     res = dict(
         workload=name, activations=act, T=T, H=H, I=I, E=E, k=k,
         tokens_per_s=T * steps / (r["total_ms"] * 1e-3), ms_per_step=ms,
+        step_ms={q: round(v, 4) for q, v in r["step_ms"].items()},
+        tokens_per_s_median=T / (r["step_ms"]["median"] * 1e-3),
         touched_experts=touched, layer_bytes=lb, layer_flops=lf,
         layer_hbm_frac=round(lb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
         layer_bf16_mfma_frac=round(lf / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
@@ -314,7 +318,8 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "layer": {k: main_res[k] for k in ("touched_experts", "layer_bytes", "layer_flops",
                                            "layer_hbm_frac", "layer_bf16_mfma_frac",
-                                           "layer_fp8_mfma_frac")},
+                                           "layer_fp8_mfma_frac", "step_ms",
+                                           "tokens_per_s_median")},
         "prefill": None if prefill is None else {
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in prefill.items()},
         "prefill_a8": None if a8 is None else {
