@@ -164,9 +164,23 @@ def time_layer(layer, steps: int, warmup: int, act: str = "bf16"):
     k1.record(stream)
     torch.cuda.synchronize()
     counts = L.counts.cpu().numpy()
+    # the same layer captured into a HIP graph and replayed `steps` times
+    graph_ms = None
+    if act == "bf16":
+        L.capture(layer.scores, layer.x)
+        L.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(steps):
+            L.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / steps
     pick = lambda f: step_ms[min(steps - 1, int(round(f * (steps - 1))))]
     return dict(total_ms=total_ms, wall_s=wall, gate_up_ms=k0.elapsed_time(k1) / steps,
-                step_ms=dict(median=pick(0.5), p10=pick(0.1), p90=pick(0.9)),
+                step_ms=dict(median=pick(0.5), p10=pick(0.1), p90=pick(0.9)), graph_ms=graph_ms,
                 gate_up_ms_in_layer=sum(gu_ms) / len(gu_ms) if gu_ms else None, counts=counts)
 
 
@@ -238,6 +252,7 @@ def run_workload(name: str, steps: int, warmup: int, seed: int = 0, act: str = "
         workload=name, activations=act, T=T, H=H, I=I, E=E, k=k,
         tokens_per_s=T * steps / (r["total_ms"] * 1e-3), ms_per_step=ms,
         step_ms={q: round(v, 4) for q, v in r["step_ms"].items()},
+        graph_ms_per_step=None if r["graph_ms"] is None else round(r["graph_ms"], 4),
         tokens_per_s_median=T / (r["step_ms"]["median"] * 1e-3),
         touched_experts=touched, layer_bytes=lb, layer_flops=lf,
         layer_hbm_frac=round(lb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
@@ -319,7 +334,7 @@ def main(argv=None):
         "layer": {k: main_res[k] for k in ("touched_experts", "layer_bytes", "layer_flops",
                                            "layer_hbm_frac", "layer_bf16_mfma_frac",
                                            "layer_fp8_mfma_frac", "step_ms",
-                                           "tokens_per_s_median")},
+                                           "tokens_per_s_median", "graph_ms_per_step")},
         "prefill": None if prefill is None else {
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in prefill.items()},
         "prefill_a8": None if a8 is None else {

@@ -251,6 +251,8 @@ class MoeLayer:
 
     act="fp8" selects the FP8 activation mode (moe_expert_ffn_a8) for the routed and the shared
     experts; `h` then views the routed h inside the workspace, before its quantisation.
+
+    capture(scores, x) records the forward into a HIP graph and replay() reruns it.
     """
 
     def __init__(self, T, H, I, E, k, experts, shared, score_fn="sigmoid", renorm=1, device="cuda",
@@ -287,6 +289,26 @@ class MoeLayer:
         self.sh_y = torch.empty((max(1, T), H), dtype=torch.int16, device=d)
         self.out = torch.empty((max(1, T), H), dtype=torch.int16, device=d)
         self.side = torch.cuda.Stream(device=d) if (overlap_shared and shared is not None) else None
+
+    def capture(self, scores, x):
+        """Record one forward on the tensors `scores` and `x` into a HIP graph; replay() reruns it
+        on whatever they hold then.  None of the layer's calls allocates or clears memory, so the
+        whole sequence (both streams) can be captured."""
+        warm = torch.cuda.Stream()
+        warm.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(warm):
+            self.forward(scores, x)
+        torch.cuda.current_stream().wait_stream(warm)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.forward(scores, x)
+        return self.graph
+
+    def replay(self):
+        """Enqueue the captured forward on torch's current stream; returns `out`."""
+        self.graph.replay()
+        return self.out
 
     def _shared(self, x, st):
         if self.act == "fp8":

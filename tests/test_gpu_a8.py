@@ -81,6 +81,9 @@ def test_quantize_act_ragged_row_counts():
     mid(T=200, H=2560, E=8, k=2),                 # 20 exponent blocks a row (32-byte pitch)
     mid(T=150, H=5120, E=6, k=2),                 # 40 blocks (48-byte pitch)
     mid(T=256, E=32, k=2, scores="zipf"),         # skewed routing
+    mid(T=144, H=8192, I=256, E=2, k=2),          # K = 8192, the FP8-code GEMM's largest
+    mid(T=200, H=16384, I=256, E=4, k=2),         # the largest H: phase 1 dequantises
+    mid(T=150, H=256, I=16384, E=2, k=1),         # the largest I: phase 2 dequantises
 ])
 def test_a8_layer(cfg):
     layer = layer_for(cfg, seed=1)

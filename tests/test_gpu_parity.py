@@ -68,6 +68,9 @@ def test_tiny_layer(cfg):
     dict(T=64, E=16, k=16, renorm=0),        # k = E (every expert), unnormalised sigmoid
     dict(T=96, E=40, k=3, score_fn="softmax", renorm=0, wdtype="bf16"),
     dict(T=160, H=640, E=8, k=2),            # H an odd multiple of 128: register-staged GEMM
+    dict(T=48, H=16384, I=256, E=4, k=2),    # the largest H (MOE_MAX_DIM), GEMV path
+    dict(T=200, H=16384, I=256, E=4, k=2),   # the largest H, GEMM path (128 scale blocks)
+    dict(T=150, H=256, I=16384, E=2, k=1),   # the largest I, GEMM path
 ])
 def test_mid_layer(over):
     layer = layer_for(mid(**over), seed=1)
