@@ -47,6 +47,10 @@ def lib():
         i32 = ctypes.c_int
         L.oracle_fp8_e4m3fn_to_double.restype = ctypes.c_double
         L.oracle_fp8_e4m3fn_to_double.argtypes = [ctypes.c_uint8]
+        L.oracle_fp4_e2m1_to_double.restype = ctypes.c_double
+        L.oracle_fp4_e2m1_to_double.argtypes = [ctypes.c_uint8]
+        L.oracle_e8m0_to_double.restype = ctypes.c_double
+        L.oracle_e8m0_to_double.argtypes = [ctypes.c_uint8]
         L.oracle_bf16_to_double.restype = ctypes.c_double
         L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_double_to_bf16.restype = ctypes.c_uint16
@@ -129,16 +133,29 @@ def permute(ids, E: int):
     return counts, offsets, perm, inv
 
 
+WDTYPE = {"fp8": 0, "bf16": 1, "mxfp4": 2}
+
+
 def _weights(ew, keep):
     """ctypes struct for a synth.ExpertWeights-like object (host copies kept alive in `keep`)."""
-    wd = 1 if ew.wdtype == "bf16" else 0
-    mats = [_np(ew.gate, np.uint16 if wd else np.uint8), _np(ew.up, np.uint16 if wd else np.uint8),
-            _np(ew.down, np.uint16 if wd else np.uint8)]
-    scales = [None, None, None] if wd else [_np(ew.s_gate, np.float32), _np(ew.s_up, np.float32),
-                                            _np(ew.s_down, np.float32)]
+    wd = WDTYPE[ew.wdtype]
+    mt = np.uint16 if wd == 1 else np.uint8
+    mats = [_np(ew.gate, mt), _np(ew.up, mt), _np(ew.down, mt)]
+    st = {0: np.float32, 2: np.uint8}.get(wd)
+    scales = [None] * 3 if st is None else [_np(ew.s_gate, st), _np(ew.s_up, st), _np(ew.s_down, st)]
     keep.extend(mats + scales)
     n, I, H = mats[0].shape
+    if wd == 2:  # two codes a byte along the input dimension
+        H *= 2
     return _Weights(wd, n, H, I, *[_ptr(m) for m in mats], *[_ptr(s) for s in scales])
+
+
+def fp4_e2m1_to_double(code: int) -> float:
+    return lib().oracle_fp4_e2m1_to_double(code)
+
+
+def e8m0_to_double(s: int) -> float:
+    return lib().oracle_e8m0_to_double(s)
 
 
 def float_to_e4m3fn(v: float) -> int:

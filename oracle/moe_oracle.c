@@ -72,6 +72,18 @@ double oracle_fp8_e4m3fn_to_double(uint8_t code) {
     return sign ? -v : v;
 }
 
+/* OCP microscaling FP4 (E2M1): sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent field 0
+ * encodes the subnormals m * 0.5.  The format has no infinity and no NaN; its largest magnitude
+ * is 6.  (The 4-bit weight codec of this library: its groups of 32 values share one E8M0 scale.) */
+double oracle_fp4_e2m1_to_double(uint8_t code) {
+    int sign = (code >> 3) & 1, expo = (code >> 1) & 3, mant = code & 1;
+    double v = expo == 0 ? 0.5 * mant : ldexp(1.0 + 0.5 * mant, expo - 1);
+    return sign ? -v : v;
+}
+
+/* OCP E8M0 scale: 2^(s - 127); s = 255 is NaN. */
+double oracle_e8m0_to_double(uint8_t s) { return s == 255 ? NAN : ldexp(1.0, (int)s - 127); }
+
 /* bf16 is the upper half of an IEEE binary32. */
 double oracle_bf16_to_double(uint16_t bits) {
     uint32_t u = (uint32_t)bits << 16;
@@ -229,6 +241,10 @@ int oracle_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int
 /* n experts of one layer, nn.Linear layout (output rows, input contiguous):
  * gate, up [n][I][H]; down [n][H][I].  wdtype 0: E4M3FN codes with fp32 scales
  * s_gate, s_up [n][I/128][H/128], s_down [n][H/128][I/128]; wdtype 1: bf16 bits, no scales. */
+/* wdtype 0: E4M3FN codes [n][rows][cols] + fp32 scales [n][rows/128][cols/128];
+ *        1: bf16 bits [n][rows][cols] (no scales);
+ *        2: MXFP4, bytes [n][rows][cols/2] (two codes a byte) + E8M0 bytes [n][rows][cols/32]
+ *           (the s_* pointers then point to bytes). */
 typedef struct {
     int32_t wdtype, n, H, I;
     const void *gate, *up, *down;
@@ -257,6 +273,12 @@ static double weight(const oracle_weights* W, const void* mat, const float* sc, 
                      int cols, int r, int c) {
     size_t at = ((size_t)x * rows + r) * cols + c;
     if (W->wdtype == 1) return oracle_bf16_to_double(((const uint16_t*)mat)[at]);
+    if (W->wdtype == 2) {  /* MXFP4: two codes a byte (element 2j low nibble), E8M0 per 32 */
+        const uint8_t b = ((const uint8_t*)mat)[at / 2];
+        const uint8_t code = (c & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15);
+        const uint8_t s = ((const uint8_t*)sc)[at / 32];
+        return oracle_fp4_e2m1_to_double(code) * oracle_e8m0_to_double(s);
+    }
     double scale = sc[((size_t)x * (rows / 128) + r / 128) * (cols / 128) + c / 128];
     return fp8_table[((const uint8_t*)mat)[at]] * scale;
 }

@@ -51,9 +51,10 @@ CONFIGS = {
 
 @dataclasses.dataclass
 class ExpertWeights:
-    """Weights of n experts. fp8: uint8 codes + fp32 scales; bf16: uint16 bit patterns."""
+    """Weights of n experts. fp8: uint8 codes + fp32 scales; bf16: uint16 bit patterns; mxfp4:
+    uint8 bytes of two FP4 codes [n, rows, cols/2] + E8M0 bytes [n, rows, cols/32]."""
 
-    wdtype: str  # "fp8" or "bf16"
+    wdtype: str  # "fp8", "bf16" or "mxfp4"
     gate: torch.Tensor  # [n, I, H]
     up: torch.Tensor  # [n, I, H]
     down: torch.Tensor  # [n, H, I]
@@ -144,6 +145,32 @@ def quantize_fp8_blocks(w: torch.Tensor):
     return q.view(torch.uint8).reshape(*lead, N, K).contiguous(), s.contiguous()
 
 
+MX_GROUP = 32  # values along K sharing one E8M0 scale in the 4-bit weight format
+
+
+def quantize_mxfp4(w: torch.Tensor):
+    """OCP microscaling FP4 quantisation of w [..., N, K] (fp32) along K: per group of 32 the
+    shared scale 2^X with X = floor(log2(max|w|)) - 2 (E8M0 byte X + 127; 0 for an all-zero
+    group), elements = E2M1 of w / 2^X rounded to nearest even and saturated at 6.  Returns
+    (packed codes uint8 [..., N, K/2]: element 2j in the low nibble of byte j, E8M0 bytes uint8
+    [..., N, K/32])."""
+    *lead, N, K = w.shape
+    assert K % MX_GROUP == 0, K
+    g = w.reshape(*lead, N, K // MX_GROUP, MX_GROUP)
+    amax = g.abs().amax(dim=-1)
+    X = torch.where(amax > 0, torch.floor(torch.log2(amax)) - 2, torch.full_like(amax, -127.0))
+    X = X.clamp(-127, 127)
+    p = (g / torch.exp2(X)[..., None]).abs()
+    # E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 (codes 0..7); ties go to the even code
+    edges = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], device=w.device)
+    idx = torch.bucketize(p, edges, right=False)  # a value on an edge gets the lower code
+    tie = torch.isin(p, edges)
+    idx = torch.where(tie & (idx % 2 == 1), idx + 1, idx)  # ties go to the even code
+    codes = (idx | torch.where(g < 0, 8, 0)).to(torch.uint8).reshape(*lead, N, K)
+    packed = codes[..., 0::2] | (codes[..., 1::2] << 4)
+    return packed.contiguous(), (X + 127).to(torch.uint8).contiguous()
+
+
 CHUNK = 16  # experts drawn per generator call
 
 
@@ -161,6 +188,9 @@ def _expert_weights(n: int, H: int, I: int, wdtype: str, seed: int, stream0: int
             mats.append(w)
         if wdtype == "fp8":
             (qg, s_g), (qu, s_u), (qd, s_d) = (quantize_fp8_blocks(w) for w in mats)
+            gate.append(qg); up.append(qu); down.append(qd); sg.append(s_g); su.append(s_u); sd.append(s_d)
+        elif wdtype == "mxfp4":
+            (qg, s_g), (qu, s_u), (qd, s_d) = (quantize_mxfp4(w) for w in mats)
             gate.append(qg); up.append(qu); down.append(qd); sg.append(s_g); su.append(s_u); sd.append(s_d)
         elif wdtype == "bf16":
             gate.append(bf16_bits(mats[0])); up.append(bf16_bits(mats[1])); down.append(bf16_bits(mats[2]))

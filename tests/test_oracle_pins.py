@@ -173,11 +173,21 @@ def test_permute_rejects_out_of_range_ids():
 # ----------------------------------------------------------------------------- expert FFN
 
 
+# The E2M1 magnitudes as the OCP microscaling spec tabulates them (codes 0..7; bit 3 is the sign)
+OCP_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
 def _dense_weights(ew, H, I):
-    """float64 [n, rows, cols] dequantised weights via torch's FP8/bf16 decode and numpy scale expansion."""
+    """float64 [n, rows, cols] dequantised weights via torch's FP8/bf16 decode, the OCP E2M1
+    table for MXFP4, and numpy scale expansion."""
     def deq(q, s):
         if ew.wdtype == "bf16":
             return q.view(torch.bfloat16).to(torch.float64).numpy()
+        if ew.wdtype == "mxfp4":
+            b = q.numpy()
+            codes = np.stack([b & 15, b >> 4], axis=-1).reshape(*b.shape[:-1], -1)
+            v = np.where(codes & 8, -1.0, 1.0) * OCP_E2M1[codes & 7]
+            return v * np.repeat(np.exp2(s.numpy().astype(np.float64) - 127), 32, axis=-1)
         v = q.view(torch.float8_e4m3fn).to(torch.float64).numpy()
         sx = np.repeat(np.repeat(s.numpy().astype(np.float64), 128, axis=1), 128, axis=2)
         return v * sx
@@ -460,3 +470,43 @@ def test_expert_phases_reproduce_the_layer():
     np.testing.assert_array_equal(h, res["h"].reshape(-1, layer.I))
     y = oracle.expert_down(h, slot, layer.experts)
     np.testing.assert_array_equal(y, res["y"].reshape(-1, layer.H))
+
+
+def test_fp4_e2m1_decode_matches_the_ocp_table():
+    for c in range(16):
+        want = (-1.0 if c & 8 else 1.0) * OCP_E2M1[c & 7]
+        assert oracle.fp4_e2m1_to_double(c) == want, c
+
+
+def test_e8m0_decode():
+    assert oracle.e8m0_to_double(127) == 1.0
+    assert np.isnan(oracle.e8m0_to_double(255))
+    v = np.array([oracle.e8m0_to_double(s) for s in range(255)])
+    m, e = np.frexp(v)
+    assert np.all(m == 0.5) and np.all(np.diff(e) == 1)  # consecutive powers of two
+    assert v[0] == 2.0 ** -127 and v[254] == 2.0 ** 127
+
+
+def test_mxfp4_generator_round_to_nearest_even():
+    """The synthetic 4-bit weights: every element is the nearest E2M1 value of w / 2^X (ties to
+    the even code), X = floor(log2(max|w|)) - 2 per group of 32."""
+    g = torch.Generator().manual_seed(3)
+    w = torch.randn((8, 256), generator=g) * 0.02
+    q, sc = synth.quantize_mxfp4(w)
+    (deq,) = [_dense_weights(synth.ExpertWeights("mxfp4", q[None], q[None], q[None], sc[None],
+                                                 sc[None], sc[None]), 256, 8)[0][0]]
+    wd = w.double().numpy()
+    X = np.floor(np.log2(np.abs(wd).reshape(8, 8, 32).max(-1))) - 2
+    assert np.array_equal(sc.numpy().astype(np.int64), (X + 127).astype(np.int64))
+    grid = np.concatenate([-OCP_E2M1[::-1], OCP_E2M1[1:]])
+    p = (wd.reshape(8, 8, 32) / np.exp2(X)[..., None]).reshape(8, 256)
+    err = np.abs(grid[None, None, :] - p[..., None])
+    best = err.min(-1)
+    got = (deq / np.repeat(np.exp2(X), 32, axis=1))
+    assert np.all(np.abs(got - p) <= best + 1e-12)  # a nearest grid value (saturation aside)
+
+
+def test_ffn_dense_brute_force_mxfp4():
+    _check_layer_against_dense(synth.make_layer(dict(T=24, H=256, I=128, E=6, k=2,
+                                                     score_fn="sigmoid", scores="uniform",
+                                                     wdtype="mxfp4"), seed=2))
