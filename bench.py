@@ -8,13 +8,14 @@ combine.
 The headline `value` is tokens/s of the DeepSeek-V3-shaped decode layer (T=16, 256 experts,
 top-8, FP8 block-scaled weights).  The same line carries the 4096-token prefill layer under
 "prefill", the same layer in the opt-in FP8 activation mode under "prefill_a8" (its gate/up
-roofline against the FP8 MFMA peak), the roofline of the dominant kernel (the routed gate/up projection: its launch
+roofline against the FP8 MFMA peak), the decode layer with 4-bit MXFP4 expert weights under
+"decode_mxfp4", the roofline of the dominant kernel (the routed gate/up projection: its launch
 duration from HIP events around back-to-back launches on the main stream, plus the average of
 the per-step brackets inside the layer) and the CPU oracle timed on a bounded sample on the
 host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_decode] [--no-cpu]
-                    [--prefill dsv3_prefill] [--a8 dsv3_prefill]
+                    [--prefill dsv3_prefill] [--a8 dsv3_prefill] [--mxfp4 dsv3_decode]
 """
 from __future__ import annotations
 
@@ -37,18 +38,25 @@ METRIC = "MoE-layer tokens/s at T=16 and T=4096; % of HBM BW / FP8 MFMA peak"
 
 # ------------------------------------------------------------------ algorithmic accounting
 
-def expert_bytes(H: int, I: int, wdtype: str = "fp8") -> int:
-    """Bytes of one expert's three projection matrices (+ fp32 128x128 block scales for FP8)."""
+def matrix_bytes(H: int, I: int, wdtype: str = "fp8") -> int:
+    """Bytes of one H x I projection matrix with its scales: FP8 (+ fp32 per 128x128 block),
+    bf16, or MXFP4 (half a byte a weight + one E8M0 byte per 32)."""
     if wdtype == "fp8":
-        return 3 * H * I + 3 * (H // 128) * (I // 128) * 4
-    return 3 * H * I * 2
+        return H * I + (H // 128) * (I // 128) * 4
+    if wdtype == "mxfp4":
+        return H * I // 2 + H * I // 32
+    return H * I * 2
+
+
+def expert_bytes(H: int, I: int, wdtype: str = "fp8") -> int:
+    """Bytes of one expert's three projection matrices with their scales."""
+    return 3 * matrix_bytes(H, I, wdtype)
 
 
 def gate_up_bytes(T: int, k: int, H: int, I: int, touched: int, wdtype: str = "fp8") -> int:
     """Algorithmic bytes of the routed gate/up launch: the gate and up weights of every touched
     expert once, every token's activation row once, and the bf16 intermediate h written once."""
-    w = 2 * H * I + 2 * (H // 128) * (I // 128) * 4 if wdtype == "fp8" else 2 * H * I * 2
-    return touched * w + T * H * 2 + T * k * I * 2
+    return touched * 2 * matrix_bytes(H, I, wdtype) + T * H * 2 + T * k * I * 2
 
 
 def gate_up_a8_bytes(T: int, k: int, H: int, I: int, touched: int) -> int:
@@ -217,19 +225,21 @@ def cpu_model() -> str:
 
 
 def run_workload(name: str, steps: int, warmup: int, seed: int = 0, act: str = "bf16",
-                 layer=None):
+                 layer=None, wdtype=None):
     import synth
 
     if layer is None:
-        layer = synth.make_layer(name, seed=seed, device="cuda")
+        over = {} if wdtype is None else {"wdtype": wdtype}
+        layer = synth.make_layer(name, seed=seed, device="cuda", **over)
+    wd = layer.experts.wdtype
     r = time_layer(layer, steps, warmup, act)
     T, H, I, E, k = layer.T, layer.H, layer.I, layer.E, layer.k
     touched = int((r["counts"] > 0).sum())
     ms = r["total_ms"] / steps
-    lb = layer_bytes(T, H, I, E, k, touched)
+    lb = layer_bytes(T, H, I, E, k, touched, wd)
     lf = layer_flops(T, H, I, k)
     a8 = act == "fp8"
-    gb = gate_up_a8_bytes(T, k, H, I, touched) if a8 else gate_up_bytes(T, k, H, I, touched)
+    gb = gate_up_a8_bytes(T, k, H, I, touched) if a8 else gate_up_bytes(T, k, H, I, touched, wd)
     gf = gate_up_flops(T, k, H, I)
     gu_s = r["gate_up_ms"] * 1e-3
     bw = gb / gu_s / 1e9
@@ -242,14 +252,15 @@ def run_workload(name: str, steps: int, warmup: int, seed: int = 0, act: str = "
     else:
         roof = dict(bound="mfma", achieved=round(tf, 1), peak=mfma_peak, unit="TFLOP/s",
                     frac=round(tf / mfma_peak, 4))
-    roof.update(traffic=counter_traffic(name + ("_a8" if a8 else "")),
+    roof.update(traffic=counter_traffic(name + ("_a8" if a8 else "") +
+                                        ("_mxfp4" if wd == "mxfp4" else "")),
                 kernel="gate_up_a8 (routed, FP8 activations)" if a8 else "gate_up (routed)",
                 kernel_ms=round(r["gate_up_ms"], 4),
                 kernel_ms_in_layer=(None if r["gate_up_ms_in_layer"] is None
                                     else round(r["gate_up_ms_in_layer"], 4)),
                 algorithmic_bytes=gb, algorithmic_flops=gf)
     res = dict(
-        workload=name, activations=act, T=T, H=H, I=I, E=E, k=k,
+        workload=name, weights=wd, activations=act, T=T, H=H, I=I, E=E, k=k,
         tokens_per_s=T * steps / (r["total_ms"] * 1e-3), ms_per_step=ms,
         step_ms={q: round(v, 4) for q, v in r["step_ms"].items()},
         graph_ms_per_step=None if r["graph_ms"] is None else round(r["graph_ms"], 4),
@@ -271,6 +282,8 @@ def main(argv=None):
     ap.add_argument("--prefill", default="dsv3_prefill", help="second workload ('' to skip)")
     ap.add_argument("--a8", default="dsv3_prefill",
                     help="workload also run in the FP8 activation mode ('' to skip)")
+    ap.add_argument("--mxfp4", default="dsv3_decode",
+                    help="workload also run with 4-bit MXFP4 expert weights ('' to skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-threads", type=int, default=int(os.environ.get("OMP_NUM_THREADS", "0") or 0))
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -301,6 +314,10 @@ def main(argv=None):
                    sample=f"{len(rows)} tokens of the {a.workload} layer (all experts they select "
                           f"+ shared), {dt:.2f} s wall", cpu=cpu_model())
     del layer
+    mx = None
+    if a.mxfp4:
+        torch.cuda.empty_cache()
+        _, mx = run_workload(a.mxfp4, a.steps, a.warmup, wdtype="mxfp4")
     prefill = a8 = None
     if a.prefill:
         torch.cuda.empty_cache()
@@ -339,6 +356,8 @@ def main(argv=None):
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in prefill.items()},
         "prefill_a8": None if a8 is None else {
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in a8.items()},
+        "decode_mxfp4": None if mx is None else {
+            k: (round(v, 4) if isinstance(v, float) else v) for k, v in mx.items()},
     }
     print(json.dumps(line))
     return 0

@@ -57,7 +57,8 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
 
 typedef enum {
     MOE_W_FP8_E4M3_B128 = 0, /* OCP E4M3FN codes + one fp32 scale per 128x128 block: w = code * s */
-    MOE_W_BF16 = 1           /* plain bf16 weights, no scales */
+    MOE_W_BF16 = 1,          /* plain bf16 weights, no scales */
+    MOE_W_MXFP4_G32 = 2      /* OCP MX FP4: E2M1 codes + one E8M0 scale per 32 inputs: w = code * 2^(s-127) */
 } moe_wdtype;
 
 /* Kernel limits of this build. */
@@ -70,6 +71,13 @@ typedef enum {
  *   w_gate, w_up : [n_groups][I][H]     w_down : [n_groups][H][I]
  *   s_gate, s_up : [n_groups][I/128][H/128] fp32   s_down : [n_groups][H/128][I/128] fp32
  * For MOE_W_BF16 the s_* pointers are ignored (may be NULL).  H and I must be multiples of 128.
+ * MOE_W_MXFP4_G32 (4-bit group-quantised weights, 4.25 bits a weight; the pages' quantised
+ * comparison model is a 4-bit group-quantised one [OSDI quantised-model results]): w_gate and
+ * w_up are bytes [n_groups][I][H/2], w_down [n_groups][H][I/2], each byte holding the codes of
+ * two consecutive inputs (the first in the low nibble); s_gate and s_up point to E8M0 bytes
+ * [n_groups][I][H/32], s_down to [n_groups][H][I/32] (one per 32 consecutive inputs of a row;
+ * 16-byte aligned; the float pointer type is reused for these bytes).  These weights run on the
+ * decode kernel at every batch size and are not accepted by the FP8-activation calls.
  * The struct itself is read on the host during the call; the arrays it points to are device
  * memory and must stay valid until the enqueued work completes. */
 typedef struct {

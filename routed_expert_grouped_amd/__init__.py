@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
-MOE_W_FP8_E4M3_B128, MOE_W_BF16 = 0, 1
+MOE_W_FP8_E4M3_B128, MOE_W_BF16, MOE_W_MXFP4_G32 = 0, 1, 2
 SCORE_FN = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
 
 EXPORTS = ("moe_route", "moe_permute", "moe_expert_gate_up", "moe_expert_down",
@@ -94,16 +94,21 @@ def moe_status_string(status: int) -> str:
     return lib().moe_status_string(int(status)).decode()
 
 
+WDTYPE = {"fp8": MOE_W_FP8_E4M3_B128, "bf16": MOE_W_BF16, "mxfp4": MOE_W_MXFP4_G32}
+
+
 def expert_weights(ew) -> MoeExpertWeights:
-    """moe_expert_weights for an object with .wdtype ("fp8"/"bf16"), .gate/.up/.down and
-    .s_gate/.s_up/.s_down device tensors (the arrays must outlive the calls that use it)."""
+    """moe_expert_weights for an object with .wdtype ("fp8", "bf16" or "mxfp4"), .gate/.up/.down
+    and .s_gate/.s_up/.s_down device tensors (the arrays must outlive the calls that use it)."""
     n, I, H = ew.gate.shape
-    fp8 = ew.wdtype == "fp8"
-    return MoeExpertWeights(MOE_W_FP8_E4M3_B128 if fp8 else MOE_W_BF16, n, H, I,
+    if ew.wdtype == "mxfp4":
+        H *= 2  # two codes a byte along the input dimension
+    scaled = ew.wdtype != "bf16"
+    return MoeExpertWeights(WDTYPE[ew.wdtype], n, H, I,
                             ew.gate.data_ptr(), ew.up.data_ptr(), ew.down.data_ptr(),
-                            ew.s_gate.data_ptr() if fp8 else None,
-                            ew.s_up.data_ptr() if fp8 else None,
-                            ew.s_down.data_ptr() if fp8 else None)
+                            ew.s_gate.data_ptr() if scaled else None,
+                            ew.s_up.data_ptr() if scaled else None,
+                            ew.s_down.data_ptr() if scaled else None)
 
 
 def moe_route(scores, k: int, score_fn="sigmoid", renorm: int = 1, topk_ids=None, topk_w=None,

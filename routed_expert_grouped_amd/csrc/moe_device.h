@@ -39,6 +39,17 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
     return r;
 }
 
+// Eight OCP MX FP4 (E2M1) codes (one word, element 2j in the low nibble of byte j) times the
+// scale `s` (a power of two) -> eight bf16 values, exactly.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float s) {
+    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((int)w, s, 0);
+    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((int)w, s, 1);
+    bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((int)w, s, 2);
+    bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((int)w, s, 3);
+    bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return r;
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ------------------------------------------------------------------ wave primitives

@@ -23,7 +23,8 @@ struct GemmArgs {
     const void* w1;
     const float* s0;
     const float* s1;
-    bool fp8;
+    bool fp8;       // E4M3FN weights + fp32 128x128 block scales (s0/s1)
+    bool fp4;       // MXFP4 weights: E2M1 codes two a byte + E8M0 bytes per 32 along K (s0/s1)
     uint16_t* out;  // [rows][N]
     // FP8 activation mode only: act holds E4M3FN codes [rows of act][K] (one byte each) and
     // aexp their block exponents e (scale 2^e), [rows of act][aexp_pitch]

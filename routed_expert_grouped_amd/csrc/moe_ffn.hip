@@ -32,11 +32,27 @@ namespace moe {
 // bandwidth).  Each block goes through the wave's private LDS rows once to change from that
 // load layout to the MFMA operand layout (no workgroup barrier: a wave's LDS operations
 // complete in order).  The K loop keeps two 128-blocks of loads in flight (2-stage ring).
-template <bool kFP8, int kPhase, bool kGrouped, int kWaves>
+//
+// Weight formats (kFmt): kBF16, kFP8 (E4M3FN + fp32 128x128 block scales, post-scaled per block)
+// and kMXFP4 (E2M1 codes, two a byte, + one E8M0 scale per 32 along K).  For MXFP4 the 32 K values
+// a lane multiplies per block are exactly one scale group, so the lane expands its codes to bf16
+// with its group's scale in the conversion instruction (exact: a power of two times a 2-bit
+// significand) and nothing is post-scaled.
+constexpr int kBF16 = 0, kFP8 = 1, kMXFP4 = 2;
+
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+    // 2^(s - 127); s = 0 is the subnormal 2^-127, s = 255 is NaN
+    return __uint_as_float(s == 0 ? 0x00400000u : s == 255 ? 0x7fc00000u : s << 23);
+}
+
+template <int kFmt, int kPhase, bool kGrouped, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     constexpr int kWaveCols = kPhase == 1 ? 16 : 32;  // output columns per wave
     constexpr int kCols = kWaves * kWaveCols;
-    constexpr int kRowB = kFP8 ? 128 : 256;           // bytes of one weight row per 128-block
+    // a stage is kBPS 128-blocks, so that every format loads whole 128-byte lines per row
+    constexpr int kBPS = kFmt == kMXFP4 ? 2 : 1;
+    constexpr int kBB = kFmt == kFP8 ? 128 : kFmt == kMXFP4 ? 64 : 256;  // bytes of a row per block
+    constexpr int kRowB = kBB * kBPS;                 // bytes of a row per stage
     constexpr int kLD = kRowB + 16;                   // LDS row stride: conflict-free reads
     constexpr int kLPR = kRowB / 16;                  // lanes per row in a load instruction
     constexpr int kRPI = 64 / kLPR;                   // rows per load instruction
@@ -64,96 +80,136 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     const uint16_t* arow = a.act + (size_t)ra * K;
     // weight rows: load layout row lrow (+ kRPI per instruction), 16-byte chunk lchunk
     const int n0 = tile.nt * kCols + wave * kWaveCols;
-    const size_t esz = kFP8 ? 1 : 2;
+    const size_t row_bytes = kFmt == kFP8 ? (size_t)K : kFmt == kMXFP4 ? (size_t)K / 2 : (size_t)K * 2;
     const int kblocks = K / 128;
+    const int nst = (kblocks + kBPS - 1) / kBPS;      // stages
+    const int nb_last = kblocks - (nst - 1) * kBPS;   // blocks in the last stage
     const int lrow = lane / kLPR, lchunk = lane % kLPR;
-    const uint8_t* g0 = (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + lrow) * K * esz + lchunk * 16;
+    const uint8_t* g0 = (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + lrow) * row_bytes + lchunk * 16;
     const uint8_t* g1 = kPhase == 1
-        ? (const uint8_t*)a.w1 + ((size_t)e * a.N + n0 + lrow) * K * esz + lchunk * 16
-        : (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + 16 + lrow) * K * esz + lchunk * 16;
-    const size_t ins_stride = (size_t)kRPI * K * esz;  // bytes between a group's instructions
+        ? (const uint8_t*)a.w1 + ((size_t)e * a.N + n0 + lrow) * row_bytes + lchunk * 16
+        : (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + 16 + lrow) * row_bytes + lchunk * 16;
+    const size_t ins_stride = (size_t)kRPI * row_bytes;  // bytes between a group's instructions
     const float* s0 = nullptr;
     const float* s1 = nullptr;
-    if (kFP8) {
+    if (kFmt == kFP8) {
         s0 = a.s0 + ((size_t)e * (a.N / 128) + n0 / 128) * kblocks;
         s1 = kPhase == 1 ? a.s1 + ((size_t)e * (a.N / 128) + n0 / 128) * kblocks : s0;
     }
+    // MXFP4: E8M0 bytes [N][K/32] of this lane's two compute rows (m, and m of the second group);
+    // a dword per block holds the scales of its 4 groups (one per K quarter kq)
+    const uint32_t* q0 = nullptr;
+    const uint32_t* q1 = nullptr;
+    if (kFmt == kMXFP4) {
+        const uint8_t* sb0 = (const uint8_t*)a.s0;
+        const uint8_t* sb1 = (const uint8_t*)(kPhase == 1 ? a.s1 : a.s0);
+        q0 = (const uint32_t*)(sb0 + ((size_t)e * a.N + n0 + m) * (K / 32));
+        q1 = (const uint32_t*)(sb1 + ((size_t)e * a.N + n0 + (kPhase == 1 ? 0 : 16) + m) * (K / 32));
+    }
 
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    u32x4 b0[2][kIns], b1[2][kIns], xa[2][4];
-    float sg0[2], sg1[2];  // block scales of the staged blocks (wave-uniform)
-    auto load = [&](int kb, int st) {
-        sg0[st] = kFP8 ? s0[kb] : 1.0f;
-        sg1[st] = kFP8 ? s1[kb] : 1.0f;
-        const size_t kofs = (size_t)kb * kRowB;
+    u32x4 b0[2][kIns], b1[2][kIns], xa[2][kBPS][4];
+    float sg0[2], sg1[2];             // FP8 block scales of the staged blocks (wave-uniform)
+    uint32_t e0[2][kBPS], e1[2][kBPS];  // MXFP4: E8M0 scales of the staged blocks' 4 groups
+    auto load = [&](int s, int st) {
+        const int kb0 = s * kBPS;
+        sg0[st] = kFmt == kFP8 ? s0[kb0] : 1.0f;
+        sg1[st] = kFmt == kFP8 ? s1[kb0] : 1.0f;
+        // in a short last stage the chunks of the missing block reload the stage's first block
+        // (in the row, never used)
+        size_t kofs = (size_t)s * kRowB;
+        if (kBPS > 1 && kb0 + 1 >= kblocks && lchunk >= kLPR / 2) kofs -= kRowB / 2;
 #pragma unroll
         for (int i = 0; i < kIns; ++i) {
             b0[st][i] = __builtin_nontemporal_load((const u32x4*)(g0 + i * ins_stride + kofs));
             b1[st][i] = __builtin_nontemporal_load((const u32x4*)(g1 + i * ins_stride + kofs));
         }
-        const u32x4* xr = (const u32x4*)(arow + kb * 128 + kq * 32);  // this lane's 32 K values
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xa[st][i] = xr[i];
+        for (int b = 0; b < kBPS; ++b) {
+            const int kb = min(kb0 + b, kblocks - 1);
+            if (kFmt == kMXFP4) {
+                e0[st][b] = q0[kb];
+                e1[st][b] = q1[kb];
+            }
+            const u32x4* xr = (const u32x4*)(arow + kb * 128 + kq * 32);  // this lane's 32 K values
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xa[st][b][i] = xr[i];
+        }
     };
-    auto compute = [&](int st) {
-        // load layout -> LDS rows -> MFMA layout (lane: row m, bytes [kq*32*esz, +32*esz))
+    auto compute = [&](int st, int nb) {
+        // load layout -> LDS rows -> MFMA layout (lane: row m; of block b the 32 K values of
+        // quarter kq, kBB / 4 bytes from byte b * kBB + kq * kBB / 4)
 #pragma unroll
         for (int i = 0; i < kIns; ++i) {
             *(u32x4*)&lds[(i * kRPI + lrow) * kLD + lchunk * 16] = b0[st][i];
             *(u32x4*)&lds[(16 + i * kRPI + lrow) * kLD + lchunk * 16] = b1[st][i];
         }
-        constexpr int kV = kFP8 ? 2 : 4;  // 16-byte vectors per lane per group
-        u32x4 r0[kV], r1[kV];
 #pragma unroll
-        for (int i = 0; i < kV; ++i) {
-            r0[i] = *(const u32x4*)&lds[m * kLD + kq * 32 * esz + i * 16];
-            r1[i] = *(const u32x4*)&lds[(16 + m) * kLD + kq * 32 * esz + i * 16];
-        }
-        f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < kBPS; ++b) {
+            if (b >= nb) break;
+            constexpr int kV = kBB / 64;  // 16-byte vectors per lane per block
+            u32x4 r0[kV], r1[kV];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bf16x8 w0v, w1v;
-            if (kFP8) {
-                const uint32_t* u0 = (const uint32_t*)r0;
-                const uint32_t* u1 = (const uint32_t*)r1;
-                w0v = fp8x8_to_bf16x8(u0[2 * i], u0[2 * i + 1]);
-                w1v = fp8x8_to_bf16x8(u1[2 * i], u1[2 * i + 1]);
-            } else {
-                w0v = as_bf16x8(r0[i]);
-                w1v = as_bf16x8(r1[i]);
+            for (int i = 0; i < kV; ++i) {
+                r0[i] = *(const u32x4*)&lds[m * kLD + b * kBB + kq * (kBB / 4) + i * 16];
+                r1[i] = *(const u32x4*)&lds[(16 + m) * kLD + b * kBB + kq * (kBB / 4) + i * 16];
             }
-            const bf16x8 xv = as_bf16x8(xa[st][i]);
-            p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w0v, p0, 0, 0, 0);
-            p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w1v, p1, 0, 0, 0);
-        }
+            float f0 = 1.0f, f1 = 1.0f;  // MXFP4: this lane's group scales
+            if (kFmt == kMXFP4) {
+                f0 = e8m0_to_f32((e0[st][b] >> (8 * kq)) & 255u);
+                f1 = e8m0_to_f32((e1[st][b] >> (8 * kq)) & 255u);
+            }
+            f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            acc0[r] = fmaf(p0[r], sg0[st], acc0[r]);
-            acc1[r] = fmaf(p1[r], sg1[st], acc1[r]);
+            for (int i = 0; i < 4; ++i) {
+                bf16x8 w0v, w1v;
+                if (kFmt == kFP8) {
+                    const uint32_t* u0 = (const uint32_t*)r0;
+                    const uint32_t* u1 = (const uint32_t*)r1;
+                    w0v = fp8x8_to_bf16x8(u0[2 * i], u0[2 * i + 1]);
+                    w1v = fp8x8_to_bf16x8(u1[2 * i], u1[2 * i + 1]);
+                } else if (kFmt == kMXFP4) {
+                    const uint32_t* u0 = (const uint32_t*)r0;
+                    const uint32_t* u1 = (const uint32_t*)r1;
+                    w0v = fp4x8_to_bf16x8(u0[i], f0);
+                    w1v = fp4x8_to_bf16x8(u1[i], f1);
+                } else {
+                    w0v = as_bf16x8(r0[i]);
+                    w1v = as_bf16x8(r1[i]);
+                }
+                const bf16x8 xv = as_bf16x8(xa[st][b][i]);
+                p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w0v, p0, 0, 0, 0);
+                p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w1v, p1, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                acc0[r] = fmaf(p0[r], sg0[st], acc0[r]);
+                acc1[r] = fmaf(p1[r], sg1[st], acc1[r]);
+            }
         }
     };
-    // 2-stage ring: two blocks in flight.  The steady-state loop issues its loads without
-    // conditions so the compiler's load counters wait only for the block being used; the tail
-    // (1 to 3 blocks) is peeled.  With a single block, stage 1 reloads block 0 (unused).
-    // (scheduling barriers keep each block's loads after the MFMAs of the block they replace)
+    // 2-stage ring: two stages in flight.  The steady-state loop issues its loads without
+    // conditions so the compiler's load counters wait only for the stage being used; the tail
+    // (1 to 3 stages) is peeled.  With a single stage, stage 1 reloads stage 0 (unused).
+    // (scheduling barriers keep each stage's loads after the MFMAs of the stage they replace)
     load(0, 0);
-    load(kblocks > 1 ? 1 : 0, 1);
-    int kb = 0;
-    for (; kb + 3 < kblocks; kb += 2) {
-        compute(0);
+    load(nst > 1 ? 1 : 0, 1);
+    int s = 0;
+    for (; s + 3 < nst; s += 2) {
+        compute(0, kBPS);
         __builtin_amdgcn_sched_barrier(0);
-        load(kb + 2, 0);
+        load(s + 2, 0);
         __builtin_amdgcn_sched_barrier(0);
-        compute(1);
+        compute(1, kBPS);
         __builtin_amdgcn_sched_barrier(0);
-        load(kb + 3, 1);
+        load(s + 3, 1);
         __builtin_amdgcn_sched_barrier(0);
     }
-    const int rest = kblocks - kb;  // 1, 2 or 3
-    compute(0);
-    if (rest == 3) load(kb + 2, 0);
-    if (rest >= 2) compute(1);
-    if (rest == 3) compute(0);
+    const int rest = nst - s;  // 1, 2 or 3
+    compute(0, rest == 1 ? nb_last : kBPS);
+    if (rest == 3) load(s + 2, 0);
+    if (rest >= 2) compute(1, rest == 2 ? nb_last : kBPS);
+    if (rest == 3) compute(0, nb_last);
 
     // D layout of the 16x16 MFMA: lane holds rows 4*(lane/16)+r (grouped rows), column lane%16
 #pragma unroll
@@ -178,7 +234,8 @@ static int max_mtiles(int rows, int n_groups, int BM) {
 
 // Launch one phase.  rows = grouped rows (T*k).
 static moe_status launch_phase(int phase, const GemmArgs& a, hipStream_t st) {
-    if (!use_gemv(a.rows, a.n_groups)) return launch_gemm(phase, a, st);
+    // MXFP4 weights run on the GEMV kernel at every size (there is no 4-bit GEMM)
+    if (!a.fp4 && !use_gemv(a.rows, a.n_groups)) return launch_gemm(phase, a, st);
     constexpr int W = kGemvWaves;
     const int cols = W * (phase == 1 ? 16 : 32);
     const int64_t wgs = (int64_t)max_mtiles(a.rows, a.offsets ? a.n_groups : 1, kGemvBM) * (a.N / cols);
@@ -187,11 +244,13 @@ static moe_status launch_phase(int phase, const GemmArgs& a, hipStream_t st) {
 #define MOE_GEMV(F, P, G) gemv_kernel<F, P, G, W><<<grid, block, 0, st>>>(a)
     const bool g = a.offsets != nullptr;
     if (phase == 1) {
-        if (a.fp8) g ? MOE_GEMV(true, 1, true) : MOE_GEMV(true, 1, false);
-        else g ? MOE_GEMV(false, 1, true) : MOE_GEMV(false, 1, false);
+        if (a.fp8) g ? MOE_GEMV(kFP8, 1, true) : MOE_GEMV(kFP8, 1, false);
+        else if (a.fp4) g ? MOE_GEMV(kMXFP4, 1, true) : MOE_GEMV(kMXFP4, 1, false);
+        else g ? MOE_GEMV(kBF16, 1, true) : MOE_GEMV(kBF16, 1, false);
     } else {
-        if (a.fp8) g ? MOE_GEMV(true, 2, true) : MOE_GEMV(true, 2, false);
-        else g ? MOE_GEMV(false, 2, true) : MOE_GEMV(false, 2, false);
+        if (a.fp8) g ? MOE_GEMV(kFP8, 2, true) : MOE_GEMV(kFP8, 2, false);
+        else if (a.fp4) g ? MOE_GEMV(kMXFP4, 2, true) : MOE_GEMV(kMXFP4, 2, false);
+        else g ? MOE_GEMV(kBF16, 2, true) : MOE_GEMV(kBF16, 2, false);
     }
 #undef MOE_GEMV
     return launch_status();
@@ -224,6 +283,7 @@ extern "C" moe_status moe_expert_gate_up(const uint16_t* x, int32_t T, int32_t k
     a.s0 = w->s_gate;
     a.s1 = w->s_up;
     a.fp8 = w->dtype == MOE_W_FP8_E4M3_B128;
+    a.fp4 = w->dtype == MOE_W_MXFP4_G32;
     a.out = h;
     return launch_phase(1, a, as_stream(stream));
 }
@@ -251,6 +311,7 @@ extern "C" moe_status moe_expert_down(const uint16_t* h, int32_t T, int32_t k,
     a.s0 = w->s_down;
     a.s1 = nullptr;
     a.fp8 = w->dtype == MOE_W_FP8_E4M3_B128;
+    a.fp4 = w->dtype == MOE_W_MXFP4_G32;
     a.out = y;
     return launch_phase(2, a, as_stream(stream));
 }

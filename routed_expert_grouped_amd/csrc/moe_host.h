@@ -25,10 +25,14 @@ inline int ceil_log2(int v) {
 // Validation shared by the expert calls.  `rows` is the number of grouped rows (T*k).
 inline moe_status check_weights(const moe_expert_weights* w) {
     if (!w) return MOE_ERR_INVALID_ARG;
-    if (w->dtype != MOE_W_FP8_E4M3_B128 && w->dtype != MOE_W_BF16) return MOE_ERR_INVALID_ARG;
+    if (w->dtype != MOE_W_FP8_E4M3_B128 && w->dtype != MOE_W_BF16 && w->dtype != MOE_W_MXFP4_G32)
+        return MOE_ERR_INVALID_ARG;
     if (w->n_groups < 1 || w->H < 1 || w->I < 1) return MOE_ERR_INVALID_ARG;
     if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
-    if (w->dtype == MOE_W_FP8_E4M3_B128 && (!w->s_gate || !w->s_up || !w->s_down))
+    if (w->dtype != MOE_W_BF16 && (!w->s_gate || !w->s_up || !w->s_down))
+        return MOE_ERR_INVALID_ARG;
+    if (w->dtype == MOE_W_MXFP4_G32 &&
+        (!aligned16(w->s_gate) || !aligned16(w->s_up) || !aligned16(w->s_down)))
         return MOE_ERR_INVALID_ARG;
     if (!aligned16(w->w_gate) || !aligned16(w->w_up) || !aligned16(w->w_down))
         return MOE_ERR_INVALID_ARG;

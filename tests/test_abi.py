@@ -83,6 +83,12 @@ def test_expert_validation():
     assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(bad_dtype), FAKE, None) == moe.MOE_ERR_INVALID_ARG
     no_scales = _w(scales=False)
     assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(no_scales), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    fp4_no_scales = _w(dtype=2, scales=False)
+    assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(fp4_no_scales), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    fp4 = _w(dtype=2)
+    assert gu(FAKE, 0, 2, FAKE, FAKE, ctypes.byref(fp4), FAKE, None) == moe.MOE_OK
+    bad_dtype3 = _w(dtype=3)
+    assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(bad_dtype3), FAKE, None) == moe.MOE_ERR_INVALID_ARG
     bf16_no_scales = _w(dtype=1, scales=False)
     assert gu(FAKE, 0, 2, FAKE, FAKE, ctypes.byref(bf16_no_scales), FAKE, None) == moe.MOE_OK
     odd = _w(H=200)

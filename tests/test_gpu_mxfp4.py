@@ -1,0 +1,61 @@
+"""GPU parity of the 4-bit MXFP4 weight format (OCP E2M1 codes with one E8M0 scale per 32 inputs)
+against the oracle.  Bars as for the other weight formats."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routed_expert_grouped_amd as moe
+import synth
+from gpu_util import DEV, compare_sampled, compare_with_oracle, layer_for, mid, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def test_mxfp4_decode_and_scale_layout_exhaustive():
+    """Down projection with identity activations reads every weight back exactly:
+    y[p][c] = code(Wd[c][p]) * 2^(s[c][p/32] - 127), over all 16 codes in both nibbles and scales
+    from 2^-20 to 2^20."""
+    H, I = 256, 128
+    rng = np.random.default_rng(0)
+    codes = rng.integers(0, 16, size=(H, I))
+    codes[:16, :16] = np.arange(16)[:, None]  # every code in both nibble positions
+    scales = rng.integers(127 - 20, 127 + 21, size=(H, I // 32))
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    q = torch.from_numpy(packed)[None].to(DEV)
+    s = torch.from_numpy(scales.astype(np.uint8))[None].to(DEV)
+    g = torch.zeros((1, I, H // 2), dtype=torch.uint8, device=DEV)
+    gs = torch.full((1, I, H // 32), 127, dtype=torch.uint8, device=DEV)
+    ew = synth.ExpertWeights("mxfp4", g, g, q, gs, gs, s)
+    eye = torch.eye(I, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).to(DEV)
+    y = moe.moe_expert_down(eye, I, 1, None, moe.expert_weights(ew))
+    torch.cuda.synchronize()
+    got = oracle.bf16_bits_to_float(y.cpu())  # [p][c]
+    want = np.where(codes & 8, -1.0, 1.0) * E2M1[codes & 7] * np.exp2(np.repeat(scales, 32, 1) - 127.0)
+    np.testing.assert_array_equal(got, want.T)
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(T=16, H=256, I=128, E=16, k=2, score_fn="softmax", scores="normal", wdtype="mxfp4"),
+    mid(wdtype="mxfp4"),                       # many rows per expert: the decode kernel still runs
+    mid(T=37, E=64, k=8, wdtype="mxfp4"),
+    mid(T=160, H=640, E=8, k=2, wdtype="mxfp4"),
+])
+def test_mxfp4_layer(cfg):
+    layer = layer_for(cfg, seed=1)
+    compare_with_oracle(layer, run_gpu(layer))
+
+
+def test_mxfp4_dsv3_decode_full():
+    layer = layer_for("dsv3_decode", wdtype="mxfp4")
+    g = run_gpu(layer)
+    compare_sampled(layer, g, rows=list(range(layer.T)))
+
+
+def test_mxfp4_rejected_by_the_fp8_activation_mode():
+    layer = layer_for(mid(wdtype="mxfp4"), seed=1)
+    with pytest.raises(moe.MoeError) as ei:
+        run_gpu(layer, act="fp8")
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
