@@ -90,7 +90,7 @@ def kernel_sources(kernel: str) -> list:
     is compiled in, with the headers it includes: moe_ffn.hip (GEMV kernels and the launches),
     moe_gemm.hip (bf16-activation GEMM) or moe_gemm_a8.hip (FP8-activation GEMM)."""
     if "gemv_kernel" in kernel:
-        names = ["moe_device.h", "moe_ffn.h", "moe_ffn.hip", "moe_host.h"]
+        names = ["moe_device.h", "moe_ffn.h", "moe_ffn.hip", "moe_host.h", "moe_lds.h"]
     elif "gemm_a8_kernel" in kernel:
         names = ["moe_device.h", "moe_ffn.h", "moe_gemm_a8.hip", "moe_host.h", "moe_lds.h"]
     else:

@@ -20,6 +20,7 @@
 #include "moe_device.h"
 #include "moe_ffn.h"
 #include "moe_host.h"
+#include "moe_lds.h"
 
 namespace moe {
 
@@ -38,7 +39,18 @@ namespace moe {
 // a lane multiplies per block are exactly one scale group, so the lane expands its codes to bf16
 // with its group's scale in the conversion instruction (exact: a power of two times a 2-bit
 // significand) and nothing is post-scaled.
+//
+// MXFP4 scales: a wave's 32 weight rows carry K/32 scale bytes each, one dword per 128-block.
+// Loaded per block they would cost a load instruction touching 16 scale rows (16 cache lines
+// for 4 useful bytes each) per row group, which keeps the address unit busier than the weight
+// stream itself.  Instead the wave copies its rows' scales of up to 64 blocks (a window) into
+// its own LDS area with direct global -> LDS loads, coalesced along each row, before its first
+// weight loads, and reads one 8-byte LDS word per row group per stage.  Rows longer than one
+// window (K > 8192) are refilled at each window boundary after the wave's loads have drained.
 constexpr int kBF16 = 0, kFP8 = 1, kMXFP4 = 2;
+constexpr int kScaleWin = 64;    // 128-blocks of scales per window
+constexpr int kScaleSlot = 264;  // LDS bytes per scale load instruction (256 + 8: 8-byte reads
+                                 // of 16 rows fall in distinct banks)
 
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
     // 2^(s - 127); s = 0 is the subnormal 2^-127, s = 255 is NaN
@@ -58,6 +70,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     constexpr int kRPI = 64 / kLPR;                   // rows per load instruction
     constexpr int kIns = 16 / kRPI;                   // load instructions per 16-row group
     __shared__ __attribute__((aligned(16))) uint8_t sW[kWaves][2 * 16 * kLD];
+    constexpr bool kMX = kFmt == kMXFP4;
+    __shared__ __attribute__((aligned(16))) uint8_t sS[kMX ? kWaves : 1][kMX ? 32 * kScaleSlot : 16];
 
     Tile tile;
     const int n_tiles = a.N / kCols;
@@ -96,21 +110,38 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
         s0 = a.s0 + ((size_t)e * (a.N / 128) + n0 / 128) * kblocks;
         s1 = kPhase == 1 ? a.s1 + ((size_t)e * (a.N / 128) + n0 / 128) * kblocks : s0;
     }
-    // MXFP4: E8M0 bytes [N][K/32] of this lane's two compute rows (m, and m of the second group);
-    // a dword per block holds the scales of its 4 groups (one per K quarter kq)
-    const uint32_t* q0 = nullptr;
-    const uint32_t* q1 = nullptr;
-    if (kFmt == kMXFP4) {
-        const uint8_t* sb0 = (const uint8_t*)a.s0;
-        const uint8_t* sb1 = (const uint8_t*)(kPhase == 1 ? a.s1 : a.s0);
-        q0 = (const uint32_t*)(sb0 + ((size_t)e * a.N + n0 + m) * (K / 32));
-        q1 = (const uint32_t*)(sb1 + ((size_t)e * a.N + n0 + (kPhase == 1 ? 0 : 16) + m) * (K / 32));
-    }
+    // MXFP4: E8M0 bytes [N][K/32]; the wave's scale row r (0..31) is weight row n0 + r of w0
+    // (r < 16) and of w1 (phase 1) or w0 (phase 2) (r >= 16).  A dword per block holds the
+    // scales of its 4 groups, one per K quarter kq.  A window of wdw blocks goes to the wave's
+    // LDS area with P = 2^ceil(log2 wdw) (at least 2) dwords per row and 64 / P rows per load
+    // instruction, each instruction filling one kScaleSlot; soff0 / soff1 are the LDS offsets of
+    // this lane's two compute rows (m and 16 + m) in the current window.
+    uint8_t* sl = sS[kMX ? wave : 0];
+    int soff0 = 0, soff1 = 0;
+    auto fill_scales = [&](int w0) {
+        if constexpr (kMX) {
+            const int wdw = min(kScaleWin, kblocks - w0);
+            const int lgP = max(1, 32 - __builtin_clz((unsigned)(wdw - 1) | 1u));
+            const int lgR = 6 - lgP;  // rows per instruction: 2^lgR (1 to 32)
+            const int d = lane & ((1 << lgP) - 1), rr = lane >> lgP;
+            const uint8_t* sb0 = (const uint8_t*)a.s0;
+            const uint8_t* sb1 = (const uint8_t*)(kPhase == 1 ? a.s1 : a.s0);
+            const int nins = 32 >> lgR;
+            for (int i = 0; i < nins; ++i) {
+                const int r = (i << lgR) + rr;  // < 32
+                const uint8_t* row = r < 16 ? sb0 + ((size_t)e * a.N + n0 + r) * (K / 32)
+                                            : sb1 + ((size_t)e * a.N + n0 + (kPhase == 1 ? r - 16 : r)) * (K / 32);
+                lds_dma4(row + 4 * (w0 + min(d, wdw - 1)), sl + i * kScaleSlot);
+            }
+            auto off = [&](int r) { return (r >> lgR) * kScaleSlot + ((r & ((1 << lgR) - 1)) << (lgP + 2)); };
+            soff0 = off(m);
+            soff1 = off(16 + m);
+        }
+    };
 
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     u32x4 b0[2][kIns], b1[2][kIns], xa[2][kBPS][4];
     float sg0[2], sg1[2];             // FP8 block scales of the staged blocks (wave-uniform)
-    uint32_t e0[2][kBPS], e1[2][kBPS];  // MXFP4: E8M0 scales of the staged blocks' 4 groups
     auto load = [&](int s, int st) {
         const int kb0 = s * kBPS;
         sg0[st] = kFmt == kFP8 ? s0[kb0] : 1.0f;
@@ -127,16 +158,28 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
 #pragma unroll
         for (int b = 0; b < kBPS; ++b) {
             const int kb = min(kb0 + b, kblocks - 1);
-            if (kFmt == kMXFP4) {
-                e0[st][b] = q0[kb];
-                e1[st][b] = q1[kb];
-            }
             const u32x4* xr = (const u32x4*)(arow + kb * 128 + kq * 32);  // this lane's 32 K values
 #pragma unroll
             for (int i = 0; i < 4; ++i) xa[st][b][i] = xr[i];
         }
     };
-    auto compute = [&](int st, int nb) {
+    auto compute = [&](int st, int stage, int nb) {
+        // MXFP4: scales of the stage's blocks (a stage starts a window only at a multiple of
+        // kScaleWin / kBPS; the first window is filled before the loop)
+        uint32_t sc0[kBPS], sc1[kBPS];
+        if constexpr (kMX) {
+            const int j = stage * kBPS % kScaleWin;
+            if (j == 0 && stage > 0) {
+                // refill: every load of this wave has landed and every LDS read returned
+                __builtin_amdgcn_s_waitcnt(0);
+                fill_scales(stage * kBPS);
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            }
+            static_assert(kBPS == 2, "one 8-byte LDS read per row group covers a stage");
+            const uint2 v0 = *(const uint2*)(sl + soff0 + 4 * j);
+            const uint2 v1 = *(const uint2*)(sl + soff1 + 4 * j);
+            sc0[0] = v0.x, sc0[1] = v0.y, sc1[0] = v1.x, sc1[1] = v1.y;
+        }
         // load layout -> LDS rows -> MFMA layout (lane: row m; of block b the 32 K values of
         // quarter kq, kBB / 4 bytes from byte b * kBB + kq * kBB / 4)
 #pragma unroll
@@ -155,9 +198,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
                 r1[i] = *(const u32x4*)&lds[(16 + m) * kLD + b * kBB + kq * (kBB / 4) + i * 16];
             }
             float f0 = 1.0f, f1 = 1.0f;  // MXFP4: this lane's group scales
-            if (kFmt == kMXFP4) {
-                f0 = e8m0_to_f32((e0[st][b] >> (8 * kq)) & 255u);
-                f1 = e8m0_to_f32((e1[st][b] >> (8 * kq)) & 255u);
+            if constexpr (kMX) {
+                f0 = e8m0_to_f32((sc0[b] >> (8 * kq)) & 255u);
+                f1 = e8m0_to_f32((sc1[b] >> (8 * kq)) & 255u);
             }
             f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -192,24 +235,30 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     // conditions so the compiler's load counters wait only for the stage being used; the tail
     // (1 to 3 stages) is peeled.  With a single stage, stage 1 reloads stage 0 (unused).
     // (scheduling barriers keep each stage's loads after the MFMAs of the stage they replace)
+    // MXFP4: the first scale window's direct loads go first; at least the 2 * kStageLoads weight
+    // and activation loads of stages 0 and 1 follow them, so waiting until only stage 1's are
+    // outstanding also covers them.
+    constexpr int kStageLoads = 2 * kIns + 4 * kBPS;
+    fill_scales(0);
     load(0, 0);
     load(nst > 1 ? 1 : 0, 1);
+    if constexpr (kMX) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStageLoads));
     int s = 0;
     for (; s + 3 < nst; s += 2) {
-        compute(0, kBPS);
+        compute(0, s, kBPS);
         __builtin_amdgcn_sched_barrier(0);
         load(s + 2, 0);
         __builtin_amdgcn_sched_barrier(0);
-        compute(1, kBPS);
+        compute(1, s + 1, kBPS);
         __builtin_amdgcn_sched_barrier(0);
         load(s + 3, 1);
         __builtin_amdgcn_sched_barrier(0);
     }
     const int rest = nst - s;  // 1, 2 or 3
-    compute(0, rest == 1 ? nb_last : kBPS);
+    compute(0, s, rest == 1 ? nb_last : kBPS);
     if (rest == 3) load(s + 2, 0);
-    if (rest >= 2) compute(1, rest == 2 ? nb_last : kBPS);
-    if (rest == 3) compute(0, nb_last);
+    if (rest >= 2) compute(1, s + 1, rest == 2 ? nb_last : kBPS);
+    if (rest == 3) compute(0, s + 2, nb_last);
 
     // D layout of the 16x16 MFMA: lane holds rows 4*(lane/16)+r (grouped rows), column lane%16
 #pragma unroll

@@ -1,4 +1,4 @@
-// moe_lds.h -- direct global -> LDS loads (gfx950 global_load_lds_dwordx4) and the wait
+// moe_lds.h -- direct global -> LDS loads (gfx950 global_load_lds_dword[x4]) and the wait
 // encoding the kernels that use them count their own loads with.
 //
 // The loads are inline assembly (they set M0), so the compiler does not track them: a kernel
@@ -19,6 +19,15 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >>
 __device__ __forceinline__ void lds_dma16(const void* src, const void* lds) {
     const uint32_t addr = (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)lds;
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(addr))
+                 : "memory", "m0");
+}
+
+// One direct global -> LDS load of 4 bytes per lane: lane l's dword lands at lds + 4 * l.
+__device__ __forceinline__ void lds_dma4(const void* src, const void* lds) {
+    const uint32_t addr = (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)lds;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                  :
                  : "v"(src), "s"(__builtin_amdgcn_readfirstlane(addr))
                  : "memory", "m0");

@@ -14,12 +14,18 @@ pytestmark = pytest.mark.gpu
 E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
-def test_mxfp4_decode_and_scale_layout_exhaustive():
+@pytest.mark.parametrize("I", [
+    128,    # one 128-block per row: the smallest scale window
+    640,    # 5 blocks: a window of odd length, the last stage half used
+    2048,   # 16 blocks
+    8448,   # 66 blocks: a full 64-block scale window, then one of 2
+])
+def test_mxfp4_decode_and_scale_layout_exhaustive(I):
     """Down projection with identity activations reads every weight back exactly:
     y[p][c] = code(Wd[c][p]) * 2^(s[c][p/32] - 127), over all 16 codes in both nibbles and scales
     from 2^-20 to 2^20."""
-    H, I = 256, 128
-    rng = np.random.default_rng(0)
+    H = 256
+    rng = np.random.default_rng(I)
     codes = rng.integers(0, 16, size=(H, I))
     codes[:16, :16] = np.arange(16)[:, None]  # every code in both nibble positions
     scales = rng.integers(127 - 20, 127 + 21, size=(H, I // 32))
@@ -42,6 +48,9 @@ def test_mxfp4_decode_and_scale_layout_exhaustive():
     mid(wdtype="mxfp4"),                       # many rows per expert: the decode kernel still runs
     mid(T=37, E=64, k=8, wdtype="mxfp4"),
     mid(T=160, H=640, E=8, k=2, wdtype="mxfp4"),
+    mid(T=30, H=128, I=384, E=4, k=2, wdtype="mxfp4"),       # K = 128 in phase 1
+    mid(T=60, H=16384, I=256, E=4, k=2, wdtype="mxfp4"),     # the largest H: two scale windows
+    mid(T=40, H=256, I=8320, E=3, k=1, wdtype="mxfp4"),      # phase 2: 65 blocks, a 1-block window
 ])
 def test_mxfp4_layer(cfg):
     layer = layer_for(cfg, seed=1)

@@ -1,5 +1,6 @@
-"""Invariants of the compiled prefill GEMMs (bf16 and FP8 activations) that their hand-counted
-load waits rely on (CPU only: hipcc cross-compiles gfx950 device code without a GPU).
+"""Invariants of the compiled kernels with direct-to-LDS loads (the prefill GEMMs with bf16 and FP8
+activations, and the MXFP4 decode kernel's scale staging) that their hand-counted load waits rely
+on (CPU only: hipcc cross-compiles gfx950 device code without a GPU).
 
 The direct-to-LDS loads are issued from inline assembly, so the compiler neither knows that
 they write M0 nor counts them when it inserts its own load waits; the kernel waits for them
@@ -17,7 +18,7 @@ import pytest
 
 from routed_expert_grouped_amd import build
 
-SRCS = [os.path.join(build.CSRC, f) for f in ("moe_gemm.hip", "moe_gemm_a8.hip")]
+SRCS = [os.path.join(build.CSRC, f) for f in ("moe_gemm.hip", "moe_gemm_a8.hip", "moe_ffn.hip")]
 KERNELS = ("gemm_fp8_q256_kernel", "gemm_a8_kernel")  # the kernels with direct-to-LDS loads
 
 pytestmark = pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not available")
@@ -63,12 +64,12 @@ def test_kernels_present(isa):
 def test_m0_only_in_inline_asm(isa):
     checked = 0
     for name, lines in isa.items():
-        if "gemm" not in name:
+        if "gemm" not in name and "gemv" not in name:
             continue
         checked += 1
         bad = [t for t, inasm in _code(lines) if not inasm and re.search(r"\bm0\b", t)]
         assert not bad, (name, bad[:5])
-    assert checked >= 12
+    assert checked >= 24
 
 
 def test_no_other_vector_memory_between_direct_loads(isa):
@@ -84,3 +85,34 @@ def test_no_other_vector_memory_between_direct_loads(isa):
                   if _VMEM.match(t) and not t.startswith("global_load_lds")]
         assert not inside, (name, inside[:5])
     assert checked == 8
+
+
+def _vmcnt(t):
+    m = re.match(r"s_waitcnt\b.*\bvmcnt\((\d+)\)", t)
+    return int(m.group(1)) if m else None
+
+
+def test_mxfp4_scale_loads_waited_for_before_their_lds_reads(isa):
+    """The MXFP4 decode kernel copies its scales to LDS with direct loads and reads them back with
+    8-byte LDS reads (the only ds_read_b64 in the kernel).  Between a direct load and the next
+    such read there must be an s_waitcnt vmcnt(n) with at least n ordinary loads issued after the
+    direct load (completion is in issue order, so only those n can still be outstanding)."""
+    checked = 0
+    for name, lines in isa.items():
+        if "gemv_kernelILi2E" not in name:
+            continue
+        checked += 1
+        pending, younger, reads = False, 0, 0
+        for t, _ in _code(lines):
+            n = _vmcnt(t)
+            if t.startswith("global_load_lds"):
+                pending, younger = True, 0
+            elif _VMEM.match(t):
+                younger += 1
+            elif n is not None and pending and younger >= n:
+                pending = False
+            elif t.startswith("ds_read_b64"):
+                assert not pending, (name, t)
+                reads += 1
+        assert reads >= 2, name
+    assert checked == 4
