@@ -9,13 +9,15 @@ The headline `value` is tokens/s of the DeepSeek-V3-shaped decode layer (T=16, 2
 top-8, FP8 block-scaled weights).  The same line carries the 4096-token prefill layer under
 "prefill", the same layer in the opt-in FP8 activation mode under "prefill_a8" (its gate/up
 roofline against the FP8 MFMA peak), the decode layer with 4-bit MXFP4 expert weights under
-"decode_mxfp4", the roofline of the dominant kernel (the routed gate/up projection: its launch
+"decode_mxfp4", the prefill layer with MXFP4 expert weights and FP8 activations (W4A8) under
+"prefill_mxfp4_a8", the roofline of the dominant kernel (the routed gate/up projection: its launch
 duration from HIP events around back-to-back launches on the main stream, plus the average of
 the per-step brackets inside the layer) and the CPU oracle timed on a bounded sample on the
 host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_decode] [--no-cpu]
                     [--prefill dsv3_prefill] [--a8 dsv3_prefill] [--mxfp4 dsv3_decode]
+                    [--w4a8 dsv3_prefill]
 """
 from __future__ import annotations
 
@@ -59,10 +61,10 @@ def gate_up_bytes(T: int, k: int, H: int, I: int, touched: int, wdtype: str = "f
     return touched * 2 * matrix_bytes(H, I, wdtype) + T * H * 2 + T * k * I * 2
 
 
-def gate_up_a8_bytes(T: int, k: int, H: int, I: int, touched: int) -> int:
+def gate_up_a8_bytes(T: int, k: int, H: int, I: int, touched: int, wdtype: str = "fp8") -> int:
     """Algorithmic bytes of the FP8-activation gate/up launch: the touched experts' gate and up
     weights (+ scales) once, every token's FP8 codes and exponent row once, h written once."""
-    w = 2 * H * I + 2 * (H // 128) * (I // 128) * 4
+    w = 2 * matrix_bytes(H, I, wdtype)
     pitch = (H // 128 + 15) // 16 * 16
     return touched * w + T * (H + pitch) + T * k * I * 2
 
@@ -239,7 +241,7 @@ def run_workload(name: str, steps: int, warmup: int, seed: int = 0, act: str = "
     lb = layer_bytes(T, H, I, E, k, touched, wd)
     lf = layer_flops(T, H, I, k)
     a8 = act == "fp8"
-    gb = gate_up_a8_bytes(T, k, H, I, touched) if a8 else gate_up_bytes(T, k, H, I, touched, wd)
+    gb = gate_up_a8_bytes(T, k, H, I, touched, wd) if a8 else gate_up_bytes(T, k, H, I, touched, wd)
     gf = gate_up_flops(T, k, H, I)
     gu_s = r["gate_up_ms"] * 1e-3
     bw = gb / gu_s / 1e9
@@ -284,6 +286,8 @@ def main(argv=None):
                     help="workload also run in the FP8 activation mode ('' to skip)")
     ap.add_argument("--mxfp4", default="dsv3_decode",
                     help="workload also run with 4-bit MXFP4 expert weights ('' to skip)")
+    ap.add_argument("--w4a8", default="dsv3_prefill",
+                    help="workload also run with MXFP4 weights and FP8 activations ('' to skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-threads", type=int, default=int(os.environ.get("OMP_NUM_THREADS", "0") or 0))
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -329,6 +333,11 @@ def main(argv=None):
     if a.a8 and a8 is None:
         torch.cuda.empty_cache()
         _, a8 = run_workload(a.a8, max(3, a.steps // 2), max(1, a.warmup // 2), act="fp8")
+    w4 = None
+    if a.w4a8:
+        torch.cuda.empty_cache()
+        _, w4 = run_workload(a.w4a8, max(3, a.steps // 2), max(1, a.warmup // 2), act="fp8",
+                             wdtype="mxfp4")
     line = {
         "metric": METRIC,
         "value": round(main_res["tokens_per_s"], 2),
@@ -358,6 +367,8 @@ def main(argv=None):
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in a8.items()},
         "decode_mxfp4": None if mx is None else {
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in mx.items()},
+        "prefill_mxfp4_a8": None if w4 is None else {
+            k: (round(v, 4) if isinstance(v, float) else v) for k, v in w4.items()},
     }
     print(json.dumps(line))
     return 0

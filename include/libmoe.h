@@ -76,8 +76,10 @@ typedef enum {
  * w_up are bytes [n_groups][I][H/2], w_down [n_groups][H][I/2], each byte holding the codes of
  * two consecutive inputs (the first in the low nibble); s_gate and s_up point to E8M0 bytes
  * [n_groups][I][H/32], s_down to [n_groups][H][I/32] (one per 32 consecutive inputs of a row;
- * 16-byte aligned; the float pointer type is reused for these bytes).  These weights run on the
- * decode kernel at every batch size and are not accepted by the FP8-activation calls.
+ * 16-byte aligned; the float pointer type is reused for these bytes).  With bf16 activations
+ * these weights run on the decode kernel at every batch size; the FP8-activation calls take
+ * them too (W4A8: E2M1 weight codes and their E8M0 scales go straight into the scaled matrix
+ * instruction, beside the E4M3FN activation codes).
  * The struct itself is read on the host during the call; the arrays it points to are device
  * memory and must stay valid until the enqueued work completes. */
 typedef struct {
@@ -185,12 +187,13 @@ moe_status moe_quantize_act(const uint16_t* x, int32_t rows, int32_t K, uint8_t*
 
 /* Expert phase 1 on FP8 activations: moe_expert_gate_up with x given as moe_quantize_act writes
  * it (x_codes [T][H], x_exps [T][exp_pitch]), i.e. with activations x = code * 2^e.  Both
- * operands go to the scaled FP8 matrix instruction; fp32 accumulation, weight block scales
- * after each 128-long partial sum, h as in moe_expert_gate_up.
+ * operands go to the scaled matrix instruction with fp32 accumulation; FP8 weights' block
+ * scales multiply each 128-long partial sum, MXFP4 weights' E8M0 scales are applied by the
+ * instruction with the codes (W4A8); h as in moe_expert_gate_up.
  * For the shapes of the FP8-code GEMM only: UNSUPPORTED when T*k <= 32*n_groups (few rows per
  * expert: moe_expert_ffn_a8 covers those), H > 8192, exp_pitch not a multiple of 16 or above 64,
- * or weights not MOE_W_FP8_E4M3_B128; INVALID_ARG for exp_pitch < H/128; other errors as for
- * moe_expert_gate_up. */
+ * or weights neither MOE_W_FP8_E4M3_B128 nor MOE_W_MXFP4_G32; INVALID_ARG for
+ * exp_pitch < H/128; other errors as for moe_expert_gate_up. */
 moe_status moe_expert_gate_up_a8(const uint8_t* x_codes, const int8_t* x_exps, int32_t exp_pitch,
                                  int32_t T, int32_t k, const int32_t* perm,
                                  const int32_t* offsets, const moe_expert_weights* w, uint16_t* h,
@@ -213,8 +216,9 @@ moe_status moe_expert_ffn_a8_workspace_size(int32_t T, int32_t k, const moe_expe
  * With many rows per expert both operands of each expert GEMM are FP8 codes and the activation
  * scales are applied by the matrix instruction; otherwise the activations are dequantised
  * exactly to bf16 first (same values up to the order of fp32 sums).  The workspace begins with
- * h (bf16 [T*k][I], before its quantisation); the rest holds the quantised activations.  Only
- * FP8 weights (MOE_W_FP8_E4M3_B128) are accepted (UNSUPPORTED otherwise). */
+ * h (bf16 [T*k][I], before its quantisation); the rest holds the quantised activations.  FP8
+ * (MOE_W_FP8_E4M3_B128) and MXFP4 (MOE_W_MXFP4_G32) weights are accepted; bf16 weights are
+ * UNSUPPORTED. */
 moe_status moe_expert_ffn_a8(const uint16_t* x, int32_t T, int32_t k, const int32_t* perm,
                              const int32_t* offsets, const moe_expert_weights* w, uint16_t* y,
                              void* ws, size_t ws_bytes, void* stream);

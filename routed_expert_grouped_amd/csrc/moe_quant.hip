@@ -81,6 +81,7 @@ static GemmArgs a8_args(int phase, int T, int k, const moe_expert_weights* w) {
     a.N = phase == 1 ? w->I : w->H;
     a.K = phase == 1 ? w->H : w->I;
     a.fp8 = w->dtype == MOE_W_FP8_E4M3_B128;
+    a.fp4 = w->dtype == MOE_W_MXFP4_G32;
     a.aexp_pitch = (a.K / 128 + 15) & ~15;
     return a;
 }
@@ -144,7 +145,7 @@ extern "C" moe_status moe_expert_ffn_a8(const uint16_t* x, int32_t T, int32_t k,
     size_t need = 0;
     moe_status s = moe_expert_ffn_a8_workspace_size(T, k, w, &need);
     if (s != MOE_OK) return s;
-    if (w->dtype != MOE_W_FP8_E4M3_B128) return MOE_ERR_UNSUPPORTED;
+    if (w->dtype != MOE_W_FP8_E4M3_B128 && w->dtype != MOE_W_MXFP4_G32) return MOE_ERR_UNSUPPORTED;
     if ((s = check_grouping(T, k, perm, offsets, w, true)) != MOE_OK) return s;
     if (!x || !y || !aligned16(x) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;

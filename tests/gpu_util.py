@@ -78,9 +78,23 @@ def quantise_dequantise(h_bits, K):
     return (q.numpy() / s).reshape(-1, K)
 
 
+_FP4 = None
+_E8M0 = None
+
+
 def down_columns(ew, e, cols):
-    """Columns `cols` of expert e's down matrix [H][I], dequantised (FP8 code x block scale)."""
+    """Columns `cols` of expert e's down matrix [H][I], dequantised (FP8 code x block scale, or
+    MXFP4 code x E8M0 group scale)."""
     idx = torch.as_tensor(cols, dtype=torch.long, device=ew.down.device)
+    if ew.wdtype == "mxfp4":
+        global _FP4, _E8M0
+        if _FP4 is None:
+            _FP4 = np.array([oracle.fp4_e2m1_to_double(c) for c in range(16)])
+            _E8M0 = np.array([oracle.e8m0_to_double(v) for v in range(256)])
+        b = ew.down[e].index_select(1, idx // 2).cpu().numpy()  # [H, n] bytes
+        codes = (b >> (4 * (np.asarray(cols) % 2))) & 15
+        s = ew.s_down[e].index_select(1, idx // 32).cpu().numpy()  # [H, n] E8M0
+        return _FP4[codes] * _E8M0[s]
     q = ew.down[e].index_select(1, idx).cpu().view(torch.float8_e4m3fn).to(torch.float64).numpy()
     sc = ew.s_down[e].index_select(1, idx // 128).cpu().to(torch.float64).numpy()  # [H/128, n]
     return q * np.repeat(sc, 128, axis=0)

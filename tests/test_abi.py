@@ -147,6 +147,10 @@ def test_a8_phase_validation():
     assert gu(FAKE, FAKE, 16, 16, 2, FAKE, FAKE, ctypes.byref(w), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
     bf16 = _w(dtype=1, scales=False)
     assert gu(FAKE, FAKE, 16, *big, FAKE, FAKE, ctypes.byref(bf16), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    # MXFP4 weights pass the format check (W4A8) and reach the later argument checks
+    fp4 = _w(n=4, H=256, I=384, dtype=2)
+    assert gu(FAKE, FAKE, 1, *big, FAKE, FAKE, ctypes.byref(fp4), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert gu(FAKE, FAKE, 1, *big, FAKE, FAKE, ctypes.byref(bf16), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
     wide = _w(n=4, H=8192 + 128, I=384)
     assert gu(FAKE, FAKE, 80, *big, FAKE, FAKE, ctypes.byref(wide), FAKE, None) == moe.MOE_ERR_UNSUPPORTED
     assert gu(None, None, 0, 0, 2, None, None, None, None, None) == moe.MOE_OK
@@ -183,6 +187,10 @@ def test_ffn_a8_validation():
     bf16 = _w(dtype=1, scales=False)
     assert f(FAKE, 16, 2, FAKE, FAKE, ctypes.byref(bf16), FAKE, FAKE, 1 << 30,
              None) == moe.MOE_ERR_UNSUPPORTED
+    fp4 = _w(H=256, I=384, dtype=2)  # accepted: reaches the workspace check
+    assert L.moe_expert_ffn_a8_workspace_size(16, 2, ctypes.byref(fp4), ctypes.byref(n)) == moe.MOE_OK
+    assert f(FAKE, 16, 2, FAKE, FAKE, ctypes.byref(fp4), FAKE, FAKE, n.value - 1,
+             None) == moe.MOE_ERR_WORKSPACE
     assert f(FAKE, 16, 0, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, n.value,
              None) == moe.MOE_ERR_INVALID_ARG
     assert f(None, 0, 2, None, None, None, None, None, 0, None) == moe.MOE_OK

@@ -153,16 +153,18 @@ def _padded(exps, pitch):
     return out
 
 
+@pytest.mark.parametrize("wdtype", ["fp8", "mxfp4"])
 @pytest.mark.parametrize("cfg,rows", [
     (mid(T=200, E=8, k=2), None),                      # every row; ragged m-tiles
     (mid(T=300, H=2560, I=256, E=4, k=2), None),      # 32-byte exponent pitch, deep m-tile stacks
     (mid(T=120, H=256, I=1152, E=3, k=1), None),      # odd number of 128-blocks in phase 2
     ("dsv3_prefill", [0, 1, 777, 2048, 4095]),          # full size, sampled tokens
 ])
-def test_a8_phases_exact_inputs(cfg, rows):
-    """The FP8-code GEMMs on quantised activations drawn directly (codes and exponents), against
-    the oracle's phases on the values they stand for: no quantisation on either side."""
-    layer = layer_for(cfg)
+def test_a8_phases_exact_inputs(cfg, rows, wdtype):
+    """The FP8-code GEMMs (FP8 or MXFP4 weights) on quantised activations drawn directly (codes
+    and exponents), against the oracle's phases on the values they stand for: no quantisation
+    on either side."""
+    layer = layer_for(cfg, wdtype=wdtype) if isinstance(cfg, str) else layer_for(dict(cfg, wdtype=wdtype))
     T, H, I, E, k = layer.T, layer.H, layer.I, layer.E, layer.k
     ids = synth.random_topk_ids(T, E, k, seed=21)
     counts, offsets, perm, inv = oracle.permute(ids.numpy(), E)

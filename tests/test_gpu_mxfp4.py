@@ -63,8 +63,22 @@ def test_mxfp4_dsv3_decode_full():
     compare_sampled(layer, g, rows=list(range(layer.T)))
 
 
-def test_mxfp4_rejected_by_the_fp8_activation_mode():
-    layer = layer_for(mid(wdtype="mxfp4"), seed=1)
-    with pytest.raises(moe.MoeError) as ei:
-        run_gpu(layer, act="fp8")
-    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+@pytest.mark.parametrize("cfg", [
+    mid(wdtype="mxfp4"),                                        # W4A8 GEMMs, ragged m-tiles
+    mid(T=300, E=4, k=1, score_fn="softmax", wdtype="mxfp4"),   # phase 2: 384 = 1.5 weight slots
+    mid(T=200, H=2560, E=8, k=2, wdtype="mxfp4"),               # 10 slots, 32-byte exponent rows
+    mid(T=160, H=640, E=8, k=2, wdtype="mxfp4"),                # 2.5 slots; phase 2 dequantises
+    mid(T=144, H=8192, I=256, E=2, k=2, wdtype="mxfp4"),        # K = 8192, the GEMM's largest
+    mid(T=200, H=16384, I=256, E=4, k=2, wdtype="mxfp4"),       # phase 1 dequantises (K > 8192)
+    mid(T=37, E=64, k=8, wdtype="mxfp4"),                       # few rows: dequantise + GEMV
+])
+def test_w4a8_layer(cfg):
+    """MXFP4 weights with FP8 activations against the oracle's model of the same arithmetic."""
+    layer = layer_for(cfg, seed=1)
+    compare_with_oracle(layer, run_gpu(layer, act="fp8"), act_fp8=True)
+
+
+def test_w4a8_dsv3_prefill_sampled_rows():
+    layer = layer_for("dsv3_prefill", wdtype="mxfp4")
+    g = run_gpu(layer, act="fp8")
+    compare_sampled(layer, g, rows=[0, 1, 2048, 4095], act_fp8=True)

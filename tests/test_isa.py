@@ -7,8 +7,8 @@ they write M0 nor counts them when it inserts its own load waits; the kernel wai
 explicitly with s_waitcnt vmcnt(n), n = loads issued after the ones it needs.  That is correct
 only if
   * no compiler-generated instruction reads or writes M0 (the asm clobbers it), and
-  * no other vector-memory instruction is issued while those loads are in flight (it would
-    shift the counts).
+  * no other vector-memory load is issued while those loads are in flight (it would shift the
+    counts); the only stores are the epilogue's, after the last wait.
 """
 import os
 import re
@@ -56,9 +56,10 @@ def _code(lines):
 
 
 def test_kernels_present(isa):
-    for kernel in KERNELS:
+    for kernel, count in zip(KERNELS, (4, 8)):
         names = [n for n in isa if kernel in n]
-        assert len(names) == 4, names  # 2 phases x (grouped, identity)
+        # 2 phases x (grouped, identity), and for the FP8-activation GEMM x (FP8, MXFP4 weights)
+        assert len(names) == count, names
 
 
 def test_m0_only_in_inline_asm(isa):
@@ -81,10 +82,13 @@ def test_no_other_vector_memory_between_direct_loads(isa):
         code = list(_code(lines))
         dma = [i for i, (t, _) in enumerate(code) if t.startswith("global_load_lds")]
         assert dma, name
+        # the kernels store only in their epilogue, after the K loop's last vmcnt(0) wait; the
+        # compiler may lay that code out between the loop's variants, so stores are allowed
         inside = [t for t, _ in code[dma[0]:dma[-1] + 1]
-                  if _VMEM.match(t) and not t.startswith("global_load_lds")]
+                  if _VMEM.match(t) and not t.startswith("global_load_lds")
+                  and not re.match(r"(global|buffer|flat)_store", t)]
         assert not inside, (name, inside[:5])
-    assert checked == 8
+    assert checked == 12
 
 
 def _vmcnt(t):
@@ -116,3 +120,46 @@ def test_mxfp4_scale_loads_waited_for_before_their_lds_reads(isa):
                 reads += 1
         assert reads >= 2, name
     assert checked == 4
+
+
+def _a8_issue_model(K, w4, load_a):
+    """The FP8-activation GEMM's loads in issue order, and the wait of each stage, as its source
+    states them: weight slots of 128 K (FP8, 4 loads a wave) or 256 K (MXFP4, 4 + 1 scale load),
+    activation stages of 64 K (2 loads); prologue weight slots 0, 1 then activation stages 0, 1;
+    at stage q: wait, then weight slot q / sps + 2 (first stage of a slot), activation stage
+    q + 2.  Yields (loads issued so far, the stage's wait, the loads it needs)."""
+    sps, per_slot = (4, 5) if w4 else (2, 4)
+    nq, nslots = K // 64, -(-K // (64 * sps))
+    seq = []
+    seq += [("B", 0)] * per_slot
+    if nslots > 1:
+        seq += [("B", 1)] * per_slot
+    if load_a:
+        seq += [("A", 0)] * 2 + [("A", 1)] * 2
+    for q in range(nq):
+        hs, sl = q % sps, q // sps
+        b1, b2, a1 = sl + 1 < nslots, sl + 2 < nslots, q + 1 < nq
+        if load_a:  # the kernel's wait immediates
+            if hs == 1:
+                n = per_slot + 2 if b2 and a1 else per_slot if b2 else 2 if a1 else 0
+            else:
+                n = 2 if a1 else 0
+        else:
+            n = 2 * per_slot if hs >= 1 and b1 and b2 else per_slot if b1 else 0
+        yield list(seq), n, {("B", sl)} | ({("A", q)} if load_a else set())
+        if hs == 0 and b2:
+            seq += [("B", sl + 2)] * per_slot
+        if load_a and q + 2 < nq:
+            seq += [("A", q + 2)] * 2
+
+
+@pytest.mark.parametrize("w4", [False, True])
+@pytest.mark.parametrize("load_a", [False, True])
+def test_a8_gemm_waits_cover_exactly_the_needed_loads(w4, load_a):
+    """Loads land in issue order, so vmcnt(n) leaves exactly the last n issued in flight: each
+    stage's n must leave none of the loads it reads, and (for speed) no more than needed, at
+    every K the kernel takes."""
+    for K in range(128, 8192 + 1, 128):
+        for seq, n, need in _a8_issue_model(K, w4, load_a):
+            newest = max(i for i, x in enumerate(seq) if x in need)
+            assert n == len(seq) - 1 - newest, (K, n, len(seq) - 1 - newest)
