@@ -9,15 +9,15 @@ The headline `value` is tokens/s of the DeepSeek-V3-shaped decode layer (T=16, 2
 top-8, FP8 block-scaled weights).  The same line carries the 4096-token prefill layer under
 "prefill", the same layer in the opt-in FP8 activation mode under "prefill_a8" (its gate/up
 roofline against the FP8 MFMA peak), the decode layer with 4-bit MXFP4 expert weights under
-"decode_mxfp4", the prefill layer with MXFP4 expert weights and FP8 activations (W4A8) under
-"prefill_mxfp4_a8", the roofline of the dominant kernel (the routed gate/up projection: its launch
+"decode_mxfp4", the prefill layer with MXFP4 expert weights under "prefill_mxfp4" (bf16
+activations) and "prefill_mxfp4_a8" (FP8 activations, W4A8), the roofline of the dominant kernel (the routed gate/up projection: its launch
 duration from HIP events around back-to-back launches on the main stream, plus the average of
 the per-step brackets inside the layer) and the CPU oracle timed on a bounded sample on the
 host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_decode] [--no-cpu]
                     [--prefill dsv3_prefill] [--a8 dsv3_prefill] [--mxfp4 dsv3_decode]
-                    [--w4a8 dsv3_prefill]
+                    [--mxfp4-prefill dsv3_prefill] [--w4a8 dsv3_prefill]
 """
 from __future__ import annotations
 
@@ -90,11 +90,14 @@ def layer_flops(T, H, I, k, shared=True) -> int:
 def kernel_sources(kernel: str) -> list:
     """Sources (relative to the repository root) of the translation unit a libmoe gate/up kernel
     is compiled in, with the headers it includes: moe_ffn.hip (GEMV kernels and the launches),
-    moe_gemm.hip (bf16-activation GEMM) or moe_gemm_a8.hip (FP8-activation GEMM)."""
+    moe_gemm.hip (bf16-activation GEMM), moe_gemm_a8.hip (FP8-activation GEMM) or
+    moe_gemm_w4.hip (MXFP4 weights, bf16 activations)."""
     if "gemv_kernel" in kernel:
         names = ["moe_device.h", "moe_ffn.h", "moe_ffn.hip", "moe_host.h", "moe_lds.h"]
     elif "gemm_a8_kernel" in kernel:
         names = ["moe_device.h", "moe_ffn.h", "moe_gemm_a8.hip", "moe_host.h", "moe_lds.h"]
+    elif "gemm_w4_kernel" in kernel:
+        names = ["moe_device.h", "moe_ffn.h", "moe_gemm_w4.hip", "moe_host.h", "moe_lds.h"]
     else:
         names = ["moe_device.h", "moe_ffn.h", "moe_ffn.hip", "moe_gemm.hip", "moe_host.h",
                  "moe_lds.h"]
@@ -286,6 +289,8 @@ def main(argv=None):
                     help="workload also run in the FP8 activation mode ('' to skip)")
     ap.add_argument("--mxfp4", default="dsv3_decode",
                     help="workload also run with 4-bit MXFP4 expert weights ('' to skip)")
+    ap.add_argument("--mxfp4-prefill", default="dsv3_prefill",
+                    help="workload also run with MXFP4 weights and bf16 activations ('' to skip)")
     ap.add_argument("--w4a8", default="dsv3_prefill",
                     help="workload also run with MXFP4 weights and FP8 activations ('' to skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -333,8 +338,16 @@ def main(argv=None):
     if a.a8 and a8 is None:
         torch.cuda.empty_cache()
         _, a8 = run_workload(a.a8, max(3, a.steps // 2), max(1, a.warmup // 2), act="fp8")
-    w4 = None
-    if a.w4a8:
+    mxp = w4 = None
+    if a.mxfp4_prefill:
+        torch.cuda.empty_cache()
+        mlayer, mxp = run_workload(a.mxfp4_prefill, max(3, a.steps // 2), max(1, a.warmup // 2),
+                                   wdtype="mxfp4")
+        if a.w4a8 == a.mxfp4_prefill:  # same layer, FP8 activations
+            _, w4 = run_workload(a.w4a8, max(3, a.steps // 2), max(1, a.warmup // 2), act="fp8",
+                                 layer=mlayer)
+        del mlayer
+    if a.w4a8 and w4 is None:
         torch.cuda.empty_cache()
         _, w4 = run_workload(a.w4a8, max(3, a.steps // 2), max(1, a.warmup // 2), act="fp8",
                              wdtype="mxfp4")
@@ -367,6 +380,8 @@ def main(argv=None):
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in a8.items()},
         "decode_mxfp4": None if mx is None else {
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in mx.items()},
+        "prefill_mxfp4": None if mxp is None else {
+            k: (round(v, 4) if isinstance(v, float) else v) for k, v in mxp.items()},
         "prefill_mxfp4_a8": None if w4 is None else {
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in w4.items()},
     }

@@ -77,9 +77,11 @@ typedef enum {
  * two consecutive inputs (the first in the low nibble); s_gate and s_up point to E8M0 bytes
  * [n_groups][I][H/32], s_down to [n_groups][H][I/32] (one per 32 consecutive inputs of a row;
  * 16-byte aligned; the float pointer type is reused for these bytes).  With bf16 activations
- * these weights run on the decode kernel at every batch size; the FP8-activation calls take
- * them too (W4A8: E2M1 weight codes and their E8M0 scales go straight into the scaled matrix
- * instruction, beside the E4M3FN activation codes).
+ * the codes are expanded exactly to bf16 with their group's scale (few rows per expert: the
+ * decode kernel; many: a 4-bit GEMM, for phase 1 with I a multiple of 128 and phase 2 with H a
+ * multiple of 256, else the decode kernel).  The FP8-activation calls take them too (W4A8: E2M1
+ * weight codes and their E8M0 scales go straight into the scaled matrix instruction, beside the
+ * E4M3FN activation codes).
  * The struct itself is read on the host during the call; the arrays it points to are device
  * memory and must stay valid until the enqueued work completes. */
 typedef struct {

@@ -50,6 +50,11 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float s) {
     return r;
 }
 
+// The E8M0 scale byte s as a float: 2^(s - 127); s = 0 is the subnormal 2^-127, s = 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+    return __uint_as_float(s == 0 ? 0x00400000u : s == 255 ? 0x7fc00000u : s << 23);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ------------------------------------------------------------------ wave primitives

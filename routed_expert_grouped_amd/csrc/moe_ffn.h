@@ -54,4 +54,9 @@ constexpr int kA8MaxPitch = kA8MaxK / 128;
 bool a8_gemm_fits(int phase, const GemmArgs& a);
 moe_status launch_gemm_a8(int phase, const GemmArgs& a, hipStream_t st);
 
+// MXFP4 weights with bf16 activations, many rows per expert: the 4-bit GEMM (moe_gemm_w4.hip)
+// for the shapes w4_gemm_fits accepts; the decode kernel runs the rest
+bool w4_gemm_fits(int phase, const GemmArgs& a);
+moe_status launch_gemm_w4(int phase, const GemmArgs& a, hipStream_t st);
+
 }  // namespace moe

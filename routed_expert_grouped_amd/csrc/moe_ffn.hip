@@ -52,11 +52,6 @@ constexpr int kScaleWin = 64;    // 128-blocks of scales per window
 constexpr int kScaleSlot = 264;  // LDS bytes per scale load instruction (256 + 8: 8-byte reads
                                  // of 16 rows fall in distinct banks)
 
-__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-    // 2^(s - 127); s = 0 is the subnormal 2^-127, s = 255 is NaN
-    return __uint_as_float(s == 0 ? 0x00400000u : s == 255 ? 0x7fc00000u : s << 23);
-}
-
 template <int kFmt, int kPhase, bool kGrouped, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     constexpr int kWaveCols = kPhase == 1 ? 16 : 32;  // output columns per wave
@@ -283,8 +278,11 @@ static int max_mtiles(int rows, int n_groups, int BM) {
 
 // Launch one phase.  rows = grouped rows (T*k).
 static moe_status launch_phase(int phase, const GemmArgs& a, hipStream_t st) {
-    // MXFP4 weights run on the GEMV kernel at every size (there is no 4-bit GEMM)
-    if (!a.fp4 && !use_gemv(a.rows, a.n_groups)) return launch_gemm(phase, a, st);
+    // many rows per expert: the GEMMs (MXFP4 weights: the 4-bit GEMM where its shape fits)
+    if (!use_gemv(a.rows, a.n_groups)) {
+        if (!a.fp4) return launch_gemm(phase, a, st);
+        if (w4_gemm_fits(phase, a)) return launch_gemm_w4(phase, a, st);
+    }
     constexpr int W = kGemvWaves;
     const int cols = W * (phase == 1 ? 16 : 32);
     const int64_t wgs = (int64_t)max_mtiles(a.rows, a.offsets ? a.n_groups : 1, kGemvBM) * (a.N / cols);

@@ -14,16 +14,18 @@ pytestmark = pytest.mark.gpu
 E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
+@pytest.mark.parametrize("route", ["gemv", "gemm"])
 @pytest.mark.parametrize("I", [
     128,    # one 128-block per row: the smallest scale window
     640,    # 5 blocks: a window of odd length, the last stage half used
     2048,   # 16 blocks
     8448,   # 66 blocks: a full 64-block scale window, then one of 2
 ])
-def test_mxfp4_decode_and_scale_layout_exhaustive(I):
+def test_mxfp4_decode_and_scale_layout_exhaustive(I, route):
     """Down projection with identity activations reads every weight back exactly:
     y[p][c] = code(Wd[c][p]) * 2^(s[c][p/32] - 127), over all 16 codes in both nibbles and scales
-    from 2^-20 to 2^20."""
+    from 2^-20 to 2^20.  "gemv": 32 rows a call (the decode kernel); "gemm": all I rows in one
+    call (the 4-bit GEMM)."""
     H = 256
     rng = np.random.default_rng(I)
     codes = rng.integers(0, 16, size=(H, I))
@@ -36,7 +38,12 @@ def test_mxfp4_decode_and_scale_layout_exhaustive(I):
     gs = torch.full((1, I, H // 32), 127, dtype=torch.uint8, device=DEV)
     ew = synth.ExpertWeights("mxfp4", g, g, q, gs, gs, s)
     eye = torch.eye(I, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).to(DEV)
-    y = moe.moe_expert_down(eye, I, 1, None, moe.expert_weights(ew))
+    w = moe.expert_weights(ew)
+    if route == "gemm":
+        y = moe.moe_expert_down(eye, I, 1, None, w)
+    else:
+        y = torch.cat([moe.moe_expert_down(eye[p:p + 32].contiguous(), 32, 1, None, w)
+                       for p in range(0, I, 32)])
     torch.cuda.synchronize()
     got = oracle.bf16_bits_to_float(y.cpu())  # [p][c]
     want = np.where(codes & 8, -1.0, 1.0) * E2M1[codes & 7] * np.exp2(np.repeat(scales, 32, 1) - 127.0)
@@ -45,16 +52,25 @@ def test_mxfp4_decode_and_scale_layout_exhaustive(I):
 
 @pytest.mark.parametrize("cfg", [
     dict(T=16, H=256, I=128, E=16, k=2, score_fn="softmax", scores="normal", wdtype="mxfp4"),
-    mid(wdtype="mxfp4"),                       # many rows per expert: the decode kernel still runs
+    mid(wdtype="mxfp4"),                       # many rows per expert: the 4-bit GEMM
     mid(T=37, E=64, k=8, wdtype="mxfp4"),
-    mid(T=160, H=640, E=8, k=2, wdtype="mxfp4"),
+    mid(T=160, H=640, E=8, k=2, wdtype="mxfp4"),              # phase 2 (N = 640) on the decode kernel
     mid(T=30, H=128, I=384, E=4, k=2, wdtype="mxfp4"),       # K = 128 in phase 1
     mid(T=60, H=16384, I=256, E=4, k=2, wdtype="mxfp4"),     # the largest H: two scale windows
     mid(T=40, H=256, I=8320, E=3, k=1, wdtype="mxfp4"),      # phase 2: 65 blocks, a 1-block window
+    mid(T=300, E=4, k=1, score_fn="softmax", wdtype="mxfp4"),  # 4-bit GEMM: deep m-tile stacks
+    mid(T=200, H=16384, I=256, E=4, k=2, wdtype="mxfp4"),    # 4-bit GEMM at K = 16384
+    mid(T=200, H=256, I=8320, E=3, k=1, wdtype="mxfp4"),     # 4-bit GEMM phase 2: 65 slots (odd)
 ])
 def test_mxfp4_layer(cfg):
     layer = layer_for(cfg, seed=1)
     compare_with_oracle(layer, run_gpu(layer))
+
+
+def test_mxfp4_dsv3_prefill_sampled_rows():
+    layer = layer_for("dsv3_prefill", wdtype="mxfp4")
+    g = run_gpu(layer)
+    compare_sampled(layer, g, rows=[0, 1, 2048, 4095])
 
 
 def test_mxfp4_dsv3_decode_full():

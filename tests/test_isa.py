@@ -18,8 +18,11 @@ import pytest
 
 from routed_expert_grouped_amd import build
 
-SRCS = [os.path.join(build.CSRC, f) for f in ("moe_gemm.hip", "moe_gemm_a8.hip", "moe_ffn.hip")]
-KERNELS = ("gemm_fp8_q256_kernel", "gemm_a8_kernel")  # the kernels with direct-to-LDS loads
+SRCS = [os.path.join(build.CSRC, f)
+        for f in ("moe_gemm.hip", "moe_gemm_a8.hip", "moe_gemm_w4.hip", "moe_ffn.hip")]
+# the GEMMs with direct-to-LDS loads (and their instantiation counts: 2 phases x (grouped,
+# identity), x (FP8, MXFP4 weights) for the FP8-activation GEMM)
+KERNELS = {"gemm_fp8_q256_kernel": 4, "gemm_a8_kernel": 8, "gemm_w4_kernel": 4}
 
 pytestmark = pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not available")
 
@@ -56,9 +59,8 @@ def _code(lines):
 
 
 def test_kernels_present(isa):
-    for kernel, count in zip(KERNELS, (4, 8)):
+    for kernel, count in KERNELS.items():
         names = [n for n in isa if kernel in n]
-        # 2 phases x (grouped, identity), and for the FP8-activation GEMM x (FP8, MXFP4 weights)
         assert len(names) == count, names
 
 
@@ -70,7 +72,7 @@ def test_m0_only_in_inline_asm(isa):
         checked += 1
         bad = [t for t, inasm in _code(lines) if not inasm and re.search(r"\bm0\b", t)]
         assert not bad, (name, bad[:5])
-    assert checked >= 24
+    assert checked >= 28
 
 
 def test_no_other_vector_memory_between_direct_loads(isa):
@@ -88,7 +90,7 @@ def test_no_other_vector_memory_between_direct_loads(isa):
                   if _VMEM.match(t) and not t.startswith("global_load_lds")
                   and not re.match(r"(global|buffer|flat)_store", t)]
         assert not inside, (name, inside[:5])
-    assert checked == 12
+    assert checked == 16
 
 
 def _vmcnt(t):
@@ -122,44 +124,47 @@ def test_mxfp4_scale_loads_waited_for_before_their_lds_reads(isa):
     assert checked == 4
 
 
-def _a8_issue_model(K, w4, load_a):
-    """The FP8-activation GEMM's loads in issue order, and the wait of each stage, as its source
-    states them: weight slots of 128 K (FP8, 4 loads a wave) or 256 K (MXFP4, 4 + 1 scale load),
-    activation stages of 64 K (2 loads); prologue weight slots 0, 1 then activation stages 0, 1;
-    at stage q: wait, then weight slot q / sps + 2 (first stage of a slot), activation stage
-    q + 2.  Yields (loads issued so far, the stage's wait, the loads it needs)."""
-    sps, per_slot = (4, 5) if w4 else (2, 4)
+def _issue_model(K, sps, per_slot, per_stage, load_a):
+    """Loads of a two-ring direct-to-LDS GEMM in issue order, and each stage's wait, as its
+    source states them: weight slots of sps 64-K stages (per_slot loads a wave), activation stages
+    of 64 K (per_stage loads); prologue weight slots 0, 1 then activation stages 0, 1; at stage q:
+    wait, then weight slot q / sps + 2 (first stage of a slot), activation stage q + 2.  Yields
+    (loads issued so far, the stage's wait, the loads it needs)."""
     nq, nslots = K // 64, -(-K // (64 * sps))
-    seq = []
-    seq += [("B", 0)] * per_slot
+    seq = [("B", 0)] * per_slot
     if nslots > 1:
         seq += [("B", 1)] * per_slot
     if load_a:
-        seq += [("A", 0)] * 2 + [("A", 1)] * 2
+        seq += [("A", 0)] * per_stage + [("A", 1)] * per_stage
     for q in range(nq):
         hs, sl = q % sps, q // sps
         b1, b2, a1 = sl + 1 < nslots, sl + 2 < nslots, q + 1 < nq
-        if load_a:  # the kernel's wait immediates
+        if load_a:  # the kernels' wait immediates
             if hs == 1:
-                n = per_slot + 2 if b2 and a1 else per_slot if b2 else 2 if a1 else 0
+                n = (per_slot + per_stage if b2 and a1 else per_slot if b2
+                     else per_stage if a1 else 0)
             else:
-                n = 2 if a1 else 0
+                n = per_stage if a1 else 0
         else:
             n = 2 * per_slot if hs >= 1 and b1 and b2 else per_slot if b1 else 0
         yield list(seq), n, {("B", sl)} | ({("A", q)} if load_a else set())
         if hs == 0 and b2:
             seq += [("B", sl + 2)] * per_slot
         if load_a and q + 2 < nq:
-            seq += [("A", q + 2)] * 2
+            seq += [("A", q + 2)] * per_stage
 
 
-@pytest.mark.parametrize("w4", [False, True])
+@pytest.mark.parametrize("kernel,sps,per_slot,per_stage", [
+    ("FP8-activation GEMM, FP8 weights", 2, 4, 2),
+    ("FP8-activation GEMM, MXFP4 weights", 4, 5, 2),
+    ("4-bit GEMM, bf16 activations", 2, 3, 4),
+])
 @pytest.mark.parametrize("load_a", [False, True])
-def test_a8_gemm_waits_cover_exactly_the_needed_loads(w4, load_a):
+def test_gemm_waits_cover_exactly_the_needed_loads(kernel, sps, per_slot, per_stage, load_a):
     """Loads land in issue order, so vmcnt(n) leaves exactly the last n issued in flight: each
     stage's n must leave none of the loads it reads, and (for speed) no more than needed, at
     every K the kernel takes."""
     for K in range(128, 8192 + 1, 128):
-        for seq, n, need in _a8_issue_model(K, w4, load_a):
+        for seq, n, need in _issue_model(K, sps, per_slot, per_stage, load_a):
             newest = max(i for i, x in enumerate(seq) if x in need)
             assert n == len(seq) - 1 - newest, (K, n, len(seq) - 1 - newest)
