@@ -10,14 +10,16 @@ top-8, FP8 block-scaled weights).  The same line carries the 4096-token prefill 
 "prefill", the same layer in the opt-in FP8 activation mode under "prefill_a8" (its gate/up
 roofline against the FP8 MFMA peak), the decode layer with 4-bit MXFP4 expert weights under
 "decode_mxfp4", the prefill layer with MXFP4 expert weights under "prefill_mxfp4" (bf16
-activations) and "prefill_mxfp4_a8" (FP8 activations, W4A8), the roofline of the dominant kernel (the routed gate/up projection: its launch
+activations) and "prefill_mxfp4_a8" (FP8 activations, W4A8), with --ep-ranks G rank 0's share of the decode and
+prefill layers under expert parallelism over G ranks under "ep_rank_share" (collectives
+excluded), the roofline of the dominant kernel (the routed gate/up projection: its launch
 duration from HIP events around back-to-back launches on the main stream, plus the average of
 the per-step brackets inside the layer) and the CPU oracle timed on a bounded sample on the
 host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_decode] [--no-cpu]
                     [--prefill dsv3_prefill] [--a8 dsv3_prefill] [--mxfp4 dsv3_decode]
-                    [--mxfp4-prefill dsv3_prefill] [--w4a8 dsv3_prefill]
+                    [--mxfp4-prefill dsv3_prefill] [--w4a8 dsv3_prefill] [--ep-ranks 0]
 """
 from __future__ import annotations
 
@@ -197,6 +199,47 @@ def time_layer(layer, steps: int, warmup: int, act: str = "bf16"):
                 gate_up_ms_in_layer=sum(gu_ms) / len(gu_ms) if gu_ms else None, counts=counts)
 
 
+def run_rank_share(layer, G: int, rank: int, steps: int, warmup: int):
+    """One rank's share of the layer under expert parallelism over G ranks (route + permute of
+    all tokens, the rank's E/G routed experts on their assignments, the local partial reduction,
+    the shared expert on the rank's T/G token rows), timed per step with HIP events.  The
+    collectives that would join the ranks are not part of this single-GPU build."""
+    import torch
+
+    import routed_expert_grouped_amd as moe
+
+    T, H, I, E, k = layer.T, layer.H, layer.I, layer.E, layer.k
+    e0, e1, t0, t1 = rank * E // G, (rank + 1) * E // G, rank * T // G, (rank + 1) * T // G
+    R = moe.MoeRankShare(T, H, I, E, k, layer.experts, layer.shared, e0, e1, t0, t1,
+                         layer.score_fn, layer.renorm)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        R.forward(layer.scores, layer.x)
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record(stream)
+    for i in range(steps):
+        R.forward(layer.scores, layer.x)
+        marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    total_ms = marks[0].elapsed_time(marks[-1])
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    pick = lambda f: step_ms[min(steps - 1, int(round(f * (steps - 1))))]
+    counts = R.counts.cpu().numpy()[e0:e1]
+    touched = int((counts > 0).sum())
+    wd = layer.experts.wdtype
+    # the local experts' and the shared expert's weights, x and the partial output once, the
+    # router scores and the top-k ids and weights
+    nbytes = (touched + 1) * expert_bytes(H, I, wd) + 2 * T * H * 2 + T * E * 4 + T * k * 8
+    ms = total_ms / steps
+    return dict(ranks=G, rank=rank, experts=[e0, e1], shared_tokens=[t0, t1],
+                local_assignments=int(counts.sum()), touched_local_experts=touched,
+                ms_per_step=round(ms, 4),
+                step_ms={q: round(pick(f), 4) for q, f in (("median", 0.5), ("p10", 0.1), ("p90", 0.9))},
+                algorithmic_bytes=nbytes, hbm_frac=round(nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                tokens_per_s_at_G_ranks_without_collectives=round(T / (ms * 1e-3), 1))
+
+
 def cpu_baseline(layer, rows, n_threads: int):
     """The oracle on `rows` of the same layer, wall-clock on the host (inputs copied first)."""
     import numpy as np
@@ -293,6 +336,10 @@ def main(argv=None):
                     help="workload also run with MXFP4 weights and bf16 activations ('' to skip)")
     ap.add_argument("--w4a8", default="dsv3_prefill",
                     help="workload also run with MXFP4 weights and FP8 activations ('' to skip)")
+    ap.add_argument("--ep-ranks", type=int, default=0,
+                    help="also time rank 0's share of the decode and prefill layers under expert "
+                         "parallelism over this many ranks (off by default: its smaller launches "
+                         "of the same kernels would mix into a profile of the default run)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-threads", type=int, default=int(os.environ.get("OMP_NUM_THREADS", "0") or 0))
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -322,6 +369,9 @@ def main(argv=None):
         cpu = dict(value=round(len(rows) / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
                    sample=f"{len(rows)} tokens of the {a.workload} layer (all experts they select "
                           f"+ shared), {dt:.2f} s wall", cpu=cpu_model())
+    ep = {}
+    if a.ep_ranks:
+        ep[a.workload] = run_rank_share(layer, a.ep_ranks, 0, a.steps, a.warmup)
     del layer
     mx = None
     if a.mxfp4:
@@ -331,6 +381,9 @@ def main(argv=None):
     if a.prefill:
         torch.cuda.empty_cache()
         player, prefill = run_workload(a.prefill, max(3, a.steps // 2), max(1, a.warmup // 2))
+        if a.ep_ranks:
+            ep[a.prefill] = run_rank_share(player, a.ep_ranks, 0, max(3, a.steps // 2),
+                                           max(1, a.warmup // 2))
         if a.a8 == a.prefill:  # same layer, FP8 activations
             _, a8 = run_workload(a.a8, max(3, a.steps // 2), max(1, a.warmup // 2), act="fp8",
                                  layer=player)
@@ -380,6 +433,7 @@ def main(argv=None):
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in a8.items()},
         "decode_mxfp4": None if mx is None else {
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in mx.items()},
+        "ep_rank_share": ep or None,
         "prefill_mxfp4": None if mxp is None else {
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in mxp.items()},
         "prefill_mxfp4_a8": None if w4 is None else {

@@ -136,6 +136,10 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
  *   perm    : int32 [T*k] from moe_permute; NULL selects the identity grouping used for the
  *             shared expert (then k must be 1, offsets NULL, w->n_groups 1, and row p = token p).
  *   offsets : int32 [n_groups+1] from moe_permute (n_groups = E); NULL with perm == NULL.
+ *             One rank's share under expert parallelism [OSDI SmallEP section] passes the
+ *             slice offsets + e0 with w holding experts e0 .. e0 + n_groups - 1 (the same arrays
+ *             advanced by e0 experts): only grouped rows [offsets[e0], offsets[e0 + n_groups])
+ *             are computed, and the other rows of h are not written.
  *   h       : bf16 [T*k][I] out, in grouped order.
  * Rows of experts with no assignment cost nothing: their weights are not read.
  * Errors: INVALID_ARG for null pointers, T < 0, k < 1, inconsistent identity grouping, unknown
@@ -237,6 +241,20 @@ moe_status moe_expert_ffn_a8(const uint16_t* x, int32_t T, int32_t k, const int3
 moe_status moe_combine(const uint16_t* y, const int32_t* inv, const float* topk_w,
                        const uint16_t* shared_y, int32_t T, int32_t k, int32_t H, uint16_t* out,
                        void* stream);
+
+/* One rank's local weighted partial reduction under expert parallelism [OSDI SmallEP section:
+ * each rank reduces its local experts' outputs to a partial T x H before the partials are
+ * exchanged and summed]:
+ *     out[t][c] = bf16_rne( S[t][c] + sum_{j : e_begin <= ids[t][j] < e_end} w[t][j] * y[inv[t*k+j]][c] )
+ * accumulated in fp32 in that order (S first, then j ascending, skipping other experts); rows
+ * of y of skipped assignments are never read (the rank did not compute them).  A token none of
+ * whose experts is local gets S (0 without shared_y).
+ *   ids      : int32 [T][k] from moe_route; the other arguments as for moe_combine.
+ * Errors as for moe_combine, plus INVALID_ARG for a null ids or e_begin > e_end. */
+moe_status moe_combine_partial(const uint16_t* y, const int32_t* inv, const int32_t* ids,
+                               const float* topk_w, int32_t e_begin, int32_t e_end,
+                               const uint16_t* shared_y, int32_t T, int32_t k, int32_t H,
+                               uint16_t* out, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status s);

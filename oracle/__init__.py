@@ -62,7 +62,7 @@ def lib():
         L.oracle_moe_layer.restype = i32
         L.oracle_moe_layer.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32,
                                        ctypes.POINTER(_Weights), P, ctypes.POINTER(_Weights),
-                                       P, i32, P, P, P, P, P, P, i32, i32, P]
+                                       P, i32, P, P, P, P, P, P, i32, i32, P, i32, i32]
         L.oracle_float_to_e4m3fn.restype = ctypes.c_uint8
         L.oracle_float_to_e4m3fn.argtypes = [ctypes.c_float]
         L.oracle_act_scale_exp.restype = i32
@@ -176,7 +176,7 @@ def quantize_rows(x, K: int):
 
 
 def moe_layer(layer, rows=None, routed=None, expert_slot=None, with_shared=True, want_h=False,
-              want_y=False, n_threads: int = 0, act_fp8: bool = False):
+              want_y=False, n_threads: int = 0, act_fp8: bool = False, expert_range=None):
     """Oracle of the whole layer for token rows `rows` (default: all).
 
     `layer` is a synth.Layer (its tensors may live on any device; they are copied to host).
@@ -186,6 +186,8 @@ def moe_layer(layer, rows=None, routed=None, expert_slot=None, with_shared=True,
     expert, hS (its h) (uint16), y, S (float64).
     act_fp8: quantise the activations x and h to E4M3FN in 1x128 blocks first (the FP8 MFMA
     mode's arithmetic); h is reported before its quantisation.
+    expert_range=(e_begin, e_end): evaluate and sum only those routed experts (one rank's local
+    partial reduction under expert parallelism); the others' h and y are zeros.
     """
     keep = []
     scores = _np(layer.scores, np.float32)
@@ -210,7 +212,7 @@ def moe_layer(layer, rows=None, routed=None, expert_slot=None, with_shared=True,
         ctypes.byref(rw), _ptr(slot), ctypes.byref(sw) if sw is not None else None,
         _ptr(r), n, _ptr(res["ids"]), _ptr(res["w"]), _ptr(res["out"]), _ptr(res.get("h")),
         _ptr(res.get("y")), _ptr(res.get("S")), int(n_threads), int(bool(act_fp8)),
-        _ptr(res.get("hS")))
+        _ptr(res.get("hS")), *((0, E) if expert_range is None else map(int, expert_range)))
     if rc:
         raise ValueError("oracle_moe_layer: invalid arguments (row, k or expert slot)")
     return res

@@ -393,13 +393,16 @@ static void set_error(int* err) {
  * Outputs for row i (all optional except out):
  *   ids [i][k], w [i][k], out [i][H] bf16 bits, h [i][k][I] bf16 bits, y [i][k][H] double,
  *   S [i][H] double (shared expert output), hS [i][I] bf16 bits (the shared expert's h).
- * out = bf16( S + sum_j w_j * y_j ), accumulated in double in the order S, j = 0..k-1. */
+ * out = bf16( S + sum_j w_j * y_j ), accumulated in double in the order S, j = 0..k-1.
+ * Only experts e_begin <= e < e_end are evaluated and summed: one rank's local weighted partial
+ * reduction under expert parallelism (OSDI'26 article, SmallEP section); [0, E) is the layer.
+ * The h and y of the other assignments are reported as zeros. */
 int oracle_moe_layer(const float* scores, const uint16_t* x, int T, int H, int I, int E, int k,
                      int score_fn, int renorm, const oracle_weights* routed,
                      const int32_t* expert_slot, const oracle_weights* shared,
                      const int32_t* rows, int n_rows, int32_t* ids_out, float* w_out,
                      uint16_t* out, uint16_t* h_out, double* y_out, double* S_out,
-                     int n_threads, int act_fp8, uint16_t* hS_out) {
+                     int n_threads, int act_fp8, uint16_t* hS_out, int e_begin, int e_end) {
     if (routed->H != H || routed->I != I) return ORACLE_ERR;
     if (shared && (shared->H != H || shared->I != I)) return ORACLE_ERR;
     if (rows == NULL) n_rows = T;
@@ -433,6 +436,11 @@ int oracle_moe_layer(const float* scores, const uint16_t* x, int T, int H, int I
                 expert_on_token(shared, 0, xrow, hS_out ? hS_out + (size_t)i * I : NULL, S, xd, hd,
                                 act_fp8);
             for (int j = 0; j < k; ++j) {
+                if (id[j] < e_begin || id[j] >= e_end) {  /* not this share's expert */
+                    for (int c = 0; c < H; ++c) y[(size_t)j * H + c] = 0.0;
+                    if (h_out) memset(h_out + ((size_t)i * k + j) * I, 0, sizeof(uint16_t) * I);
+                    continue;
+                }
                 int slot = expert_slot ? expert_slot[id[j]] : id[j];
                 if (slot < 0 || slot >= routed->n) { set_error(&err); break; }
                 expert_on_token(routed, slot, xrow, hb, y + (size_t)j * H, xd, hd, act_fp8);
@@ -440,7 +448,8 @@ int oracle_moe_layer(const float* scores, const uint16_t* x, int T, int H, int I
             }
             for (int c = 0; c < H; ++c) {
                 double acc = S[c];
-                for (int j = 0; j < k; ++j) acc += (double)wt[j] * y[(size_t)j * H + c];
+                for (int j = 0; j < k; ++j)
+                    if (id[j] >= e_begin && id[j] < e_end) acc += (double)wt[j] * y[(size_t)j * H + c];
                 out[(size_t)i * H + c] = oracle_double_to_bf16(acc);
             }
             if (ids_out) memcpy(ids_out + (size_t)i * k, id, sizeof(int32_t) * k);

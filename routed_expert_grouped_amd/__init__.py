@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import types
 
 import torch
 
@@ -23,7 +24,7 @@ SCORE_FN = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
 EXPORTS = ("moe_route", "moe_permute", "moe_expert_gate_up", "moe_expert_down",
            "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine", "moe_quantize_act",
            "moe_expert_gate_up_a8", "moe_expert_down_a8", "moe_expert_ffn_a8_workspace_size",
-           "moe_expert_ffn_a8", "moe_status_string")
+           "moe_expert_ffn_a8", "moe_combine_partial", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -60,6 +61,7 @@ def lib():
         L.moe_expert_ffn_workspace_size.argtypes = [i32, i32, W, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_expert_ffn.argtypes = [P, i32, i32, P, P, W, P, P, ctypes.c_size_t, P]
         L.moe_combine.argtypes = [P, P, P, P, i32, i32, i32, P, P]
+        L.moe_combine_partial.argtypes = [P, P, P, P, i32, i32, P, i32, i32, i32, P, P]
         L.moe_quantize_act.argtypes = [P, i32, i32, P, P, i32, P]
         L.moe_expert_gate_up_a8.argtypes = [P, P, i32, i32, i32, P, P, W, P, P]
         L.moe_expert_down_a8.argtypes = [P, P, i32, i32, i32, P, W, P, P]
@@ -109,6 +111,16 @@ def expert_weights(ew) -> MoeExpertWeights:
                             ew.s_gate.data_ptr() if scaled else None,
                             ew.s_up.data_ptr() if scaled else None,
                             ew.s_down.data_ptr() if scaled else None)
+
+
+def expert_slice(ew, e_begin: int, e_end: int):
+    """Experts e_begin .. e_end - 1 of an object accepted by expert_weights(), as views of the
+    same arrays (no copy): the weights one rank holds under expert parallelism."""
+    return types.SimpleNamespace(
+        wdtype=ew.wdtype, gate=ew.gate[e_begin:e_end], up=ew.up[e_begin:e_end],
+        down=ew.down[e_begin:e_end],
+        **{n: (None if getattr(ew, n) is None else getattr(ew, n)[e_begin:e_end])
+           for n in ("s_gate", "s_up", "s_down")})
 
 
 def moe_route(scores, k: int, score_fn="sigmoid", renorm: int = 1, topk_ids=None, topk_w=None,
@@ -178,6 +190,16 @@ def moe_combine(y, inv, topk_w, shared_y, T: int, k: int, H: int, out=None, stre
         out = torch.empty((T, H), dtype=torch.int16, device=y.device)
     _check("moe_combine", lib().moe_combine(_p(y), _p(inv), _p(topk_w), _p(shared_y), T, k, H,
                                             _p(out), _s(stream)))
+    return out
+
+
+def moe_combine_partial(y, inv, topk_ids, topk_w, e_begin: int, e_end: int, shared_y, T: int,
+                        k: int, H: int, out=None, stream=None):
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.int16, device=y.device)
+    _check("moe_combine_partial",
+           lib().moe_combine_partial(_p(y), _p(inv), _p(topk_ids), _p(topk_w), int(e_begin),
+                                     int(e_end), _p(shared_y), T, k, H, _p(out), _s(stream)))
     return out
 
 
@@ -351,3 +373,62 @@ class MoeLayer:
             main.wait_stream(self.side)
         moe_combine(self.y, self.inv, self.topk_w, shared_y, T, k, self.H, self.out, stream)
         return self.out
+
+
+class MoeRankShare:
+    """One rank's share of the layer under expert parallelism over G ranks, as in the SmallEP
+    scheme of the OSDI'26 hybrid-inference article (SmallEP section): after the tokens are
+    all-gathered, every rank routes and groups all T tokens (redundantly), runs its local routed
+    experts [e_begin, e_end) on the assignments that select them, and reduces their weighted
+    outputs to a partial [T, H] (moe_combine_partial); the partials are then exchanged and
+    summed.  The shared expert runs on the rank's own token rows [t_begin, t_end).
+
+    `experts` holds all E experts' weights (only the local slice is ever read: expert_slice);
+    forward() returns (partial [T, H], shared output [t_end - t_begin, H]), bf16 bits.  The
+    collectives are not part of this single-GPU build.
+    """
+
+    def __init__(self, T, H, I, E, k, experts, shared, e_begin, e_end, t_begin, t_end,
+                 score_fn="sigmoid", renorm=1, device="cuda"):
+        if not (0 <= e_begin <= e_end <= E and 0 <= t_begin <= t_end <= T):
+            raise ValueError("expert or token range out of bounds")
+        self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
+        self.e0, self.e1, self.t0, self.t1 = e_begin, e_end, t_begin, t_end
+        self.score_fn, self.renorm = score_fn, renorm
+        local = expert_slice(experts, e_begin, e_end)
+        self.w = expert_weights(local) if e_end > e_begin else None
+        self.ws_ = expert_weights(shared) if shared is not None else None
+        self._keep = (experts, shared, local)
+        d, i32 = device, torch.int32
+        self.topk_ids = torch.empty((T, k), dtype=i32, device=d)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=d)
+        self.counts = torch.empty(E, dtype=i32, device=d)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=d)
+        self.perm = torch.empty(max(1, T * k), dtype=i32, device=d)
+        self.inv = torch.empty(max(1, T * k), dtype=i32, device=d)
+        self.h = torch.empty((max(1, T * k), I), dtype=torch.int16, device=d)
+        self.y = torch.empty((max(1, T * k), H), dtype=torch.int16, device=d)
+        self.out = torch.empty((max(1, T), H), dtype=torch.int16, device=d)
+        nt = max(1, t_end - t_begin)
+        self.sh_h = torch.empty((nt, I), dtype=torch.int16, device=d)
+        self.sh_y = torch.empty((nt, H), dtype=torch.int16, device=d)
+
+    def forward(self, scores, x, stream=None, gate_up_events=None):
+        T, k = self.T, self.k
+        moe_route(scores, k, self.score_fn, self.renorm, self.topk_ids, self.topk_w, stream)
+        moe_permute(self.topk_ids, self.E, self.counts, self.offsets, self.perm, self.inv, stream)
+        if self.w is not None:
+            offs = self.offsets[self.e0:]  # the local experts' slice of the grouping
+            if gate_up_events is not None:
+                gate_up_events[0].record(stream)
+            moe_expert_gate_up(x, k, self.perm, offs, self.w, self.h, stream)
+            if gate_up_events is not None:
+                gate_up_events[1].record(stream)
+            moe_expert_down(self.h, T, k, offs, self.w, self.y, stream)
+        moe_combine_partial(self.y, self.inv, self.topk_ids, self.topk_w, self.e0, self.e1, None,
+                            T, k, self.H, self.out, stream)
+        if self.ws_ is not None and self.t1 > self.t0:
+            xs = x[self.t0:self.t1]
+            moe_expert_gate_up(xs, 1, None, None, self.ws_, self.sh_h, stream)
+            moe_expert_down(self.sh_h, self.t1 - self.t0, 1, None, self.ws_, self.sh_y, stream)
+        return self.out, self.sh_y

@@ -134,6 +134,16 @@ def test_quantize_act_validation():
     assert moe.exp_pitch(7168) == 64 and moe.exp_pitch(2048) == 16 and moe.exp_pitch(640) == 16
 
 
+def test_combine_partial_validation():
+    L = moe.lib()
+    f = L.moe_combine_partial
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 2, None, 16, 2, 256, FAKE, None) == moe.MOE_ERR_INVALID_ARG  # e_begin > e_end
+    assert f(FAKE, FAKE, None, FAKE, 0, 8, None, 16, 2, 256, FAKE, None) == moe.MOE_ERR_INVALID_ARG  # null ids
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 8, None, 16, 0, 256, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 8, None, 16, 2, 250, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(None, None, None, None, 0, 8, None, 0, 2, 256, None, None) == moe.MOE_OK
+
+
 def test_a8_phase_validation():
     L = moe.lib()
     gu, dn = L.moe_expert_gate_up_a8, L.moe_expert_down_a8

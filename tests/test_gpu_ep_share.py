@@ -1,0 +1,75 @@
+"""GPU parity of one rank's share of the layer under expert parallelism, as in the SmallEP scheme
+of the OSDI'26 hybrid-inference article (SmallEP section): route and permute of all T tokens, the
+routed experts of the rank's range on the assignments that select them, the local weighted
+partial reduction (moe_combine_partial), and the shared expert on the rank's own token rows.
+Bars as for the layer: ids bit-exact, partial and shared outputs within 1e-2 relative L2 per row
+(tokens with no local expert: exactly zero)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routed_expert_grouped_amd as moe
+from gpu_util import assert_rows_close, layer_for, mid
+
+pytestmark = pytest.mark.gpu
+
+f = oracle.bf16_bits_to_float
+
+
+def _ranges(layer, G, r):
+    E, T = layer.E, layer.T
+    return r * E // G, (r + 1) * E // G, r * T // G, (r + 1) * T // G
+
+
+def _run(layer, G, r):
+    e0, e1, t0, t1 = _ranges(layer, G, r)
+    R = moe.MoeRankShare(layer.T, layer.H, layer.I, layer.E, layer.k, layer.experts, layer.shared,
+                         e0, e1, t0, t1, layer.score_fn, layer.renorm)
+    part, sh = R.forward(layer.scores, layer.x)
+    torch.cuda.synchronize()
+    return (R.topk_ids.cpu().numpy(), part.cpu().numpy().view(np.uint16),
+            sh[:t1 - t0].cpu().numpy().view(np.uint16))
+
+
+@pytest.mark.parametrize("cfg,G", [
+    ("tiny", 4),                                  # bf16 weights
+    (mid(), 4),                                   # decode kernel, ragged expert ranges
+    (mid(T=300, E=8, k=2), 8),                    # one expert per rank, GEMM shapes
+    (mid(T=200, E=24, k=4, wdtype="mxfp4"), 3),   # 4-bit weights
+])
+def test_rank_partials_and_their_sum(cfg, G):
+    layer = layer_for(cfg, seed=1)
+    total = np.zeros((layer.T, layer.H))
+    for r in range(G):
+        e0, e1, t0, t1 = _ranges(layer, G, r)
+        ids, part, sh = _run(layer, G, r)
+        ref = oracle.moe_layer(layer, with_shared=False, expert_range=(e0, e1))
+        np.testing.assert_array_equal(ids, ref["ids"])
+        assert_rows_close("partial", f(part), f(ref["out"]))
+        local = ((ref["ids"] >= e0) & (ref["ids"] < e1)).any(axis=1)
+        assert not part[~local].any()
+        refS = oracle.moe_layer(layer, rows=list(range(t0, t1)), want_y=True)["S"]
+        assert_rows_close("shared", f(sh), refS)
+        total += f(part)
+        total[t0:t1] += f(sh)
+    # every rank's partial plus its shared rows: the whole layer
+    assert_rows_close("sum of the shares", total, f(oracle.moe_layer(layer)["out"]))
+
+
+@pytest.mark.parametrize("cfg,rows", [("dsv3_decode", None), ("dsv3_prefill", [0, 1, 2048, 4095])])
+def test_rank_share_at_full_size(cfg, rows):
+    """Rank 0 of 8 (32 of the 256 experts) at the DeepSeek-V3 shapes; sampled tokens at
+    prefill (the oracle gets only the local experts those tokens select)."""
+    layer = layer_for(cfg)
+    e0, e1, _, _ = _ranges(layer, 8, 0)
+    ids, part, _ = _run(layer, 8, 0)
+    r = np.arange(layer.T) if rows is None else np.asarray(rows)
+    sel = ids[r]
+    used = sorted(set(sel[(sel >= e0) & (sel < e1)].tolist()))
+    slot = np.full(layer.E, -1, np.int32)
+    slot[used] = np.arange(len(used), dtype=np.int32)
+    ref = oracle.moe_layer(layer, rows=r, routed=layer.experts.select(used), expert_slot=slot,
+                           with_shared=False, expert_range=(e0, e1))
+    np.testing.assert_array_equal(sel, ref["ids"])
+    assert_rows_close("partial", f(part[r]), f(ref["out"]))

@@ -261,6 +261,43 @@ def test_ffn_dense_brute_force_tiny_fp8():
     _check_layer_against_dense(synth.make_layer("tiny_fp8", seed=0))
 
 
+@pytest.mark.parametrize("e_range", [(0, 4), (4, 9), (9, 16), (5, 5)])
+def test_partial_reduction_dense_brute_force(e_range):
+    """One rank's partial (experts [e0, e1) only, no shared expert) against the dense brute force
+    with the gate weights of the other experts set to zero; inside the range y equals the full
+    run's y bit for bit, outside it is zero."""
+    e0, e1 = e_range
+    layer = synth.make_layer("tiny_fp8", seed=0)
+    full = oracle.moe_layer(layer, want_y=True)
+    res = oracle.moe_layer(layer, with_shared=False, want_y=True, expert_range=e_range)
+    np.testing.assert_array_equal(res["ids"], full["ids"])
+    _, _, ys, _, _ = _dense_brute_force(layer, full["ids"], full["w"])
+    local = (res["ids"] >= e0) & (res["ids"] < e1)  # [T, k]
+    np.testing.assert_array_equal(res["y"][local], full["y"][local])
+    assert not res["y"][~local].any()
+    gate = np.zeros((layer.T, layer.E))
+    np.put_along_axis(gate, res["ids"], np.where(local, res["w"], 0).astype(np.float64), axis=1)
+    acc = np.einsum("te,teh->th", gate, ys)
+    out = oracle.bf16_bits_to_float(res["out"])
+    np.testing.assert_allclose(out, _to_bf16_f64(acc), rtol=2.0 ** -7, atol=1e-30)
+    assert not out[~local.any(axis=1)].any()  # tokens with no local expert: exactly zero
+
+
+def test_partial_reductions_partition_the_layer_at_k1():
+    """With one expert per token, each token's output comes from exactly one of the ranks'
+    expert ranges: that rank's partial equals the full output bit for bit, the others are 0."""
+    layer = synth.make_layer(dict(T=40, H=256, I=128, E=12, k=1, score_fn="softmax",
+                                  scores="normal", wdtype="fp8"), seed=2)
+    full = oracle.moe_layer(layer, with_shared=False)
+    bounds = [0, 3, 7, 12]
+    owner = np.searchsorted(bounds, full["ids"][:, 0], side="right") - 1
+    for r in range(3):
+        part = oracle.moe_layer(layer, with_shared=False, expert_range=(bounds[r], bounds[r + 1]))
+        mine = owner == r
+        np.testing.assert_array_equal(part["out"][mine], full["out"][mine])
+        assert not part["out"][~mine].any()
+
+
 def test_ffn_dense_brute_force_rectangular_scale_grid():
     # H != I so that a transposed scale index or weight layout cannot go unnoticed; random
     # per-block scales so that every block's scale matters.
