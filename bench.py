@@ -20,6 +20,7 @@ host.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_decode] [--no-cpu]
                     [--prefill dsv3_prefill] [--a8 dsv3_prefill] [--mxfp4 dsv3_decode]
                     [--mxfp4-prefill dsv3_prefill] [--w4a8 dsv3_prefill] [--ep-ranks 0]
+                    [--extra tiny,dsv3_long_zipf,kimi_k2]
 """
 from __future__ import annotations
 
@@ -336,6 +337,9 @@ def main(argv=None):
                     help="workload also run with MXFP4 weights and bf16 activations ('' to skip)")
     ap.add_argument("--w4a8", default="dsv3_prefill",
                     help="workload also run with MXFP4 weights and FP8 activations ('' to skip)")
+    ap.add_argument("--extra", default="",
+                    help="comma-separated further workloads to report under 'extra' (e.g. "
+                         "tiny,dsv3_long_zipf,kimi_k2; off by default)")
     ap.add_argument("--ep-ranks", type=int, default=0,
                     help="also time rank 0's share of the decode and prefill layers under expert "
                          "parallelism over this many ranks (off by default: its smaller launches "
@@ -404,6 +408,11 @@ def main(argv=None):
         torch.cuda.empty_cache()
         _, w4 = run_workload(a.w4a8, max(3, a.steps // 2), max(1, a.warmup // 2), act="fp8",
                              wdtype="mxfp4")
+    extra = {}
+    for name in [w for w in a.extra.split(",") if w]:
+        torch.cuda.empty_cache()
+        _, r = run_workload(name, max(3, a.steps // 2), max(1, a.warmup // 2))
+        extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
     line = {
         "metric": METRIC,
         "value": round(main_res["tokens_per_s"], 2),
@@ -434,6 +443,7 @@ def main(argv=None):
         "decode_mxfp4": None if mx is None else {
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in mx.items()},
         "ep_rank_share": ep or None,
+        "extra": extra or None,
         "prefill_mxfp4": None if mxp is None else {
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in mxp.items()},
         "prefill_mxfp4_a8": None if w4 is None else {
