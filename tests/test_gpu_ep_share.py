@@ -73,3 +73,27 @@ def test_rank_share_at_full_size(cfg, rows):
                            with_shared=False, expert_range=(e0, e1))
     np.testing.assert_array_equal(sel, ref["ids"])
     assert_rows_close("partial", f(part[r]), f(ref["out"]))
+
+
+def test_partial_combine_full_range_is_the_combine_and_ranges_add_up():
+    """moe_combine_partial over [0, E) with the shared output is moe_combine bit for bit (same
+    fp32 order); over two complementary ranges (the second with S) the two results sum, in
+    float64, to the combine up to the two bf16 roundings."""
+    rng = np.random.default_rng(4)
+    T, k, H, E = 50, 6, 512, 40
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    inv = rng.permutation(T * k).astype(np.int32)
+    y = torch.from_numpy(rng.standard_normal((T * k, H)).astype(np.float32)).to(torch.bfloat16)
+    S = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16)
+    dev = lambda a: (a if torch.is_tensor(a) else torch.from_numpy(a)).to("cuda")
+    y_d, S_d = dev(y.view(torch.int16)), dev(S.view(torch.int16))
+    ids_d, w_d, inv_d = dev(ids), dev(w), dev(inv)
+    full = moe.moe_combine(y_d, inv_d, w_d, S_d, T, k, H)
+    whole = moe.moe_combine_partial(y_d, inv_d, ids_d, w_d, 0, E, S_d, T, k, H)
+    lo = moe.moe_combine_partial(y_d, inv_d, ids_d, w_d, 0, 17, None, T, k, H)
+    hi = moe.moe_combine_partial(y_d, inv_d, ids_d, w_d, 17, E, S_d, T, k, H)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(whole.cpu().numpy(), full.cpu().numpy())
+    got = f(lo.cpu().numpy().view(np.uint16)) + f(hi.cpu().numpy().view(np.uint16))
+    assert_rows_close("two ranges", got, f(full.cpu().numpy().view(np.uint16)))
