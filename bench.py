@@ -93,12 +93,16 @@ def layer_flops(T, H, I, k, shared=True) -> int:
 def kernel_sources(kernel: str) -> list:
     """Sources (relative to the repository root) of the translation unit a libmoe gate/up kernel
     is compiled in, with the headers it includes: moe_ffn.hip (GEMV kernels and the launches),
-    moe_gemm.hip (bf16-activation GEMM), moe_gemm_a8.hip (FP8-activation GEMM) or
-    moe_gemm_w4.hip (MXFP4 weights, bf16 activations)."""
+    moe_gemm.hip (bf16-activation GEMM, with the launch choice of moe_gemm_wide.hip's 160 x 512
+    tiles), moe_gemm_a8.hip (FP8-activation GEMM) or moe_gemm_w4.hip (MXFP4 weights, bf16
+    activations)."""
     if "gemv_kernel" in kernel:
         names = ["moe_device.h", "moe_ffn.h", "moe_ffn.hip", "moe_host.h", "moe_lds.h"]
     elif "gemm_a8_kernel" in kernel:
         names = ["moe_device.h", "moe_ffn.h", "moe_gemm_a8.hip", "moe_host.h", "moe_lds.h"]
+    elif "gemm_fp8_wide_kernel" in kernel:
+        names = ["moe_device.h", "moe_ffn.h", "moe_ffn.hip", "moe_gemm.hip", "moe_gemm_wide.hip",
+                 "moe_host.h", "moe_lds.h"]
     elif "gemm_w4_kernel" in kernel:
         names = ["moe_device.h", "moe_ffn.h", "moe_gemm_w4.hip", "moe_host.h", "moe_lds.h"]
     else:

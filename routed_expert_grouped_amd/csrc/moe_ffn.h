@@ -54,6 +54,10 @@ constexpr int kA8MaxPitch = kA8MaxK / 128;
 bool a8_gemm_fits(int phase, const GemmArgs& a);
 moe_status launch_gemm_a8(int phase, const GemmArgs& a, hipStream_t st);
 
+// FP8 weights, bf16 activations: the 160 x 512 tile GEMM (moe_gemm_wide.hip)
+bool wide_gemm_fits(int phase, const GemmArgs& a);
+moe_status launch_gemm_wide(int phase, const GemmArgs& a, hipStream_t st);
+
 // MXFP4 weights with bf16 activations, many rows per expert: the 4-bit GEMM (moe_gemm_w4.hip)
 // for the shapes w4_gemm_fits accepts; the decode kernel runs the rest
 bool w4_gemm_fits(int phase, const GemmArgs& a);

@@ -71,6 +71,9 @@ def test_tiny_layer(cfg):
     dict(T=48, H=16384, I=256, E=4, k=2),    # the largest H (MOE_MAX_DIM), GEMV path
     dict(T=200, H=16384, I=256, E=4, k=2),   # the largest H, GEMM path (128 scale blocks)
     dict(T=150, H=256, I=16384, E=2, k=1),   # the largest I, GEMM path
+    dict(T=300, I=512, E=8, k=4),            # 160 x 512 tiles in both phases; experts above
+                                             # 160 rows take a second m-tile
+    dict(T=600, I=512, E=8, k=4),            # 300 rows per expert: 256 x 256 tiles
 ])
 def test_mid_layer(over):
     layer = layer_for(mid(**over), seed=1)
@@ -85,13 +88,14 @@ def test_skewed_routing_one_hot_expert():
     compare_with_oracle(layer, g)
 
 
-@pytest.mark.parametrize("I", [384, 512])
-def test_block_scales_zero_and_wide_range(I):
+@pytest.mark.parametrize("I,T,E", [(384, 200, 8), (512, 200, 8), (512, 400, 4)])
+def test_block_scales_zero_and_wide_range(I, T, E):
     """Weight blocks with zero scales and scales spread over six decades, on the grouped-GEMM
     path (many rows per expert) of the routed and the shared experts (I = 384: phase 2 has an
-    odd number of 128-long K blocks; I = 512: an even number).  A zero scale
-    makes its whole block contribute nothing."""
-    layer = synth.make_layer(mid(T=200, E=8, k=2, I=I), seed=5)
+    odd number of 128-long K blocks; I = 512: an even number; 50 rows per expert take the
+    160 x 512 tiles where the shape allows, 200 the 256 x 256 ones).  A zero scale makes its
+    whole block contribute nothing."""
+    layer = synth.make_layer(mid(T=T, E=E, k=2, I=I), seed=5)
     rng = np.random.default_rng(5)
     for ew in (layer.experts, layer.shared):
         for name in ("s_gate", "s_up", "s_down"):

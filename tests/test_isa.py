@@ -19,10 +19,12 @@ import pytest
 from routed_expert_grouped_amd import build
 
 SRCS = [os.path.join(build.CSRC, f)
-        for f in ("moe_gemm.hip", "moe_gemm_a8.hip", "moe_gemm_w4.hip", "moe_ffn.hip")]
+        for f in ("moe_gemm.hip", "moe_gemm_wide.hip", "moe_gemm_a8.hip", "moe_gemm_w4.hip",
+                  "moe_ffn.hip")]
 # the GEMMs with direct-to-LDS loads (and their instantiation counts: 2 phases x (grouped,
 # identity), x (FP8, MXFP4 weights) for the FP8-activation GEMM)
-KERNELS = {"gemm_fp8_q256_kernel": 4, "gemm_a8_kernel": 8, "gemm_w4_kernel": 4}
+KERNELS = {"gemm_fp8_q256_kernel": 4, "gemm_fp8_wide_kernel": 4, "gemm_a8_kernel": 8,
+           "gemm_w4_kernel": 4}
 
 pytestmark = pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not available")
 
@@ -72,7 +74,7 @@ def test_m0_only_in_inline_asm(isa):
         checked += 1
         bad = [t for t, inasm in _code(lines) if not inasm and re.search(r"\bm0\b", t)]
         assert not bad, (name, bad[:5])
-    assert checked >= 28
+    assert checked >= 32
 
 
 def test_no_other_vector_memory_between_direct_loads(isa):
@@ -90,7 +92,7 @@ def test_no_other_vector_memory_between_direct_loads(isa):
                   if _VMEM.match(t) and not t.startswith("global_load_lds")
                   and not re.match(r"(global|buffer|flat)_store", t)]
         assert not inside, (name, inside[:5])
-    assert checked == 16
+    assert checked == 20
 
 
 def _vmcnt(t):
