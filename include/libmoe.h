@@ -124,6 +124,17 @@ moe_status moe_route(const float* scores, int32_t T, int32_t E, int32_t k, int32
 moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
                        int32_t* offsets, int32_t* perm, int32_t* inv, void* stream);
 
+/* moe_route followed by moe_permute in one launch, for decode-sized batches (T*k <= 2048): the
+ * same outputs, bit for bit, as the two calls [A2 4.1 and OSDI DSLP "gating + sorting"]; one
+ * workgroup routes the tokens (a wave per token) and one of its waves then groups the
+ * assignments, which saves a launch and a dependent kernel boundary on the decode critical path.
+ * Arguments as for the two calls.  Errors as for the two calls, plus UNSUPPORTED for
+ * T*k > 2048. */
+moe_status moe_route_permute(const float* scores, int32_t T, int32_t E, int32_t k,
+                             int32_t score_fn, int32_t renorm, int32_t* topk_ids, float* topk_w,
+                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                             void* stream);
+
 /* Expert phase 1: gate and up projections with the activated product
  * [OSDI "CPU fine-grained parallelism" (gate and up feed act*mul before down), "native FP8
  * GEMV" (E4M3FN, 128-blocks, post-scaling); KT 2.2 (grouped GEMM)].

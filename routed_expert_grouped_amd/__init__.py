@@ -24,7 +24,7 @@ SCORE_FN = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
 EXPORTS = ("moe_route", "moe_permute", "moe_expert_gate_up", "moe_expert_down",
            "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine", "moe_quantize_act",
            "moe_expert_gate_up_a8", "moe_expert_down_a8", "moe_expert_ffn_a8_workspace_size",
-           "moe_expert_ffn_a8", "moe_combine_partial", "moe_status_string")
+           "moe_expert_ffn_a8", "moe_combine_partial", "moe_route_permute", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -56,6 +56,7 @@ def lib():
         W = ctypes.POINTER(MoeExpertWeights)
         L.moe_route.argtypes = [P, i32, i32, i32, i32, i32, P, P, P]
         L.moe_permute.argtypes = [P, i32, i32, i32, P, P, P, P, P]
+        L.moe_route_permute.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.moe_expert_gate_up.argtypes = [P, i32, i32, P, P, W, P, P]
         L.moe_expert_down.argtypes = [P, i32, i32, P, W, P, P]
         L.moe_expert_ffn_workspace_size.argtypes = [i32, i32, W, ctypes.POINTER(ctypes.c_size_t)]
@@ -134,6 +135,28 @@ def moe_route(scores, k: int, score_fn="sigmoid", renorm: int = 1, topk_ids=None
     _check("moe_route", lib().moe_route(_p(scores), T, E, k, fn, int(renorm), _p(topk_ids),
                                         _p(topk_w), _s(stream)))
     return topk_ids, topk_w
+
+
+FUSED_ROUTE_PERMUTE_MAX = 2048  # assignments up to which moe_route_permute runs
+
+
+def moe_route_permute(scores, k: int, score_fn="sigmoid", renorm: int = 1, topk_ids=None,
+                      topk_w=None, counts=None, offsets=None, perm=None, inv=None, stream=None):
+    """moe_route + moe_permute in one launch (T*k <= 2048); returns ids, w, counts, offsets,
+    perm, inv."""
+    T, E = scores.shape
+    dev, i32 = scores.device, torch.int32
+    topk_ids = torch.empty((T, k), dtype=i32, device=dev) if topk_ids is None else topk_ids
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    counts = torch.empty(E, dtype=i32, device=dev) if counts is None else counts
+    offsets = torch.empty(E + 1, dtype=i32, device=dev) if offsets is None else offsets
+    perm = torch.empty(max(1, T * k), dtype=i32, device=dev) if perm is None else perm
+    inv = torch.empty(max(1, T * k), dtype=i32, device=dev) if inv is None else inv
+    fn = SCORE_FN[score_fn] if isinstance(score_fn, str) else int(score_fn)
+    _check("moe_route_permute",
+           lib().moe_route_permute(_p(scores), T, E, k, fn, int(renorm), _p(topk_ids), _p(topk_w),
+                                   _p(counts), _p(offsets), _p(perm), _p(inv), _s(stream)))
+    return topk_ids, topk_w, counts, offsets, perm, inv
 
 
 def moe_permute(topk_ids, E: int, counts=None, offsets=None, perm=None, inv=None, stream=None):
@@ -265,8 +288,9 @@ def moe_expert_ffn_a8(x, k: int, perm, offsets, w: MoeExpertWeights, y=None, ws=
 
 
 class MoeLayer:
-    """Buffers and the call sequence of one MoE layer forward: route -> permute -> routed
-    gate/up -> routed down -> combine on the caller's stream, and the shared expert (which only
+    """Buffers and the call sequence of one MoE layer forward: route -> permute (one launch,
+    moe_route_permute, for T*k <= 2048) -> routed gate/up -> routed down -> combine on the
+    caller's stream, and the shared expert (which only
     needs x) on a second stream that runs alongside the routed experts and joins before combine.
 
     `experts` and `shared` are objects accepted by expert_weights(); `x` is bf16 bits [T, H]
@@ -337,6 +361,17 @@ class MoeLayer:
         self.graph.replay()
         return self.out
 
+    def _route_permute(self, scores, stream):
+        """Routing and grouping; one launch for decode-sized batches."""
+        k = self.k
+        if self.T * k <= FUSED_ROUTE_PERMUTE_MAX:
+            moe_route_permute(scores, k, self.score_fn, self.renorm, self.topk_ids, self.topk_w,
+                              self.counts, self.offsets, self.perm, self.inv, stream)
+        else:
+            moe_route(scores, k, self.score_fn, self.renorm, self.topk_ids, self.topk_w, stream)
+            moe_permute(self.topk_ids, self.E, self.counts, self.offsets, self.perm, self.inv,
+                        stream)
+
     def _shared(self, x, st):
         if self.act == "fp8":
             moe_expert_ffn_a8(x, 1, None, None, self.ws_, self.sh_y, self.sh_ws, st)
@@ -355,8 +390,7 @@ class MoeLayer:
             self.side.wait_stream(main)
             self._shared(x, self.side)
             shared_y = self.sh_y
-        moe_route(scores, k, self.score_fn, self.renorm, self.topk_ids, self.topk_w, stream)
-        moe_permute(self.topk_ids, self.E, self.counts, self.offsets, self.perm, self.inv, stream)
+        self._route_permute(scores, stream)
         if self.act == "fp8":
             moe_expert_ffn_a8(x, k, self.perm, self.offsets, self.w, self.y, self.ws, stream)
         else:
@@ -415,8 +449,13 @@ class MoeRankShare:
 
     def forward(self, scores, x, stream=None, gate_up_events=None):
         T, k = self.T, self.k
-        moe_route(scores, k, self.score_fn, self.renorm, self.topk_ids, self.topk_w, stream)
-        moe_permute(self.topk_ids, self.E, self.counts, self.offsets, self.perm, self.inv, stream)
+        if T * k <= FUSED_ROUTE_PERMUTE_MAX:
+            moe_route_permute(scores, k, self.score_fn, self.renorm, self.topk_ids, self.topk_w,
+                              self.counts, self.offsets, self.perm, self.inv, stream)
+        else:
+            moe_route(scores, k, self.score_fn, self.renorm, self.topk_ids, self.topk_w, stream)
+            moe_permute(self.topk_ids, self.E, self.counts, self.offsets, self.perm, self.inv,
+                        stream)
         if self.w is not None:
             offs = self.offsets[self.e0:]  # the local experts' slice of the grouping
             if gate_up_events is not None:

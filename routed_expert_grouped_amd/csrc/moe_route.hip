@@ -1,7 +1,9 @@
-// moe_route.hip -- top-k routing: one wave64 per token (the routine is in moe_route.h).
+// moe_route.hip -- top-k routing: one wave64 per token (the routine is in moe_route.h); and,
+// for decode-sized batches, routing and grouping in one launch (moe_permute.h's wave walk).
 #include "libmoe.h"
 #include "moe_device.h"
 #include "moe_host.h"
+#include "moe_permute.h"
 #include "moe_route.h"
 
 namespace moe {
@@ -15,6 +17,26 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ sc
     if (t >= T) return;  // whole waves leave together
     route_token<VPL>(scores + (size_t)t * E, E, k, score_fn, renorm, ids + (size_t)t * k,
                      wts + (size_t)t * k);
+}
+
+// Routing then grouping in one workgroup: its waves route the tokens (a wave per token), and
+// after the barrier, which makes the workgroup's global writes visible to all its waves, wave 0
+// groups the T*k assignments from the ids just written.
+constexpr int kFusedN = 2048;  // assignments up to which one workgroup routes and groups
+constexpr int kFusedWaves = 16;
+
+template <int VPL>
+__global__ __launch_bounds__(kFusedWaves * 64) void route_permute_kernel(
+    const float* __restrict__ scores, int T, int E, int k, int score_fn, int renorm, int nbits,
+    int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    __shared__ int cnt[MOE_MAX_EXPERTS];
+    const int wave = (int)(threadIdx.x >> 6);
+    for (int t = wave; t < T; t += kFusedWaves)
+        route_token<VPL>(scores + (size_t)t * E, E, k, score_fn, renorm, ids + (size_t)t * k,
+                         wts + (size_t)t * k);
+    __syncthreads();
+    if (wave == 0) permute_wave(ids, T * k, E, nbits, cnt, counts, offsets, perm, inv);
 }
 
 static moe_status check_route(const float* scores, int32_t T, int32_t E, int32_t k, int32_t score_fn,
@@ -42,6 +64,31 @@ static moe_status launch_route(const float* scores, int32_t T, int32_t E, int32_
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" moe_status moe_route_permute(const float* scores, int32_t T, int32_t E, int32_t k,
+                                        int32_t score_fn, int32_t renorm, int32_t* topk_ids,
+                                        float* topk_w, int32_t* counts, int32_t* offsets,
+                                        int32_t* perm, int32_t* inv, void* stream) {
+    moe_status s = check_route(scores, T, E, k, score_fn, topk_ids, topk_w);
+    if (s != MOE_OK) return s;
+    if (T > 0 && (!counts || !offsets || !perm || !inv)) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if ((int64_t)T * k > kFusedN) return MOE_ERR_UNSUPPORTED;
+    const int nbits = ceil_log2(E) > 0 ? ceil_log2(E) : 1;
+    const dim3 grid(1), block(kFusedWaves * 64);
+    hipStream_t st = as_stream(stream);
+    switch (route_vpl(E)) {
+#define MOE_FUSED(V)                                                                          \
+    case V:                                                                                   \
+        route_permute_kernel<V><<<grid, block, 0, st>>>(scores, T, E, k, score_fn, renorm,     \
+                                                        nbits, topk_ids, topk_w, counts,       \
+                                                        offsets, perm, inv);                   \
+        break;
+        MOE_FUSED(1) MOE_FUSED(2) MOE_FUSED(4) MOE_FUSED(8) MOE_FUSED(16)
+#undef MOE_FUSED
+    }
+    return launch_status();
+}
 
 extern "C" moe_status moe_route(const float* scores, int32_t T, int32_t E, int32_t k,
                                 int32_t score_fn, int32_t renorm, int32_t* topk_ids, float* topk_w,

@@ -134,6 +134,19 @@ def test_quantize_act_validation():
     assert moe.exp_pitch(7168) == 64 and moe.exp_pitch(2048) == 16 and moe.exp_pitch(640) == 16
 
 
+def test_route_permute_validation():
+    L = moe.lib()
+    f = L.moe_route_permute
+    args = lambda T, E, k, fn=1, c=FAKE: (FAKE, T, E, k, fn, 1, FAKE, FAKE, c, FAKE, FAKE, FAKE, None)
+    assert f(*args(16, 256, 0)) == moe.MOE_ERR_INVALID_ARG           # k < 1
+    assert f(*args(16, 8, 9)) == moe.MOE_ERR_INVALID_ARG             # k > E
+    assert f(*args(16, 256, 8, fn=7)) == moe.MOE_ERR_INVALID_ARG     # unknown score function
+    assert f(*args(16, 256, 8, c=None)) == moe.MOE_ERR_INVALID_ARG   # null grouping output
+    assert f(*args(257, 256, 8)) == moe.MOE_ERR_UNSUPPORTED          # T*k > 2048
+    assert f(*args(16, 2048, 8)) == moe.MOE_ERR_UNSUPPORTED          # E > MOE_MAX_EXPERTS
+    assert f(None, 0, 256, 8, 1, 1, None, None, None, None, None, None, None) == moe.MOE_OK
+
+
 def test_combine_partial_validation():
     L = moe.lib()
     f = L.moe_combine_partial

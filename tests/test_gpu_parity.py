@@ -146,6 +146,21 @@ def test_permute_large_and_skewed(T, E, k, skew):
         np.testing.assert_array_equal(got.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("T,E,k,fn", [(16, 256, 8, "sigmoid"), (1, 7, 7, "softmax"),
+                                      (33, 1024, 32, "softmax"), (256, 256, 8, "sigmoid"),
+                                      (100, 64, 6, "sigmoid")])
+def test_fused_route_permute_is_the_two_calls(T, E, k, fn):
+    """moe_route_permute (one launch, T*k <= 2048) gives the outputs of moe_route followed by
+    moe_permute bit for bit, up to the largest fused size (T*k = 2048)."""
+    scores = torch.rand((T, E), generator=torch.Generator().manual_seed(T * E + k)).to(DEV)
+    ids, w = moe.moe_route(scores, k, fn)
+    sep = (ids, w) + tuple(moe.moe_permute(ids, E))
+    fused = moe.moe_route_permute(scores, k, fn)
+    torch.cuda.synchronize()
+    for a, b in zip(sep, fused):
+        assert torch.equal(a, b)
+
+
 def test_permute_all_to_one_expert():
     ids = torch.full((5000, 1), 3, dtype=torch.int32)
     c, o, p, i = moe.moe_permute(ids.to(DEV), 8)
