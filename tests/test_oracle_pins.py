@@ -547,3 +547,13 @@ def test_ffn_dense_brute_force_mxfp4():
     _check_layer_against_dense(synth.make_layer(dict(T=24, H=256, I=128, E=6, k=2,
                                                      score_fn="sigmoid", scores="uniform",
                                                      wdtype="mxfp4"), seed=2))
+
+
+def test_ffn_mxfp4_fp8_activations_dense_brute_force():
+    """W4A8: MXFP4 weights (OCP E2M1 table, numpy scale expansion) with the FP8-quantised
+    activations of the dense brute force."""
+    layer = synth.make_layer(dict(T=24, H=384, I=256, E=6, k=3, score_fn="sigmoid",
+                                  scores="uniform", wdtype="mxfp4"), seed=6)
+    res = _check_layer_against_dense(layer, act_fp8=True)
+    plain = oracle.moe_layer(layer, act_fp8=False)
+    assert np.any(plain["out"] != res["out"])
