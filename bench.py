@@ -147,20 +147,31 @@ def time_layer(layer, steps: int, warmup: int, act: str = "bf16"):
     for _ in range(warmup):
         L.forward(layer.scores, layer.x)
     torch.cuda.synchronize()
-    # per-step brackets around the routed gate/up launch (the FP8 mode runs both phases in one
-    # call, so it has none)
+    # the timed region: exactly `steps` layer steps back to back, between one event pair, with
+    # nothing else on the stream (each timing event recorded between kernels costs GPU time)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(steps):
+        L.forward(layer.scores, layer.x)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    # a second, separate pass for the per-step distribution: an event at every step boundary and
+    # a bracket around the routed gate/up launch (the FP8 mode runs both phases in one call, so
+    # it has none)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)] if act == "bf16" else [None] * steps
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]  # step boundaries
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
     marks[0].record(stream)
     for i in range(steps):
         L.forward(layer.scores, layer.x, gate_up_events=ev[i])
         marks[i + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = marks[0].elapsed_time(marks[-1])
     step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
     gu_ms = [e[0].elapsed_time(e[1]) for e in ev if e is not None]
     # The same routed gate/up launch, `steps` times back to back on the same stream between one

@@ -33,12 +33,10 @@ struct GemmArgs {
 };
 
 // gemv shape: m-tiles of 16 rows; kGemvWaves waves per workgroup, each wave owning 16 h-columns
-// (phase 1: 16 gate + 16 up rows) or 32 y-columns (phase 2).
+// (phase 1: 16 gate + 16 up rows) or 32 y-columns (phase 2); FP8 gate/up splits each column
+// group's K over 2 or 4 waves (moe_ffn.hip).
 constexpr int kGemvBM = 16;
-#ifndef MOE_GEMV_WAVES
-#define MOE_GEMV_WAVES 4
-#endif
-constexpr int kGemvWaves = MOE_GEMV_WAVES;
+constexpr int kGemvWaves = 4;
 
 // Few rows per expert (decode): stream the weights with 16-row m-tiles; many rows (prefill):
 // 128-row LDS-staged GEMM tiles, which read each expert's weights once per 128 rows.

@@ -28,6 +28,13 @@ namespace moe {
 // rows of gate and of up; phase 2: 32 consecutive rows of down) over the full K, for one m-tile
 // of up to 16 grouped rows.  kGrouped = false is the identity grouping (shared expert).
 //
+// kSplit > 1 (FP8 gate/up): the workgroup's waves own kWaves / kSplit column groups, each over
+// kSplit consecutive parts of K; after the K loop the other parts' fp32 sums are added to part
+// 0's, in part order, through LDS.  A workgroup then streams 1/kSplit of the bytes, so the launch
+// has kSplit times more, shorter workgroups and its ramp-down at the end (the last workgroups
+// running on a few CUs) is that much shorter.  At the DeepSeek-V3 decode shape the unsplit
+// launch is 3168 workgroups for 1024 resident slots.
+//
 // HBM access: a wave's load instruction covers 8 weight rows x 128 contiguous bytes (whole
 // cache lines; 16 rows x 64 B per instruction, the MFMA operand layout, reaches only ~75% of the
 // bandwidth).  Each block goes through the wave's private LDS rows once to change from that
@@ -52,10 +59,12 @@ constexpr int kScaleWin = 64;    // 128-blocks of scales per window
 constexpr int kScaleSlot = 264;  // LDS bytes per scale load instruction (256 + 8: 8-byte reads
                                  // of 16 rows fall in distinct banks)
 
-template <int kFmt, int kPhase, bool kGrouped, int kWaves>
+template <int kFmt, int kPhase, bool kGrouped, int kWaves, int kSplit>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
+    static_assert(kWaves % kSplit == 0, "whole column groups per workgroup");
+    constexpr int kColWaves = kWaves / kSplit;        // waves per K part
     constexpr int kWaveCols = kPhase == 1 ? 16 : 32;  // output columns per wave
-    constexpr int kCols = kWaves * kWaveCols;
+    constexpr int kCols = kColWaves * kWaveCols;
     // a stage is kBPS 128-blocks, so that every format loads whole 128-byte lines per row
     constexpr int kBPS = kFmt == kMXFP4 ? 2 : 1;
     constexpr int kBB = kFmt == kFP8 ? 128 : kFmt == kMXFP4 ? 64 : 256;  // bytes of a row per block
@@ -74,6 +83,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
         return;
 
     const int lane = lane_id(), wave = uniform((int)(threadIdx.x >> 6));
+    const int cw = wave % kColWaves, kp = wave / kColWaves;  // column group, K part
     const int m = lane & 15, kq = lane >> 4;
     const int K = a.K;
     const int e = tile.group;
@@ -86,24 +96,26 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     // never stored, so the loads stay unconditional (exact load counters, no branches).
     const int pa = valid ? p : tile.row0;
     const int ra = (kPhase == 1 && kGrouped) ? a.perm[pa] / a.k : pa;
-    const uint16_t* arow = a.act + (size_t)ra * K;
+    // this wave's K part: 128-blocks [kb0w, kb0w + kblocks) of kb_all
+    const int kb_all = K / 128, kblocks = kb_all / kSplit, kb0w = kp * kblocks;
+    const uint16_t* arow = a.act + (size_t)ra * K + (size_t)kb0w * 128;
     // weight rows: load layout row lrow (+ kRPI per instruction), 16-byte chunk lchunk
-    const int n0 = tile.nt * kCols + wave * kWaveCols;
+    const int n0 = tile.nt * kCols + cw * kWaveCols;
     const size_t row_bytes = kFmt == kFP8 ? (size_t)K : kFmt == kMXFP4 ? (size_t)K / 2 : (size_t)K * 2;
-    const int kblocks = K / 128;
     const int nst = (kblocks + kBPS - 1) / kBPS;      // stages
     const int nb_last = kblocks - (nst - 1) * kBPS;   // blocks in the last stage
     const int lrow = lane / kLPR, lchunk = lane % kLPR;
-    const uint8_t* g0 = (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + lrow) * row_bytes + lchunk * 16;
+    const size_t kofs0 = (size_t)kb0w * kBB + lchunk * 16;  // the part's first byte of a row
+    const uint8_t* g0 = (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + lrow) * row_bytes + kofs0;
     const uint8_t* g1 = kPhase == 1
-        ? (const uint8_t*)a.w1 + ((size_t)e * a.N + n0 + lrow) * row_bytes + lchunk * 16
-        : (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + 16 + lrow) * row_bytes + lchunk * 16;
+        ? (const uint8_t*)a.w1 + ((size_t)e * a.N + n0 + lrow) * row_bytes + kofs0
+        : (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + 16 + lrow) * row_bytes + kofs0;
     const size_t ins_stride = (size_t)kRPI * row_bytes;  // bytes between a group's instructions
     const float* s0 = nullptr;
     const float* s1 = nullptr;
     if (kFmt == kFP8) {
-        s0 = a.s0 + ((size_t)e * (a.N / 128) + n0 / 128) * kblocks;
-        s1 = kPhase == 1 ? a.s1 + ((size_t)e * (a.N / 128) + n0 / 128) * kblocks : s0;
+        s0 = a.s0 + ((size_t)e * (a.N / 128) + n0 / 128) * kb_all + kb0w;
+        s1 = kPhase == 1 ? a.s1 + ((size_t)e * (a.N / 128) + n0 / 128) * kb_all + kb0w : s0;
     }
     // MXFP4: E8M0 bytes [N][K/32]; the wave's scale row r (0..31) is weight row n0 + r of w0
     // (r < 16) and of w1 (phase 1) or w0 (phase 2) (r >= 16).  A dword per block holds the
@@ -126,7 +138,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
                 const int r = (i << lgR) + rr;  // < 32
                 const uint8_t* row = r < 16 ? sb0 + ((size_t)e * a.N + n0 + r) * (K / 32)
                                             : sb1 + ((size_t)e * a.N + n0 + (kPhase == 1 ? r - 16 : r)) * (K / 32);
-                lds_dma4(row + 4 * (w0 + min(d, wdw - 1)), sl + i * kScaleSlot);
+                lds_dma4(row + 4 * (kb0w + w0 + min(d, wdw - 1)), sl + i * kScaleSlot);
             }
             auto off = [&](int r) { return (r >> lgR) * kScaleSlot + ((r & ((1 << lgR) - 1)) << (lgP + 2)); };
             soff0 = off(m);
@@ -255,6 +267,20 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     if (rest >= 2) compute(1, s + 1, rest == 2 ? nb_last : kBPS);
     if (rest == 3) compute(0, s + 2, nb_last);
 
+    if constexpr (kSplit > 1) {  // the sums of K parts 1.. join part 0's, in part order
+        __shared__ f32x4 red[kSplit - 1][kColWaves][2][kWave];
+        if (kp > 0) {
+            red[kp - 1][cw][0][lane] = acc0;
+            red[kp - 1][cw][1][lane] = acc1;
+        }
+        __syncthreads();
+        if (kp > 0) return;
+#pragma unroll
+        for (int q = 0; q < kSplit - 1; ++q) {
+            acc0 += red[q][cw][0][lane];
+            acc1 += red[q][cw][1][lane];
+        }
+    }
     // D layout of the 16x16 MFMA: lane holds rows 4*(lane/16)+r (grouped rows), column lane%16
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -284,14 +310,24 @@ static moe_status launch_phase(int phase, const GemmArgs& a, hipStream_t st) {
         if (w4_gemm_fits(phase, a)) return launch_gemm_w4(phase, a, st);
     }
     constexpr int W = kGemvWaves;
-    const int cols = W * (phase == 1 ? 16 : 32);
+    // FP8 gate/up: K split in 4 parts where the 128-blocks divide evenly, else 2, else none
+    // (measured at the DeepSeek-V3 decode shape: 0.425 ms unsplit, 0.411 ms in 4 parts; the down
+    // projection, 5544 workgroups of a quarter of the bytes, gained nothing; MXFP4 weights, whose
+    // per-wave scale copy does not shrink with the part, lost 28%)
+    const int kb = a.K / 128;
+    const int split = (phase != 1 || !a.fp8) ? 1 : kb % 4 == 0 ? 4 : kb % 2 == 0 ? 2 : 1;
+    const int cols = W / split * (phase == 1 ? 16 : 32);
     const int64_t wgs = (int64_t)max_mtiles(a.rows, a.offsets ? a.n_groups : 1, kGemvBM) * (a.N / cols);
     if (wgs > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((wgs + 7) & ~int64_t(7))), block(W * 64);
-#define MOE_GEMV(F, P, G) gemv_kernel<F, P, G, W><<<grid, block, 0, st>>>(a)
+#define MOE_GEMV(F, P, G) gemv_kernel<F, P, G, W, 1><<<grid, block, 0, st>>>(a)
+#define MOE_GEMV_SPLIT(G)                                                          \
+    (split == 4   ? gemv_kernel<kFP8, 1, G, W, 4><<<grid, block, 0, st>>>(a)        \
+     : split == 2 ? gemv_kernel<kFP8, 1, G, W, 2><<<grid, block, 0, st>>>(a)        \
+                  : gemv_kernel<kFP8, 1, G, W, 1><<<grid, block, 0, st>>>(a))
     const bool g = a.offsets != nullptr;
     if (phase == 1) {
-        if (a.fp8) g ? MOE_GEMV(kFP8, 1, true) : MOE_GEMV(kFP8, 1, false);
+        if (a.fp8) g ? MOE_GEMV_SPLIT(true) : MOE_GEMV_SPLIT(false);
         else if (a.fp4) g ? MOE_GEMV(kMXFP4, 1, true) : MOE_GEMV(kMXFP4, 1, false);
         else g ? MOE_GEMV(kBF16, 1, true) : MOE_GEMV(kBF16, 1, false);
     } else {
@@ -300,6 +336,7 @@ static moe_status launch_phase(int phase, const GemmArgs& a, hipStream_t st) {
         else g ? MOE_GEMV(kBF16, 2, true) : MOE_GEMV(kBF16, 2, false);
     }
 #undef MOE_GEMV
+#undef MOE_GEMV_SPLIT
     return launch_status();
 }
 

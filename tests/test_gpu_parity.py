@@ -69,6 +69,8 @@ def test_tiny_layer(cfg):
     dict(T=96, E=40, k=3, score_fn="softmax", renorm=0, wdtype="bf16"),
     dict(T=160, H=640, E=8, k=2),            # H an odd multiple of 128: register-staged GEMM
     dict(T=48, H=16384, I=256, E=4, k=2),    # the largest H (MOE_MAX_DIM), GEMV path
+    dict(T=24, H=640, E=16, k=2),            # GEMV gate/up with an odd count of 128-blocks:
+    dict(T=24, H=768, E=16, k=2),            # K unsplit, and K in two parts (four elsewhere)
     dict(T=200, H=16384, I=256, E=4, k=2),   # the largest H, GEMM path (128 scale blocks)
     dict(T=150, H=256, I=16384, E=2, k=1),   # the largest I, GEMM path
     dict(T=300, I=512, E=8, k=4),            # 160 x 512 tiles in both phases; experts above
