@@ -117,8 +117,10 @@ moe_status moe_route(const float* scores, int32_t T, int32_t E, int32_t k, int32
  *   perm     : int32 [T*k] out, perm[p] = flat index t*k+j of the p-th assignment in expert
  *              order; stable: within one expert the flat indices ascend (so do the tokens).
  *   inv      : int32 [T*k] out, inv[perm[p]] = p.
- * The result is unique and deterministic (no atomics decide an order).  Ids outside [0, E) are
- * a precondition violation: they are skipped and leave perm/inv entries unwritten.
+ * The result is unique and deterministic (no atomics decide an order).  Above 2048 assignments
+ * the call is four launches and uses inv as its scratch until the last one writes it.  Ids
+ * outside [0, E) are a precondition violation: they are skipped (not counted), and the perm
+ * entries past offsets[E] and the inv entries of the skipped assignments are unspecified.
  * Limits: E <= MOE_MAX_EXPERTS, T*k < 2^31.  Errors: INVALID_ARG for null pointers, T < 0,
  * k < 1, E < 1. */
 moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,

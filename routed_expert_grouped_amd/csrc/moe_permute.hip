@@ -4,17 +4,22 @@
 // them (KTransformers article, 2.2); in the expert-parallel flow this is the "sorting" after
 // gating (OSDI'26 hybrid-inference article, DSLP section).
 //
-// One workgroup of 16 waves does the whole job, so the order is decided without atomics:
-//   pass 1  each wave walks its contiguous run of 64-assignment chunks (the ids of 8 chunks
-//           are loaded together, so the loads overlap) and counts, per expert, its own
-//           assignments (peers with the same expert are found with one ballot per bit of the
-//           expert id; the lowest peer adds the group's size to the wave's LDS row);
-//   scan    per expert: exclusive sum over the waves (in wave order) and the total; then an
-//           exclusive sum of the totals over experts gives `offsets`;
-//   pass 2  each wave walks its chunks again in order; an assignment's slot is
-//           offsets[e] + (earlier waves' count of e) + (count of e in this wave's earlier
-//           chunks) + (lower peers in its chunk).
+// Above kSmallN assignments the work is spread over the chip in four launches, and still no
+// atomics decide an order:
+//   hist    block b (kBlockN consecutive assignments) counts its ids per expert in LDS and writes
+//           the counts to row b of a table [B][E];
+//   scan    one workgroup turns every expert's column into exclusive per-block bases (block
+//           order), writes `counts`, and `offsets` as the exclusive sum of the counts;
+//   place   block b walks its 64-assignment chunks in order, 16 waves each taking a contiguous
+//           run: pass 1 counts per wave and expert (peers with the same expert are found with one
+//           ballot per bit of the expert id), then per expert the waves' counts become running
+//           bases from offsets[e] + table[b][e]; pass 2 gives an assignment the slot
+//           base + (lower peers in its chunk), and perm[slot] = its flat index;
+//   invert  inv[perm[p]] = p.
 // The result is the stable order by construction (ascending flat index within each expert).
+// The table lives in `inv` until the last launch overwrites it.  With B = ceil(n / kBlockN)
+// blocks it holds B * E <= n / 2 + E ints (kBlockN >= 2 * E), which is at most n for every
+// n >= 2 * E, so for every n > kSmallN = 2048 >= 2 * MOE_MAX_EXPERTS.
 // Up to kSmallN assignments one wave does the same in order (moe_permute.h).
 #include "libmoe.h"
 #include "moe_device.h"
@@ -23,101 +28,140 @@
 
 namespace moe {
 
-constexpr int kPermWaves = 16;
-constexpr int kBatch = 8;  // 64-assignment chunks whose ids are loaded together
+constexpr int kPlaceWaves = 16;
+constexpr int kBlockChunks = 32;                 // 64-assignment chunks per block
+constexpr int kBlockN = kBlockChunks * kWave;    // 2048 assignments per block
+constexpr int kWaveChunks = kBlockChunks / kPlaceWaves;
+constexpr int kHistThreads = 256;
+static_assert(kBlockN >= 2 * MOE_MAX_EXPERTS, "the per-block count table fits in inv");
 
-__global__ __launch_bounds__(kPermWaves * kWave) void permute_kernel(
-    const int32_t* __restrict__ ids, int n, int E, int nbits, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
-    __shared__ int rowbase[kPermWaves * MOE_MAX_EXPERTS];  // [wave][expert]
-    __shared__ int start[MOE_MAX_EXPERTS];                  // offsets[e]
-    __shared__ int wsum[kPermWaves];
-    const int tid = (int)threadIdx.x, lane = lane_id(), wave = tid >> 6;
-
-    for (int i = tid; i < kPermWaves * E; i += kPermWaves * kWave) rowbase[i] = 0;
+__global__ __launch_bounds__(kHistThreads) void permute_hist_kernel(const int32_t* __restrict__ ids,
+                                                                    int n, int E,
+                                                                    int32_t* __restrict__ table) {
+    __shared__ int hist[MOE_MAX_EXPERTS];
+    const int tid = (int)threadIdx.x, b = (int)blockIdx.x;
+    for (int e = tid; e < E; e += kHistThreads) hist[e] = 0;
     __syncthreads();
-
-    const int chunks = (n + kWave - 1) / kWave;
-    const int c0 = (int)((int64_t)wave * chunks / kPermWaves);
-    const int c1 = (int)((int64_t)(wave + 1) * chunks / kPermWaves);
-    int* myrow = rowbase + wave * E;
-
-    // ids of kBatch chunks are loaded together (independent loads), then walked in order
-    auto load_batch = [&](int c, int (&ev)[kBatch]) {
+    const int f0 = b * kBlockN, f1 = min(n, f0 + kBlockN);
+    constexpr int kPer = kBlockN / kHistThreads;
+    int ev[kPer];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int f = (c + b) * kWave + lane;
-            ev[b] = (c + b < c1 && f < n) ? ids[f] : -1;
-        }
-    };
-
-    // pass 1: per-wave histogram
-    for (int c = c0; c < c1; c += kBatch) {
-        int ev[kBatch];
-        load_batch(c, ev);
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int e = ev[b];
-            const bool valid = e >= 0 && e < E;
-            const uint64_t peers = match_peers(e, valid, nbits);
-            if (valid && lane == __ffsll((unsigned long long)peers) - 1) myrow[e] += __popcll(peers);
-        }
+    for (int i = 0; i < kPer; ++i) {  // loads first, so they overlap
+        const int f = f0 + i * kHistThreads + tid;
+        ev[i] = f < f1 ? ids[f] : -1;
     }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if (ev[i] >= 0 && ev[i] < E) atomicAdd(&hist[ev[i]], 1);  // counts only: order-free
     __syncthreads();
+    for (int e = tid; e < E; e += kHistThreads) table[(size_t)b * E + e] = hist[e];
+}
 
-    // per-expert exclusive sum over waves; totals
+// One workgroup, one thread per expert (E <= 1024).
+__global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict__ table, int B, int E,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets) {
+    __shared__ int wsum[16];
+    const int tid = (int)threadIdx.x, lane = lane_id(), wave = tid >> 6;
     int total = 0;
     if (tid < E) {
-        for (int w = 0; w < kPermWaves; ++w) {
-            const int v = rowbase[w * E + tid];
-            rowbase[w * E + tid] = total;
+        int b = 0;
+        for (; b + 8 <= B; b += 8) {  // eight independent loads per trip
+            int v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = table[(size_t)(b + i) * E + tid];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                table[(size_t)(b + i) * E + tid] = total;
+                total += v[i];
+            }
+        }
+        for (; b < B; ++b) {
+            const int v = table[(size_t)b * E + tid];
+            table[(size_t)b * E + tid] = total;
             total += v;
         }
         counts[tid] = total;
     }
-    // exclusive sum of the totals over experts (E <= 1024 = one expert per thread)
     const int incl = wave_inclusive_scan(total);
     if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
     if (wave == 0) {
-        const int s = lane < kPermWaves ? wsum[lane] : 0;
+        const int s = lane < 16 ? wsum[lane] : 0;
         const int si = wave_inclusive_scan(s);
-        if (lane < kPermWaves) wsum[lane] = si - s;
+        if (lane < 16) wsum[lane] = si - s;
     }
     __syncthreads();
     if (tid < E) {
         const int excl = wsum[wave] + incl - total;
-        start[tid] = excl;
         offsets[tid] = excl;
         if (tid == E - 1) offsets[E] = excl + total;
     }
-    __syncthreads();
-    for (int i = tid; i < kPermWaves * E; i += kPermWaves * kWave) rowbase[i] += start[i % E];
-    __syncthreads();
+}
 
-    // pass 2: slots
-    for (int c = c0; c < c1; c += kBatch) {
-        int ev[kBatch];
-        load_batch(c, ev);
+__global__ __launch_bounds__(kPlaceWaves * kWave) void permute_place_kernel(
+    const int32_t* __restrict__ ids, int n, int E, int nbits, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ table, int32_t* __restrict__ perm) {
+    __shared__ int rowbase[kPlaceWaves * MOE_MAX_EXPERTS];  // [wave][expert]
+    const int tid = (int)threadIdx.x, lane = lane_id(), wave = tid >> 6, b = (int)blockIdx.x;
+    for (int i = tid; i < kPlaceWaves * E; i += kPlaceWaves * kWave) rowbase[i] = 0;
+    __syncthreads();
+    const int chunks = (n + kWave - 1) / kWave;
+    const int c0 = b * kBlockChunks + wave * kWaveChunks;
+    const int c1 = min(chunks, c0 + kWaveChunks);
+    int* myrow = rowbase + wave * E;
+    int ev[kWaveChunks];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int f = (c + b) * kWave + lane;
-            const int e = ev[b];
-            const bool valid = e >= 0 && e < E;
-            const uint64_t peers = match_peers(e, valid, nbits);
-            int base = 0;
-            if (valid) {
-                base = myrow[e];
-                const int pos = base + __popcll(peers & ((1ull << lane) - 1ull));
-                perm[pos] = f;
-                inv[f] = pos;
-            }
-            // the wave's reads of myrow above are issued before this write (in-order LDS per wave)
-            __builtin_amdgcn_wave_barrier();
-            if (valid && lane == __ffsll((unsigned long long)peers) - 1) myrow[e] = base + __popcll(peers);
-            __builtin_amdgcn_wave_barrier();
+    for (int i = 0; i < kWaveChunks; ++i) {
+        const int f = (c0 + i) * kWave + lane;
+        ev[i] = (c0 + i < c1 && f < n) ? ids[f] : -1;
+    }
+    // pass 1: this wave's count per expert
+#pragma unroll
+    for (int i = 0; i < kWaveChunks; ++i) {
+        const int e = ev[i];
+        const bool valid = e >= 0 && e < E;
+        const uint64_t peers = match_peers(e, valid, nbits);
+        if (valid && lane == __ffsll((unsigned long long)peers) - 1) myrow[e] += __popcll(peers);
+    }
+    __syncthreads();
+    // running bases per expert over the waves, from the block's base
+    for (int e = tid; e < E; e += kPlaceWaves * kWave) {
+        int base = offsets[e] + table[(size_t)b * E + e];
+        for (int w = 0; w < kPlaceWaves; ++w) {
+            const int v = rowbase[w * E + e];
+            rowbase[w * E + e] = base;
+            base += v;
         }
     }
+    __syncthreads();
+    // pass 2: slots
+#pragma unroll
+    for (int i = 0; i < kWaveChunks; ++i) {
+        const int f = (c0 + i) * kWave + lane;
+        const int e = ev[i];
+        const bool valid = e >= 0 && e < E;
+        const uint64_t peers = match_peers(e, valid, nbits);
+        int base = 0;
+        if (valid) {
+            base = myrow[e];
+            perm[base + __popcll(peers & ((1ull << lane) - 1ull))] = f;
+        }
+        // the wave's reads of myrow above are issued before this write (in-order LDS per wave)
+        __builtin_amdgcn_wave_barrier();
+        if (valid && lane == __ffsll((unsigned long long)peers) - 1) myrow[e] = base + __popcll(peers);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// inv[perm[p]] = p over the offsets[E] slots that were filled
+__global__ __launch_bounds__(256) void permute_invert_kernel(const int32_t* __restrict__ perm, int n,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int E, int32_t* __restrict__ inv) {
+    const int p = (int)(blockIdx.x * 256 + threadIdx.x);
+    if (p >= min(n, offsets[E])) return;
+    const int f = perm[p];
+    if (f >= 0 && f < n) inv[f] = p;
 }
 
 constexpr int kSmallN = 2048;  // assignments up to which one wave groups them
@@ -143,12 +187,19 @@ static moe_status launch_permute(const int32_t* topk_ids, int32_t T, int32_t k, 
                           int32_t* offsets, int32_t* perm, int32_t* inv, hipStream_t st) {
     const int n = T * k;
     const int nbits = ceil_log2(E) > 0 ? ceil_log2(E) : 1;
-    if (n <= kSmallN)
+    if (n <= kSmallN) {
         permute_small_kernel<<<dim3(1), dim3(kWave), 0, st>>>(topk_ids, n, E, nbits, counts, offsets,
                                                                perm, inv);
-    else
-        permute_kernel<<<dim3(1), dim3(kPermWaves * kWave), 0, st>>>(topk_ids, n, E, nbits, counts,
-                                                                     offsets, perm, inv);
+        return launch_status();
+    }
+    const int B = (int)(((int64_t)n + kBlockN - 1) / kBlockN);
+    int32_t* table = inv;  // [B][E], overwritten by the last launch
+    permute_hist_kernel<<<dim3(B), dim3(kHistThreads), 0, st>>>(topk_ids, n, E, table);
+    permute_scan_kernel<<<dim3(1), dim3(1024), 0, st>>>(table, B, E, counts, offsets);
+    permute_place_kernel<<<dim3(B), dim3(kPlaceWaves * kWave), 0, st>>>(topk_ids, n, E, nbits,
+                                                                       offsets, table, perm);
+    permute_invert_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(perm, n, offsets,
+                                                                                  E, inv);
     return launch_status();
 }
 
