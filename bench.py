@@ -20,7 +20,7 @@ host.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_decode] [--no-cpu]
                     [--prefill dsv3_prefill] [--a8 dsv3_prefill] [--mxfp4 dsv3_decode]
                     [--mxfp4-prefill dsv3_prefill] [--w4a8 dsv3_prefill] [--ep-ranks 0]
-                    [--extra tiny,dsv3_long_zipf,kimi_k2]
+                    [--extra tiny,dsv3_long_zipf,kimi_k2] [--vendor-ref]
 """
 from __future__ import annotations
 
@@ -256,6 +256,52 @@ def run_rank_share(layer, G: int, rank: int, steps: int, warmup: int):
                 tokens_per_s_at_G_ranks_without_collectives=round(T / (ms * 1e-3), 1))
 
 
+def vendor_reference(steps: int = 10):
+    """Reference rates of the vendor GEMM library (hipBLASLt through torch) at the expert shapes,
+    for context only: dense operands, no grouping or gather, and per-tensor instead of per-block
+    scales for FP8.  Nothing in the layer path uses them."""
+    import torch
+
+    dev, st = "cuda", torch.cuda.current_stream()
+
+    def tm(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(steps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    g = torch.Generator(device=dev).manual_seed(0)
+    out = {}
+    # one DeepSeek-V3 prefill gate/up at T = 4096 as 256 dense per-expert GEMMs of 128 rows
+    a = torch.randn((256, 128, 7168), device=dev, generator=g, dtype=torch.bfloat16)
+    b = torch.randn((256, 7168, 4096), device=dev, generator=g, dtype=torch.bfloat16).contiguous()
+    ms = tm(lambda: torch.bmm(a, b))
+    fl = 2 * 256 * 128 * 7168 * 4096
+    out["bf16_bmm_256x128x7168x4096"] = dict(ms=round(ms, 4), tflops=round(fl / ms / 1e9, 1),
+                                             bf16_frac=round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4))
+    del a, b
+    # one large dense GEMM: 32768 rows (the long prefill's assignments) x 7168 x 4096
+    a = torch.randn((32768, 7168), device=dev, generator=g, dtype=torch.bfloat16)
+    w = torch.randn((4096, 7168), device=dev, generator=g, dtype=torch.bfloat16)
+    fl = 2 * 32768 * 7168 * 4096
+    ms = tm(lambda: a @ w.t())
+    out["bf16_mm_32768x7168x4096"] = dict(ms=round(ms, 4), tflops=round(fl / ms / 1e9, 1),
+                                          bf16_frac=round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 4))
+    a8, w8 = a.to(torch.float8_e4m3fn), w.to(torch.float8_e4m3fn)
+    one = torch.ones((), device=dev)
+    ms = tm(lambda: torch._scaled_mm(a8, w8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16))
+    out["fp8_scaled_mm_per_tensor_32768x7168x4096"] = dict(
+        ms=round(ms, 4), tflops=round(fl / ms / 1e9, 1),
+        fp8_frac=round(fl / ms / 1e9 / FP8_PEAK_TFLOPS, 4))
+    return out
+
+
 def cpu_baseline(layer, rows, n_threads: int):
     """The oracle on `rows` of the same layer, wall-clock on the host (inputs copied first)."""
     import numpy as np
@@ -360,6 +406,9 @@ def main(argv=None):
                          "parallelism over this many ranks (off by default: its smaller launches "
                          "of the same kernels would mix into a profile of the default run)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--vendor-ref", action="store_true",
+                    help="also report the vendor GEMM library's rates at the expert shapes "
+                         "(context only; off by default)")
     ap.add_argument("--cpu-threads", type=int, default=int(os.environ.get("OMP_NUM_THREADS", "0") or 0))
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB 5 times (a known-size "
@@ -428,6 +477,10 @@ def main(argv=None):
         torch.cuda.empty_cache()
         _, r = run_workload(name, max(3, a.steps // 2), max(1, a.warmup // 2))
         extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+    vref = None
+    if a.vendor_ref:
+        torch.cuda.empty_cache()
+        vref = vendor_reference()
     line = {
         "metric": METRIC,
         "value": round(main_res["tokens_per_s"], 2),
@@ -463,6 +516,7 @@ def main(argv=None):
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in mxp.items()},
         "prefill_mxfp4_a8": None if w4 is None else {
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in w4.items()},
+        "vendor_reference": vref,
     }
     print(json.dumps(line))
     return 0
