@@ -20,7 +20,8 @@
 // The table lives in `inv` until the last launch overwrites it.  With B = ceil(n / kBlockN)
 // blocks it holds B * E <= n / 2 + E ints (kBlockN >= 2 * E), which is at most n for every
 // n >= 2 * E, so for every n > kSmallN = 2048 >= 2 * MOE_MAX_EXPERTS.
-// Up to kSmallN assignments one wave does the same in order (moe_permute.h).
+// Up to kBlockThreads (1024) assignments one workgroup places them all at once, one a thread,
+// and up to kSmallN one wave walks them in order (both in moe_permute.h).
 #include "libmoe.h"
 #include "moe_device.h"
 #include "moe_host.h"
@@ -166,6 +167,15 @@ __global__ __launch_bounds__(256) void permute_invert_kernel(const int32_t* __re
 
 constexpr int kSmallN = 2048;  // assignments up to which one wave groups them
 
+__global__ __launch_bounds__(kBlockThreads) void permute_block_kernel(
+    const int32_t* __restrict__ ids, int n, int E, int nbits, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    __shared__ int wcnt[kBlockWaves * MOE_MAX_EXPERTS];
+    __shared__ int off[MOE_MAX_EXPERTS + 1];
+    __shared__ int wsum[kBlockWaves];
+    permute_block(ids, n, E, nbits, wcnt, off, wsum, counts, offsets, perm, inv);
+}
+
 __global__ __launch_bounds__(kWave) void permute_small_kernel(
     const int32_t* __restrict__ ids, int n, int E, int nbits, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
@@ -187,6 +197,11 @@ static moe_status launch_permute(const int32_t* topk_ids, int32_t T, int32_t k, 
                           int32_t* offsets, int32_t* perm, int32_t* inv, hipStream_t st) {
     const int n = T * k;
     const int nbits = ceil_log2(E) > 0 ? ceil_log2(E) : 1;
+    if (n <= kBlockThreads) {
+        permute_block_kernel<<<dim3(1), dim3(kBlockThreads), 0, st>>>(topk_ids, n, E, nbits, counts,
+                                                                      offsets, perm, inv);
+        return launch_status();
+    }
     if (n <= kSmallN) {
         permute_small_kernel<<<dim3(1), dim3(kWave), 0, st>>>(topk_ids, n, E, nbits, counts, offsets,
                                                                perm, inv);

@@ -20,8 +20,10 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ sc
 }
 
 // Routing then grouping in one workgroup: its waves route the tokens (a wave per token), and
-// after the barrier, which makes the workgroup's global writes visible to all its waves, wave 0
-// groups the T*k assignments from the ids just written.
+// after the barrier the workgroup groups the T*k assignments: up to kBlockThreads of them all its
+// threads, one assignment each, from the ids the routing also left in LDS (permute_block); above
+// that wave 0 walks them in order from the ids just written (the barrier makes the workgroup's
+// global writes visible to all its waves).
 constexpr int kFusedN = 2048;  // assignments up to which one workgroup routes and groups
 constexpr int kFusedWaves = 16;
 
@@ -30,13 +32,22 @@ __global__ __launch_bounds__(kFusedWaves * 64) void route_permute_kernel(
     const float* __restrict__ scores, int T, int E, int k, int score_fn, int renorm, int nbits,
     int32_t* __restrict__ ids, float* __restrict__ wts, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
-    __shared__ int cnt[MOE_MAX_EXPERTS];
+    static_assert(kFusedWaves == kBlockWaves, "the grouping runs on the routing workgroup");
+    __shared__ int wcnt[kBlockWaves * MOE_MAX_EXPERTS];  // (one wave: its first E ints)
+    __shared__ int off[MOE_MAX_EXPERTS + 1];
+    __shared__ int wsum[kBlockWaves];
+    __shared__ int sids[kBlockThreads];
     const int wave = (int)(threadIdx.x >> 6);
+    const int n = T * k;
+    const bool block = n <= kBlockThreads;
     for (int t = wave; t < T; t += kFusedWaves)
         route_token<VPL>(scores + (size_t)t * E, E, k, score_fn, renorm, ids + (size_t)t * k,
-                         wts + (size_t)t * k);
+                         wts + (size_t)t * k, block ? sids + t * k : nullptr);
     __syncthreads();
-    if (wave == 0) permute_wave(ids, T * k, E, nbits, cnt, counts, offsets, perm, inv);
+    if (block)
+        permute_block(sids, n, E, nbits, wcnt, off, wsum, counts, offsets, perm, inv);
+    else if (wave == 0)
+        permute_wave(ids, n, E, nbits, wcnt, counts, offsets, perm, inv);
 }
 
 static moe_status check_route(const float* scores, int32_t T, int32_t E, int32_t k, int32_t score_fn,

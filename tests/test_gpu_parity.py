@@ -138,7 +138,11 @@ def test_route_ties_and_limits(T, E, k, fn):
 
 @pytest.mark.parametrize("T,E,k,skew", [(32768, 256, 8, 0.0), (20000, 256, 8, 2.0),
                                         (3000, 1024, 4, 0.0), (1, 7, 7, 0.0), (999, 3, 1, 0.0),
-                                        (256, 256, 8, 1.0), (2049, 64, 1, 0.0)])
+                                        (256, 256, 8, 1.0), (2049, 64, 1, 0.0),
+                                        # the smallest multi-block sizes at the most experts:
+                                        # the per-block count table (B * E ints) just fits in inv
+                                        (2049, 1024, 1, 0.0), (257, 1024, 8, 3.0),
+                                        (4097, 1024, 1, 0.0)])
 def test_permute_large_and_skewed(T, E, k, skew):
     ids = synth.random_topk_ids(T, E, k, seed=11, skew=skew)
     c, o, p, i = moe.moe_permute(ids.to(DEV), E)
