@@ -199,7 +199,7 @@ moe_status moe_expert_ffn(const uint16_t* x, int32_t T, int32_t k, const int32_t
  *               K/128 bytes of each row (the rest of the row is not written).
  *   exp_pitch : bytes per exps row, >= K/128; a multiple of 16 for moe_expert_*_a8.
  * Errors: INVALID_ARG for rows < 0, K < 1, exp_pitch < K/128, null or unaligned pointers;
- * UNSUPPORTED when K is not a multiple of 128 or rows * K/128 >= 2^31.  rows == 0 enqueues
+ * UNSUPPORTED when K is not a multiple of 128 or rows * K/128 > 2^27.  rows == 0 enqueues
  * nothing. */
 moe_status moe_quantize_act(const uint16_t* x, int32_t rows, int32_t K, uint8_t* codes,
                             int8_t* exps, int32_t exp_pitch, void* stream);
@@ -237,7 +237,7 @@ moe_status moe_expert_ffn_a8_workspace_size(int32_t T, int32_t k, const moe_expe
  * exactly to bf16 first (same values up to the order of fp32 sums).  The workspace begins with
  * h (bf16 [T*k][I], before its quantisation); the rest holds the quantised activations.  FP8
  * (MOE_W_FP8_E4M3_B128) and MXFP4 (MOE_W_MXFP4_G32) weights are accepted; bf16 weights are
- * UNSUPPORTED. */
+ * UNSUPPORTED, and so are T*H/128 or T*k*I/128 above 2^27 (the quantiser's limit). */
 moe_status moe_expert_ffn_a8(const uint16_t* x, int32_t T, int32_t k, const int32_t* perm,
                              const int32_t* offsets, const moe_expert_weights* w, uint16_t* y,
                              void* ws, size_t ws_bytes, void* stream);

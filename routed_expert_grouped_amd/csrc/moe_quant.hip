@@ -23,40 +23,74 @@ __device__ __forceinline__ int act_scale_exp(float amax) {
     return min(127, max(-127, e));
 }
 
-// One wave per (row, 128-block): lane l holds values 2l and 2l+1.  Writes any of: the codes, the
-// exponent (exps[r * exp_pitch + b]) and the dequantised values as bf16 (exact: a 4-bit
-// significand times a power of two).
-__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int rows,
-                                                       int K, uint8_t* __restrict__ codes,
-                                                       int8_t* __restrict__ exps, int exp_pitch,
-                                                       uint16_t* __restrict__ deq) {
-    const uint32_t nb = (uint32_t)K / 128;  // the launch keeps rows * nb below 2^31
-    const uint32_t blk = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (blk >= (uint32_t)rows * nb) return;  // whole waves leave together
-    const int lane = lane_id();
+// One row of 16 lanes per (row, 128-block), four blocks a wave: lane l of the row holds values
+// 8l .. 8l + 7 (one 16-byte load), the block maximum is taken over the row with DPP row
+// operations (no cross-row traffic), and every lane converts its own eight values.  Writes any
+// of: the codes, the exponent (exps[r * exp_pitch + b], by the row's first lane) and the
+// dequantised values as bf16 (exact: a 4-bit significand times a power of two).
+constexpr int kQuantThreads = 256;
+constexpr int64_t kQuantMaxBlocks = int64_t(1) << 27;  // 16 lanes a block: 32-bit thread ids
+
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    return v;
+}
+
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const uint16_t* __restrict__ x,
+                                                                 int rows, int K,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 int8_t* __restrict__ exps,
+                                                                 int exp_pitch,
+                                                                 uint16_t* __restrict__ deq) {
+    const uint32_t nb = (uint32_t)K / 128;  // the launch keeps rows * nb * 16 below 2^32
+    const uint32_t blk = (blockIdx.x * kQuantThreads + threadIdx.x) >> 4;
+    if (blk >= (uint32_t)rows * nb) return;  // whole rows of 16 lanes leave together
+    const int sub = (int)(threadIdx.x & 15);
     const uint32_t r = blk / nb, b = blk - r * nb;
-    const size_t at = (size_t)r * K + (size_t)b * 128 + 2 * lane;
-    const uint32_t pair = *(const uint32_t*)(x + at);
-    const float v0 = bf16_to_f32((uint16_t)pair), v1 = bf16_to_f32((uint16_t)(pair >> 16));
-    float amax = fmaxf(fabsf(v0), fabsf(v1));
+    const size_t at = (size_t)r * K + (size_t)b * 128 + 8 * sub;
+    const u32x4 raw = *(const u32x4*)(x + at);
+    float v[8];
 #pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_to_f32((uint16_t)raw[i]);
+        v[2 * i + 1] = bf16_to_f32((uint16_t)(raw[i] >> 16));
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    // non-negative floats order as their bit patterns
+    amax = __uint_as_float(row16_max_u32(__float_as_uint(amax)));
     const int e = act_scale_exp(amax);
-    const int c2 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v0, -e), ldexpf(v1, -e), 0, false);
-    if (codes) *(uint16_t*)(codes + at) = (uint16_t)c2;
-    if (exps && lane == 0) exps[(size_t)r * exp_pitch + b] = (int8_t)e;
+    uint32_t c[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * w], -e), ldexpf(v[4 * w + 1], -e), 0, false);
+        c[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * w + 2], -e), ldexpf(v[4 * w + 3], -e), lo, true);
+    }
+    if (codes) *(uint2*)(codes + at) = make_uint2(c[0], c[1]);
+    if (exps && sub == 0) exps[(size_t)r * exp_pitch + b] = (int8_t)e;
     if (deq) {
-        const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c2, ldexpf(1.0f, e), false);
-        *(bf16x2*)(deq + at) = d;
+        const float sc = ldexpf(1.0f, e);
+        bf16x2 d[4];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            d[2 * w] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[w], sc, false);
+            d[2 * w + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[w], sc, true);
+        }
+        *(u32x4*)(deq + at) = __builtin_bit_cast(u32x4, d);
     }
 }
 
 moe_status launch_quantize(const uint16_t* x, int64_t rows, int K, uint8_t* codes, int8_t* exps,
                            int exp_pitch, uint16_t* deq, hipStream_t st) {
     const int64_t blocks = rows * (K / 128);
-    if (blocks > INT32_MAX) return MOE_ERR_UNSUPPORTED;
-    quantize_kernel<<<dim3((unsigned)((blocks + 3) / 4)), dim3(256), 0, st>>>(
-        x, (int)rows, K, codes, exps, exp_pitch, deq);
+    if (blocks > kQuantMaxBlocks) return MOE_ERR_UNSUPPORTED;
+    const int64_t threads = blocks * 16;
+    quantize_kernel<<<dim3((unsigned)((threads + kQuantThreads - 1) / kQuantThreads)),
+                      dim3(kQuantThreads), 0, st>>>(x, (int)rows, K, codes, exps, exp_pitch, deq);
     return launch_status();
 }
 
@@ -120,7 +154,7 @@ extern "C" moe_status moe_quantize_act(const uint16_t* x, int32_t rows, int32_t 
     if (K % 128 != 0) return MOE_ERR_UNSUPPORTED;
     if (exp_pitch < K / 128) return MOE_ERR_INVALID_ARG;
     if (rows == 0) return MOE_OK;
-    if ((int64_t)rows * (K / 128) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)rows * (K / 128) > kQuantMaxBlocks) return MOE_ERR_UNSUPPORTED;
     if (!x || !codes || !exps || !aligned16(x) || !aligned16(codes) || !aligned16(exps))
         return MOE_ERR_INVALID_ARG;
     return launch_quantize(x, rows, K, codes, exps, exp_pitch, nullptr, as_stream(stream));
