@@ -256,6 +256,52 @@ def run_rank_share(layer, G: int, rank: int, steps: int, warmup: int):
                 tokens_per_s_at_G_ranks_without_collectives=round(T / (ms * 1e-3), 1))
 
 
+def read_probe(gib: int = 4, steps: int = 10):
+    """Read rate of plain HBM read kernels (libmoe_probe.so: 16-byte loads, nothing written) over a
+    `gib` GiB buffer: grid-stride, one contiguous chunk per workgroup, or rows of 7168 bytes read
+    in 128-byte columns across 8 rows per instruction (the decode weight stream's shape); the best
+    of the patterns and a few grid sizes is the measured ceiling the decode kernels' achieved
+    bandwidth is also set against."""
+    import ctypes
+
+    import torch
+
+    from routed_expert_grouped_amd import build as b
+
+    if not os.path.exists(b.PROBE_OUT):
+        return None
+    lib = ctypes.CDLL(b.PROBE_OUT)
+    lib.moe_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_void_p]
+    lib.moe_probe_read.restype = ctypes.c_int
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    best = None
+    for pattern, wgs in [(pt, w) for pt in (0, 1, 2) for w in (2048, 4096, 8192, 16384)]:
+        call = lambda: lib.moe_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                          ctypes.c_void_p(out.data_ptr()), wgs, pattern,
+                                          ctypes.c_void_p(st.cuda_stream))
+        if call() != 0:
+            return None
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(steps):
+            call()
+        e1.record(st)
+        torch.cuda.synchronize()
+        read = nbytes if pattern < 2 else (nbytes // 7168 // 32) * 32 * 7168  # whole row groups
+        gbs = read / (e0.elapsed_time(e1) / steps * 1e-3) / 1e9
+        if best is None or gbs > best["GBps"]:
+            best = dict(GBps=round(gbs, 1), bytes=read, workgroups=wgs,
+                        pattern=("strided", "blocked", "rows of 7168 bytes")[pattern])
+    del buf
+    return best
+
+
 def vendor_reference(steps: int = 10):
     """Reference rates of the vendor GEMM library (hipBLASLt through torch) at the expert shapes,
     for context only: dense operands, no grouping or gather, and per-tensor instead of per-block
@@ -429,7 +475,11 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    probe = read_probe()
     layer, main_res = run_workload(a.workload, a.steps, a.warmup)
+    if probe and main_res["roofline"]["unit"] == "GB/s":
+        main_res["roofline"].update(read_probe_GBps=probe["GBps"], frac_of_read_probe=round(
+            main_res["roofline"]["achieved"] / probe["GBps"], 4))
     cpu = None
     if not a.no_cpu:
         rows = list(range(layer.T))  # the decode layer has 16 tokens: the sample is all of them
@@ -517,6 +567,7 @@ def main(argv=None):
         "prefill_mxfp4_a8": None if w4 is None else {
             k: (round(v, 4) if isinstance(v, float) else v) for k, v in w4.items()},
         "vendor_reference": vref,
+        "hbm_read_probe": probe,
     }
     print(json.dumps(line))
     return 0

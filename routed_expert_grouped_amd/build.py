@@ -34,8 +34,27 @@ def _compile(src: str) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "read_probe.hip")
+PROBE_OUT = os.path.join(PKG, "libmoe_probe.so")
+
+
+def build_probe() -> str:
+    """The plain HBM read kernel the benchmark measures its ceiling with (libmoe_probe.so; not
+    part of libmoe)."""
+    tmp = PROBE_OUT + f".tmp{os.getpid()}"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_OUT)
+    return PROBE_OUT
+
+
 def build(jobs: int = 8) -> str:
-    """Compile every csrc/*.hip for gfx950 and link libmoe.so next to this file."""
+    """Compile every csrc/*.hip for gfx950 and link libmoe.so next to this file (and the
+    benchmark's read probe, libmoe_probe.so)."""
+    build_probe()
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, sources()))
