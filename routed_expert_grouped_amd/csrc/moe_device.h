@@ -86,6 +86,16 @@ __device__ __forceinline__ uint64_t match_peers(int key, bool valid, int nbits) 
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Maximum of v over each row of 16 lanes (every lane of the row gets it), by DPP:
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.  No LDS traffic.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    return v;
+}
+
 // ------------------------------------------------------------------ grouped tile schedule
 //
 // Rows are grouped by expert: group g owns rows [offsets[g], offsets[g+1]).  Each group is cut

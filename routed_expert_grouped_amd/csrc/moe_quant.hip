@@ -31,14 +31,6 @@ __device__ __forceinline__ int act_scale_exp(float amax) {
 constexpr int kQuantThreads = 256;
 constexpr int64_t kQuantMaxBlocks = int64_t(1) << 27;  // 16 lanes a block: 32-bit thread ids
 
-__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
-    return v;
-}
-
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const uint16_t* __restrict__ x,
                                                                  int rows, int K,
                                                                  uint8_t* __restrict__ codes,

@@ -27,13 +27,10 @@ __device__ __forceinline__ uint32_t score_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Maximum of v over the 64 lanes (wave-uniform result): within each row of 16 lanes by DPP
-// (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror), then over the four rows.
+// Maximum of v over the 64 lanes (wave-uniform result): within each row of 16 lanes by DPP,
+// then over the four rows.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    v = row16_max_u32(v);
     const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
     const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
     const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
@@ -42,8 +39,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 // Sum of x over the 64 lanes (wave-uniform result), in a fixed order: within each row of 16
-// lanes by the same DPP steps as wave_max_u32 (on both halves of the double), then the four row
-// sums in row order.
+// lanes by the DPP steps of row16_max_u32 (on both halves of the double), then the four row sums
+// in row order.
 template <int kCtrl>
 __device__ __forceinline__ double dpp_f64(double x) {
     const uint64_t u = (uint64_t)__double_as_longlong(x);
