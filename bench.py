@@ -108,8 +108,9 @@ def kernel_sources(kernel: str) -> list:
     else:
         names = ["moe_device.h", "moe_ffn.h", "moe_ffn.hip", "moe_gemm.hip", "moe_host.h",
                  "moe_lds.h"]
+    # build.py holds the compile flags (some per file), so it is part of what the kernel is
     return sorted(os.path.join("routed_expert_grouped_amd", "csrc", n) for n in names) + \
-        [os.path.join("include", "libmoe.h")]
+        [os.path.join("include", "libmoe.h"), os.path.join("routed_expert_grouped_amd", "build.py")]
 
 
 def source_digest(files) -> str:

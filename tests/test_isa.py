@@ -36,8 +36,8 @@ def isa(tmp_path_factory):
     funcs = {}
     for src in SRCS:
         out = tmp_path_factory.mktemp("isa") / (os.path.basename(src) + ".s")
-        subprocess.run([build.HIPCC, *build.FLAGS, "-S", "--cuda-device-only", "-o", str(out),
-                        src], check=True, capture_output=True)
+        subprocess.run([build.HIPCC, *build.flags_for(src), "-S", "--cuda-device-only", "-o",
+                        str(out), src], check=True, capture_output=True)
         text = out.read_text()
         for m in re.finditer(r"^(_Z\w+):[^\n]*\n(.*?)^\.Lfunc_end", text, re.S | re.M):
             funcs[m.group(1)] = m.group(2).splitlines()
