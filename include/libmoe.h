@@ -171,6 +171,27 @@ moe_status moe_expert_gate_up(const uint16_t* x, int32_t T, int32_t k, const int
 moe_status moe_expert_down(const uint16_t* h, int32_t T, int32_t k, const int32_t* offsets,
                            const moe_expert_weights* w, uint16_t* y, void* stream);
 
+/* The routed experts and the shared expert together [KT 1.2: one shared expert beside the routed
+ * ones, used by every token]: moe_expert_gate_up / moe_expert_down over the T*k grouped rows
+ * followed by T more rows, row T*k + t being token t for the shared expert `ws` (one expert,
+ * n_groups == 1, the same dtype, H and I as w).  At decode sizes (T*k <= 32 * n_groups) each
+ * phase is one launch whose grid covers both, so the shared expert needs no stream of its own;
+ * otherwise the routed and the shared GEMM run one after the other on `stream`.  The routed rows
+ * are those of moe_expert_gate_up / moe_expert_down bit for bit; the shared rows are those of
+ * the separate identity-grouped calls bit for bit when T <= 32 or outside decode sizes (the same
+ * kernel runs), and otherwise equal up to the order of the fp32 sums (the grid's decode kernel
+ * against the separate call's GEMM).
+ *   h : bf16 [T*k + T][I] (gate_up out, down in);  y : bf16 [T*k + T][H] out; the shared
+ *       expert's output is y + T*k*H (as moe_combine's shared_y).
+ * perm and offsets are required (from moe_permute).  Errors as for the separate calls, plus
+ * INVALID_ARG for a missing or mismatched ws and UNSUPPORTED when T*k + T >= 2^31. */
+moe_status moe_expert_gate_up_shared(const uint16_t* x, int32_t T, int32_t k, const int32_t* perm,
+                                     const int32_t* offsets, const moe_expert_weights* w,
+                                     const moe_expert_weights* ws, uint16_t* h, void* stream);
+moe_status moe_expert_down_shared(const uint16_t* h, int32_t T, int32_t k, const int32_t* offsets,
+                                  const moe_expert_weights* w, const moe_expert_weights* ws,
+                                  uint16_t* y, void* stream);
+
 /* Bytes of workspace moe_expert_ffn needs (host output): the bf16 intermediate h [T*k][I]. */
 moe_status moe_expert_ffn_workspace_size(int32_t T, int32_t k, const moe_expert_weights* w,
                                          size_t* bytes);

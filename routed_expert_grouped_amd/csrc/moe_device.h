@@ -108,6 +108,9 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
 // rounded up to 8), so each XCD walks one contiguous range of logical tiles, and tiles that are
 // close in that range run at about the same time on the same L2.
 //
+// An optional extra group (extra_rows > 0) follows the n_groups groups: its rows start at
+// offsets[n_groups] and it has extra_rows of them.
+//
 // Within a group, logical tiles go in supertiles of up to kSuperM m-tiles: the m-tiles of one
 // supertile are the fastest index, its n-tiles the next.  Workgroups that read the same weight
 // tile (same expert and n-tile, different rows) are therefore neighbours and walk K together,
@@ -123,18 +126,21 @@ struct Tile {
 };
 
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int n_groups,
-                                          int identity_rows, int BM, int n_tiles, Tile& t) {
+                                          int identity_rows, int BM, int n_tiles, Tile& t,
+                                          int extra_rows = 0) {
     const int lane = lane_id();
     const int wg = (int)blockIdx.x;
     int total_m, incl = 0, local = 0;
-    const int G = (n_groups + kWave - 1) / kWave;  // groups per lane, contiguous
+    const int groups = n_groups + (extra_rows > 0 ? 1 : 0);
+    const int G = (groups + kWave - 1) / kWave;  // groups per lane, contiguous
+    auto count = [&](int g) { return g < n_groups ? offsets[g + 1] - offsets[g] : extra_rows; };
     if (offsets == nullptr) {
         total_m = (identity_rows + BM - 1) / BM;
     } else {
         for (int i = 0; i < G; ++i) {
             const int g = lane * G + i;
-            if (g < n_groups) {
-                const int n = offsets[g + 1] - offsets[g];
+            if (g < groups) {
+                const int n = count(g);
                 local += (n + BM - 1) / BM;
             }
         }
@@ -177,8 +183,8 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
         int m0 = incl - local;  // first m-tile of this lane's first group
         for (int i = 0; i < G; ++i) {
             const int g = lane * G + i;
-            if (g >= n_groups) break;
-            const int a = offsets[g], n = offsets[g + 1] - a;
+            if (g >= groups) break;
+            const int a = offsets[g], n = count(g);
             const int tiles = (n + BM - 1) / BM;
             if (mt < m0 + tiles) {
                 group = g;

@@ -30,6 +30,14 @@ struct GemmArgs {
     // aexp their block exponents e (scale 2^e), [rows of act][aexp_pitch]
     const int8_t* aexp;
     int aexp_pitch;
+    // An extra group after the n_groups experts (the shared expert in the routed decode launch;
+    // GEMV only): extra_rows rows starting at grouped row `rows` (= offsets[n_groups]), row
+    // rows + t holding token t, with its own weights (one expert's matrices and scales).
+    int extra_rows;
+    const void* xw0;
+    const void* xw1;
+    const float* xs0;
+    const float* xs1;
 };
 
 // gemv shape: m-tiles of 16 rows; kGemvWaves waves per workgroup, each wave owning 16 h-columns

@@ -79,14 +79,21 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
 
     Tile tile;
     const int n_tiles = a.N / kCols;
-    if (!find_tile(kGrouped ? a.offsets : nullptr, a.n_groups, a.rows, kGemvBM, n_tiles, tile))
+    if (!find_tile(kGrouped ? a.offsets : nullptr, a.n_groups, a.rows, kGemvBM, n_tiles, tile,
+                   kGrouped ? a.extra_rows : 0))
         return;
 
     const int lane = lane_id(), wave = uniform((int)(threadIdx.x >> 6));
     const int cw = wave % kColWaves, kp = wave / kColWaves;  // column group, K part
     const int m = lane & 15, kq = lane >> 4;
     const int K = a.K;
-    const int e = tile.group;
+    // the extra group (the shared expert): its own weights, expert index 0, row rows + t = token t
+    const bool xg = kGrouped && tile.group == a.n_groups;
+    const int e = xg ? 0 : tile.group;
+    const void* W0 = xg ? a.xw0 : a.w0;
+    const void* W1 = xg ? a.xw1 : a.w1;
+    const float* S0 = xg ? a.xs0 : a.s0;
+    const float* S1 = xg ? a.xs1 : a.s1;
     const int p = tile.row0 + m;
     const bool valid = p < tile.row1;
     uint8_t* lds = sW[wave];
@@ -95,7 +102,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     // first row instead: MFMA output rows depend only on their own A row, and those rows are
     // never stored, so the loads stay unconditional (exact load counters, no branches).
     const int pa = valid ? p : tile.row0;
-    const int ra = (kPhase == 1 && kGrouped) ? a.perm[pa] / a.k : pa;
+    const int ra = (kPhase == 1 && kGrouped) ? (xg ? pa - a.rows : a.perm[pa] / a.k) : pa;
     // this wave's K part: 128-blocks [kb0w, kb0w + kblocks) of kb_all
     const int kb_all = K / 128, kblocks = kb_all / kSplit, kb0w = kp * kblocks;
     const uint16_t* arow = a.act + (size_t)ra * K + (size_t)kb0w * 128;
@@ -106,16 +113,16 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     const int nb_last = kblocks - (nst - 1) * kBPS;   // blocks in the last stage
     const int lrow = lane / kLPR, lchunk = lane % kLPR;
     const size_t kofs0 = (size_t)kb0w * kBB + lchunk * 16;  // the part's first byte of a row
-    const uint8_t* g0 = (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + lrow) * row_bytes + kofs0;
+    const uint8_t* g0 = (const uint8_t*)W0 + ((size_t)e * a.N + n0 + lrow) * row_bytes + kofs0;
     const uint8_t* g1 = kPhase == 1
-        ? (const uint8_t*)a.w1 + ((size_t)e * a.N + n0 + lrow) * row_bytes + kofs0
-        : (const uint8_t*)a.w0 + ((size_t)e * a.N + n0 + 16 + lrow) * row_bytes + kofs0;
+        ? (const uint8_t*)W1 + ((size_t)e * a.N + n0 + lrow) * row_bytes + kofs0
+        : (const uint8_t*)W0 + ((size_t)e * a.N + n0 + 16 + lrow) * row_bytes + kofs0;
     const size_t ins_stride = (size_t)kRPI * row_bytes;  // bytes between a group's instructions
     const float* s0 = nullptr;
     const float* s1 = nullptr;
     if (kFmt == kFP8) {
-        s0 = a.s0 + ((size_t)e * (a.N / 128) + n0 / 128) * kb_all + kb0w;
-        s1 = kPhase == 1 ? a.s1 + ((size_t)e * (a.N / 128) + n0 / 128) * kb_all + kb0w : s0;
+        s0 = S0 + ((size_t)e * (a.N / 128) + n0 / 128) * kb_all + kb0w;
+        s1 = kPhase == 1 ? S1 + ((size_t)e * (a.N / 128) + n0 / 128) * kb_all + kb0w : s0;
     }
     // MXFP4: E8M0 bytes [N][K/32]; the wave's scale row r (0..31) is weight row n0 + r of w0
     // (r < 16) and of w1 (phase 1) or w0 (phase 2) (r >= 16).  A dword per block holds the
@@ -131,8 +138,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
             const int lgP = max(1, 32 - __builtin_clz((unsigned)(wdw - 1) | 1u));
             const int lgR = 6 - lgP;  // rows per instruction: 2^lgR (1 to 32)
             const int d = lane & ((1 << lgP) - 1), rr = lane >> lgP;
-            const uint8_t* sb0 = (const uint8_t*)a.s0;
-            const uint8_t* sb1 = (const uint8_t*)(kPhase == 1 ? a.s1 : a.s0);
+            const uint8_t* sb0 = (const uint8_t*)S0;
+            const uint8_t* sb1 = (const uint8_t*)(kPhase == 1 ? S1 : S0);
             const int nins = 32 >> lgR;
             for (int i = 0; i < nins; ++i) {
                 const int r = (i << lgR) + rr;  // < 32
@@ -304,7 +311,9 @@ static int max_mtiles(int rows, int n_groups, int BM) {
 
 // Launch one phase.  rows = grouped rows (T*k).
 static moe_status launch_phase(int phase, const GemmArgs& a, hipStream_t st) {
-    // many rows per expert: the GEMMs (MXFP4 weights: the 4-bit GEMM where its shape fits)
+    // many rows per expert: the GEMMs (MXFP4 weights: the 4-bit GEMM where its shape fits); an
+    // extra group is a GEMV-only feature (its callers check)
+    if (a.extra_rows > 0 && !use_gemv(a.rows, a.n_groups)) return MOE_ERR_UNSUPPORTED;
     if (!use_gemv(a.rows, a.n_groups)) {
         if (!a.fp4) return launch_gemm(phase, a, st);
         if (w4_gemm_fits(phase, a)) return launch_gemm_w4(phase, a, st);
@@ -317,7 +326,8 @@ static moe_status launch_phase(int phase, const GemmArgs& a, hipStream_t st) {
     const int kb = a.K / 128;
     const int split = (phase != 1 || !a.fp8) ? 1 : kb % 4 == 0 ? 4 : kb % 2 == 0 ? 2 : 1;
     const int cols = W / split * (phase == 1 ? 16 : 32);
-    const int64_t wgs = (int64_t)max_mtiles(a.rows, a.offsets ? a.n_groups : 1, kGemvBM) * (a.N / cols);
+    const int groups = (a.offsets ? a.n_groups : 1) + (a.extra_rows > 0 ? 1 : 0);
+    const int64_t wgs = (int64_t)max_mtiles(a.rows + a.extra_rows, groups, kGemvBM) * (a.N / cols);
     if (wgs > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((wgs + 7) & ~int64_t(7))), block(W * 64);
 #define MOE_GEMV(F, P, G) gemv_kernel<F, P, G, W, 1><<<grid, block, 0, st>>>(a)
@@ -397,6 +407,95 @@ extern "C" moe_status moe_expert_down(const uint16_t* h, int32_t T, int32_t k,
     a.fp8 = w->dtype == MOE_W_FP8_E4M3_B128;
     a.fp4 = w->dtype == MOE_W_MXFP4_G32;
     a.out = y;
+    return launch_phase(2, a, as_stream(stream));
+}
+
+// The routed experts and the shared expert in one launch per phase (decode sizes): the shared
+// expert is an extra group of T rows after the T*k grouped ones, so one grid streams both
+// experts' weights and no second stream or cross-stream wait is needed.
+static moe_status check_shared(const moe_expert_weights* w, const moe_expert_weights* ws) {
+    const moe_status s = check_weights(ws);
+    if (s != MOE_OK) return s;
+    if (ws->n_groups != 1 || ws->dtype != w->dtype || ws->H != w->H || ws->I != w->I)
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_expert_gate_up_shared(const uint16_t* x, int32_t T, int32_t k,
+                                                const int32_t* perm, const int32_t* offsets,
+                                                const moe_expert_weights* w,
+                                                const moe_expert_weights* ws, uint16_t* h,
+                                                void* stream) {
+    if (T < 0 || k < 1) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!x || !h || !perm || !offsets) return MOE_ERR_INVALID_ARG;
+    moe_status s = check_weights(w);
+    if (s != MOE_OK) return s;
+    if ((s = check_shared(w, ws)) != MOE_OK) return s;
+    if ((s = check_grouping(T, k, perm, offsets, w, true)) != MOE_OK) return s;
+    if ((int64_t)T * k + T > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (!use_gemv(T * k, w->n_groups)) {  // many rows per expert: one GEMM launch each
+        if ((s = moe_expert_gate_up(x, T, k, perm, offsets, w, h, stream)) != MOE_OK) return s;
+        return moe_expert_gate_up(x, T, 1, nullptr, nullptr, ws, h + (size_t)T * k * w->I, stream);
+    }
+    GemmArgs a{};
+    a.act = x;
+    a.perm = perm;
+    a.offsets = offsets;
+    a.k = k;
+    a.rows = T * k;
+    a.n_groups = w->n_groups;
+    a.N = w->I;
+    a.K = w->H;
+    a.w0 = w->w_gate;
+    a.w1 = w->w_up;
+    a.s0 = w->s_gate;
+    a.s1 = w->s_up;
+    a.fp8 = w->dtype == MOE_W_FP8_E4M3_B128;
+    a.fp4 = w->dtype == MOE_W_MXFP4_G32;
+    a.out = h;
+    a.extra_rows = T;
+    a.xw0 = ws->w_gate;
+    a.xw1 = ws->w_up;
+    a.xs0 = ws->s_gate;
+    a.xs1 = ws->s_up;
+    return launch_phase(1, a, as_stream(stream));
+}
+
+extern "C" moe_status moe_expert_down_shared(const uint16_t* h, int32_t T, int32_t k,
+                                             const int32_t* offsets, const moe_expert_weights* w,
+                                             const moe_expert_weights* ws, uint16_t* y,
+                                             void* stream) {
+    if (T < 0 || k < 1) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!h || !y || !offsets) return MOE_ERR_INVALID_ARG;
+    moe_status s = check_weights(w);
+    if (s != MOE_OK) return s;
+    if ((s = check_shared(w, ws)) != MOE_OK) return s;
+    if ((s = check_grouping(T, k, nullptr, offsets, w, false)) != MOE_OK) return s;
+    if ((int64_t)T * k + T > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (!use_gemv(T * k, w->n_groups)) {
+        if ((s = moe_expert_down(h, T, k, offsets, w, y, stream)) != MOE_OK) return s;
+        return moe_expert_down(h + (size_t)T * k * w->I, T, 1, nullptr, ws, y + (size_t)T * k * w->H,
+                               stream);
+    }
+    GemmArgs a{};
+    a.act = h;
+    a.perm = nullptr;
+    a.offsets = offsets;
+    a.k = k;
+    a.rows = T * k;
+    a.n_groups = w->n_groups;
+    a.N = w->H;
+    a.K = w->I;
+    a.w0 = w->w_down;
+    a.s0 = w->s_down;
+    a.fp8 = w->dtype == MOE_W_FP8_E4M3_B128;
+    a.fp4 = w->dtype == MOE_W_MXFP4_G32;
+    a.out = y;
+    a.extra_rows = T;
+    a.xw0 = ws->w_down;
+    a.xs0 = ws->s_down;
     return launch_phase(2, a, as_stream(stream));
 }
 

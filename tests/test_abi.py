@@ -105,6 +105,31 @@ def test_expert_validation():
     assert dn(FAKE, 0, 2, FAKE, ctypes.byref(ok), FAKE, None) == moe.MOE_OK
 
 
+def test_shared_expert_calls_validation():
+    """moe_expert_gate_up_shared / moe_expert_down_shared: the shared expert must be one expert
+    of the routed experts' dtype and shape; perm and offsets are required."""
+    L = moe.lib()
+    gu, dn = L.moe_expert_gate_up_shared, L.moe_expert_down_shared
+    w, ws = _w(), _w(n=1)
+    assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(w), None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    two = _w(n=2)
+    assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(w), ctypes.byref(two), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    other_dtype = _w(dtype=1, n=1)
+    assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(w), ctypes.byref(other_dtype), FAKE,
+              None) == moe.MOE_ERR_INVALID_ARG
+    other_h = _w(n=1, H=384)
+    assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(w), ctypes.byref(other_h), FAKE,
+              None) == moe.MOE_ERR_INVALID_ARG
+    assert gu(FAKE, 4, 2, None, FAKE, ctypes.byref(w), ctypes.byref(ws), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert gu(FAKE, 4, 2, FAKE, None, ctypes.byref(w), ctypes.byref(ws), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert gu(FAKE, 4, 2, FAKE, FAKE, ctypes.byref(w), ctypes.byref(ws), None, None) == moe.MOE_ERR_INVALID_ARG
+    assert gu(FAKE, 0, 2, FAKE, FAKE, ctypes.byref(w), ctypes.byref(ws), FAKE, None) == moe.MOE_OK
+    assert dn(FAKE, 4, 2, None, ctypes.byref(w), ctypes.byref(ws), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert dn(FAKE, 4, 2, FAKE, ctypes.byref(w), ctypes.byref(two), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert dn(FAKE, 4, 0, FAKE, ctypes.byref(w), ctypes.byref(ws), FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert dn(FAKE, 0, 2, FAKE, ctypes.byref(w), ctypes.byref(ws), FAKE, None) == moe.MOE_OK
+
+
 def test_ffn_workspace():
     L = moe.lib()
     w = _w()

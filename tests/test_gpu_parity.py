@@ -214,3 +214,38 @@ def test_large_layers_sampled_rows(cfg, rows):
     np.testing.assert_array_equal(g["ids"], rid)
     assert np.max(np.abs(g["w"].astype(np.float64) - rw)) <= 1e-6
     compare_sampled(layer, g, rows=rows)
+
+
+@pytest.mark.parametrize("cfg,over", [("tiny_fp8", {}), ("tiny", {}), ("dsv3_decode", {}),
+                                      ("dsv3_decode", {"wdtype": "mxfp4"}),
+                                      (mid(T=37, E=64, k=8), {}),            # GEMV: one grid
+                                      (mid(T=24, H=640, E=16, k=2), {}),     # K unsplit
+                                      (mid(), {})])                          # GEMMs: two launches
+def test_shared_expert_in_the_routed_launches_is_the_separate_calls(cfg, over):
+    """moe_expert_gate_up_shared / moe_expert_down_shared (the shared expert as an extra group
+    of the routed launches at decode sizes) give the routed rows of the separate routed calls bit
+    for bit, and the shared rows of the separate shared calls bit for bit where those run the
+    same kernel (T <= 32, or many rows per expert); at T > 32 with few rows per expert the
+    separate shared call runs a GEMM, and the rows agree to the parity bar."""
+    layer = layer_for(cfg, **over) if isinstance(cfg, str) else layer_for(cfg, seed=1)
+    T, k = layer.T, layer.k
+    ids, _ = moe.moe_route(layer.scores, k, layer.score_fn, layer.renorm)
+    _, offsets, perm, _ = moe.moe_permute(ids, layer.E)
+    w, ws = moe.expert_weights(layer.experts), moe.expert_weights(layer.shared)
+    h_all = moe.moe_expert_gate_up_shared(layer.x, k, perm, offsets, w, ws)
+    y_all = moe.moe_expert_down_shared(h_all, T, k, offsets, w, ws)
+    h_r = moe.moe_expert_gate_up(layer.x, k, perm, offsets, w)
+    y_r = moe.moe_expert_down(h_r, T, k, offsets, w)
+    h_s = moe.moe_expert_gate_up(layer.x, 1, None, None, ws)
+    y_s = moe.moe_expert_down(h_s, T, 1, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(h_all[:T * k], h_r) and torch.equal(y_all[:T * k], y_r)
+    same_kernel = T <= 32 or T * k > 32 * layer.E
+    for got, ref in ((h_all[T * k:], h_s), (y_all[T * k:], y_s)):
+        if same_kernel:
+            assert torch.equal(got, ref)
+        else:
+            g = oracle.bf16_bits_to_float(got.cpu())
+            r = oracle.bf16_bits_to_float(ref.cpu())
+            rel = np.linalg.norm(g - r, axis=1) / np.linalg.norm(r, axis=1)
+            assert rel.max() <= 1e-2, rel.max()
