@@ -24,13 +24,16 @@
 
 namespace moe {
 
-// One workgroup = kWaves waves; each wave owns two 16-row weight groups (phase 1: the same 16
-// rows of gate and of up; phase 2: 32 consecutive rows of down) over the full K, for one m-tile
-// of up to 16 grouped rows.  kGrouped = false is the identity grouping (shared expert).
+// One workgroup = kWaves waves; each wave owns kG 16-row weight groups (phase 1: the same
+// 8 kG rows of gate and of up; phase 2: 16 kG consecutive rows of down) over the full K, for one
+// m-tile of up to 16 grouped rows.  kGrouped = false is the identity grouping (shared expert).
+// Every activation fragment a lane loads feeds kG MFMAs, so kG = 4 halves the activation loads
+// per weight byte; MXFP4 weights (twice the K values per weight byte of FP8) take it where the
+// shape allows.
 //
-// kSplit > 1 (FP8 gate/up): the workgroup's waves own kWaves / kSplit column groups, each over
-// kSplit consecutive parts of K; after the K loop the other parts' fp32 sums are added to part
-// 0's, in part order, through LDS.  A workgroup then streams 1/kSplit of the bytes, so the launch
+// kSplit > 1 (gate/up: FP8, and MXFP4 with four groups a wave): the workgroup's waves own
+// kWaves / kSplit column groups, each over kSplit consecutive parts of K; after the K loop the
+// other parts' fp32 sums are added to part 0's, in part order, through LDS.  A workgroup then streams 1/kSplit of the bytes, so the launch
 // has kSplit times more, shorter workgroups and its ramp-down at the end (the last workgroups
 // running on a few CUs) is that much shorter.  At the DeepSeek-V3 decode shape the unsplit
 // launch is 3168 workgroups for 1024 resident slots.
@@ -55,15 +58,17 @@ namespace moe {
 // weight loads, and reads one 8-byte LDS word per row group per stage.  Rows longer than one
 // window (K > 8192) are refilled at each window boundary after the wave's loads have drained.
 constexpr int kBF16 = 0, kFP8 = 1, kMXFP4 = 2;
-constexpr int kScaleWin = 64;    // 128-blocks of scales per window
+constexpr int kScaleWin = 64;    // 128-blocks of scales per window (32 rows a wave; half that for 64)
 constexpr int kScaleSlot = 264;  // LDS bytes per scale load instruction (256 + 8: 8-byte reads
                                  // of 16 rows fall in distinct banks)
 
-template <int kFmt, int kPhase, bool kGrouped, int kWaves, int kSplit>
+template <int kFmt, int kPhase, bool kGrouped, int kWaves, int kSplit, int kG>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     static_assert(kWaves % kSplit == 0, "whole column groups per workgroup");
+    static_assert(kG == 2 || kG == 4, "two or four 16-row weight groups a wave");
+    constexpr int kRows = 16 * kG;                    // weight rows per wave
     constexpr int kColWaves = kWaves / kSplit;        // waves per K part
-    constexpr int kWaveCols = kPhase == 1 ? 16 : 32;  // output columns per wave
+    constexpr int kWaveCols = kPhase == 1 ? kRows / 2 : kRows;  // output columns per wave
     constexpr int kCols = kColWaves * kWaveCols;
     // a stage is kBPS 128-blocks, so that every format loads whole 128-byte lines per row
     constexpr int kBPS = kFmt == kMXFP4 ? 2 : 1;
@@ -73,9 +78,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     constexpr int kLPR = kRowB / 16;                  // lanes per row in a load instruction
     constexpr int kRPI = 64 / kLPR;                   // rows per load instruction
     constexpr int kIns = 16 / kRPI;                   // load instructions per 16-row group
-    __shared__ __attribute__((aligned(16))) uint8_t sW[kWaves][2 * 16 * kLD];
+    __shared__ __attribute__((aligned(16))) uint8_t sW[kWaves][kRows * kLD];
     constexpr bool kMX = kFmt == kMXFP4;
-    __shared__ __attribute__((aligned(16))) uint8_t sS[kMX ? kWaves : 1][kMX ? 32 * kScaleSlot : 16];
+    // MXFP4 scale window: the wave's LDS area holds kRows * kWin / 64 load slots
+    constexpr int kWin = kScaleWin * 32 / kRows;
+    __shared__ __attribute__((aligned(16))) uint8_t sS[kMX ? kWaves : 1][kMX ? kRows * kWin / 64 * kScaleSlot : 16];
 
     Tile tile;
     const int n_tiles = a.N / kCols;
@@ -113,10 +120,14 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     const int nb_last = kblocks - (nst - 1) * kBPS;   // blocks in the last stage
     const int lrow = lane / kLPR, lchunk = lane % kLPR;
     const size_t kofs0 = (size_t)kb0w * kBB + lchunk * 16;  // the part's first byte of a row
-    const uint8_t* g0 = (const uint8_t*)W0 + ((size_t)e * a.N + n0 + lrow) * row_bytes + kofs0;
-    const uint8_t* g1 = kPhase == 1
-        ? (const uint8_t*)W1 + ((size_t)e * a.N + n0 + lrow) * row_bytes + kofs0
-        : (const uint8_t*)W0 + ((size_t)e * a.N + n0 + 16 + lrow) * row_bytes + kofs0;
+    // group g: phase 1 gate (g < kG / 2) or up rows n0 + 16 (g mod kG / 2); phase 2 rows n0 + 16 g
+    const uint8_t* gp[kG];
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+        const void* W = (kPhase == 1 && g >= kG / 2) ? W1 : W0;
+        const int wr = n0 + 16 * (kPhase == 1 ? g % (kG / 2) : g) + lrow;
+        gp[g] = (const uint8_t*)W + ((size_t)e * a.N + wr) * row_bytes + kofs0;
+    }
     const size_t ins_stride = (size_t)kRPI * row_bytes;  // bytes between a group's instructions
     const float* s0 = nullptr;
     const float* s1 = nullptr;
@@ -124,38 +135,42 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
         s0 = S0 + ((size_t)e * (a.N / 128) + n0 / 128) * kb_all + kb0w;
         s1 = kPhase == 1 ? S1 + ((size_t)e * (a.N / 128) + n0 / 128) * kb_all + kb0w : s0;
     }
-    // MXFP4: E8M0 bytes [N][K/32]; the wave's scale row r (0..31) is weight row n0 + r of w0
-    // (r < 16) and of w1 (phase 1) or w0 (phase 2) (r >= 16).  A dword per block holds the
-    // scales of its 4 groups, one per K quarter kq.  A window of wdw blocks goes to the wave's
-    // LDS area with P = 2^ceil(log2 wdw) (at least 2) dwords per row and 64 / P rows per load
-    // instruction, each instruction filling one kScaleSlot; soff0 / soff1 are the LDS offsets of
-    // this lane's two compute rows (m and 16 + m) in the current window.
+    // MXFP4: E8M0 bytes [N][K/32]; the wave's scale row r (0..kRows) is weight row n0 + r of w0
+    // (r < kRows / 2) and of w1 (phase 1, row n0 + r - kRows / 2) or w0 (phase 2, row n0 + r)
+    // (r >= kRows / 2).  A dword per block holds the scales of its 4 groups, one per K quarter
+    // kq.  A window of wdw blocks goes to the wave's LDS area with P = 2^ceil(log2 wdw) (at least
+    // 2) dwords per row and 64 / P rows per load instruction, each instruction filling one
+    // kScaleSlot; soff[g] is the LDS offset of this lane's compute row 16 g + m in the window.
     uint8_t* sl = sS[kMX ? wave : 0];
-    int soff0 = 0, soff1 = 0;
+    int soff[kG] = {};
     auto fill_scales = [&](int w0) {
         if constexpr (kMX) {
-            const int wdw = min(kScaleWin, kblocks - w0);
+            const int wdw = min(kWin, kblocks - w0);
             const int lgP = max(1, 32 - __builtin_clz((unsigned)(wdw - 1) | 1u));
             const int lgR = 6 - lgP;  // rows per instruction: 2^lgR (1 to 32)
             const int d = lane & ((1 << lgP) - 1), rr = lane >> lgP;
             const uint8_t* sb0 = (const uint8_t*)S0;
             const uint8_t* sb1 = (const uint8_t*)(kPhase == 1 ? S1 : S0);
-            const int nins = 32 >> lgR;
+            const int nins = kRows >> lgR;
             for (int i = 0; i < nins; ++i) {
-                const int r = (i << lgR) + rr;  // < 32
-                const uint8_t* row = r < 16 ? sb0 + ((size_t)e * a.N + n0 + r) * (K / 32)
-                                            : sb1 + ((size_t)e * a.N + n0 + (kPhase == 1 ? r - 16 : r)) * (K / 32);
+                const int r = (i << lgR) + rr;  // < kRows
+                const uint8_t* row = r < kRows / 2
+                    ? sb0 + ((size_t)e * a.N + n0 + r) * (K / 32)
+                    : sb1 + ((size_t)e * a.N + n0 + (kPhase == 1 ? r - kRows / 2 : r)) * (K / 32);
                 lds_dma4(row + 4 * (kb0w + w0 + min(d, wdw - 1)), sl + i * kScaleSlot);
             }
             auto off = [&](int r) { return (r >> lgR) * kScaleSlot + ((r & ((1 << lgR) - 1)) << (lgP + 2)); };
-            soff0 = off(m);
-            soff1 = off(16 + m);
+#pragma unroll
+            for (int g = 0; g < kG; ++g) soff[g] = off(16 * g + m);
         }
     };
 
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    u32x4 b0[2][kIns], b1[2][kIns], xa[2][kBPS][4];
-    float sg0[2], sg1[2];             // FP8 block scales of the staged blocks (wave-uniform)
+    f32x4 acc[kG];
+#pragma unroll
+    for (int g = 0; g < kG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 bw[2][kG][kIns], xa[2][kBPS][4];
+    float sg0[2], sg1[2];  // FP8 block scales of the staged blocks (wave-uniform): groups below
+                           // kG / 2, and the others
     auto load = [&](int s, int st) {
         const int kb0 = s * kBPS;
         sg0[st] = kFmt == kFP8 ? s0[kb0] : 1.0f;
@@ -165,10 +180,10 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
         size_t kofs = (size_t)s * kRowB;
         if (kBPS > 1 && kb0 + 1 >= kblocks && lchunk >= kLPR / 2) kofs -= kRowB / 2;
 #pragma unroll
-        for (int i = 0; i < kIns; ++i) {
-            b0[st][i] = __builtin_nontemporal_load((const u32x4*)(g0 + i * ins_stride + kofs));
-            b1[st][i] = __builtin_nontemporal_load((const u32x4*)(g1 + i * ins_stride + kofs));
-        }
+        for (int i = 0; i < kIns; ++i)
+#pragma unroll
+            for (int g = 0; g < kG; ++g)
+                bw[st][g][i] = __builtin_nontemporal_load((const u32x4*)(gp[g] + i * ins_stride + kofs));
 #pragma unroll
         for (int b = 0; b < kBPS; ++b) {
             const int kb = min(kb0 + b, kblocks - 1);
@@ -180,9 +195,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     auto compute = [&](int st, int stage, int nb) {
         // MXFP4: scales of the stage's blocks (a stage starts a window only at a multiple of
         // kScaleWin / kBPS; the first window is filled before the loop)
-        uint32_t sc0[kBPS], sc1[kBPS];
+        uint32_t sc[kG][kBPS];
         if constexpr (kMX) {
-            const int j = stage * kBPS % kScaleWin;
+            const int j = stage * kBPS % kWin;
             if (j == 0 && stage > 0) {
                 // refill: every load of this wave has landed and every LDS read returned
                 __builtin_amdgcn_s_waitcnt(0);
@@ -190,59 +205,52 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
             static_assert(kBPS == 2, "one 8-byte LDS read per row group covers a stage");
-            const uint2 v0 = *(const uint2*)(sl + soff0 + 4 * j);
-            const uint2 v1 = *(const uint2*)(sl + soff1 + 4 * j);
-            sc0[0] = v0.x, sc0[1] = v0.y, sc1[0] = v1.x, sc1[1] = v1.y;
+#pragma unroll
+            for (int g = 0; g < kG; ++g) {
+                const uint2 v = *(const uint2*)(sl + soff[g] + 4 * j);
+                sc[g][0] = v.x, sc[g][1] = v.y;
+            }
         }
         // load layout -> LDS rows -> MFMA layout (lane: row m; of block b the 32 K values of
         // quarter kq, kBB / 4 bytes from byte b * kBB + kq * kBB / 4)
 #pragma unroll
-        for (int i = 0; i < kIns; ++i) {
-            *(u32x4*)&lds[(i * kRPI + lrow) * kLD + lchunk * 16] = b0[st][i];
-            *(u32x4*)&lds[(16 + i * kRPI + lrow) * kLD + lchunk * 16] = b1[st][i];
-        }
+        for (int i = 0; i < kIns; ++i)
+#pragma unroll
+            for (int g = 0; g < kG; ++g)
+                *(u32x4*)&lds[(16 * g + i * kRPI + lrow) * kLD + lchunk * 16] = bw[st][g][i];
 #pragma unroll
         for (int b = 0; b < kBPS; ++b) {
             if (b >= nb) break;
             constexpr int kV = kBB / 64;  // 16-byte vectors per lane per block
-            u32x4 r0[kV], r1[kV];
+            u32x4 rw[kG][kV];
 #pragma unroll
-            for (int i = 0; i < kV; ++i) {
-                r0[i] = *(const u32x4*)&lds[m * kLD + b * kBB + kq * (kBB / 4) + i * 16];
-                r1[i] = *(const u32x4*)&lds[(16 + m) * kLD + b * kBB + kq * (kBB / 4) + i * 16];
-            }
-            float f0 = 1.0f, f1 = 1.0f;  // MXFP4: this lane's group scales
-            if constexpr (kMX) {
-                f0 = e8m0_to_f32((sc0[b] >> (8 * kq)) & 255u);
-                f1 = e8m0_to_f32((sc1[b] >> (8 * kq)) & 255u);
-            }
-            f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < kV; ++i)
+#pragma unroll
+                for (int g = 0; g < kG; ++g)
+                    rw[g][i] = *(const u32x4*)&lds[(16 * g + m) * kLD + b * kBB + kq * (kBB / 4) + i * 16];
+            float f[kG];  // MXFP4: this lane's group scales
+#pragma unroll
+            for (int g = 0; g < kG; ++g) f[g] = kMX ? e8m0_to_f32((sc[g][b] >> (8 * kq)) & 255u) : 1.0f;
+            f32x4 p[kG];
+#pragma unroll
+            for (int g = 0; g < kG; ++g) p[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                bf16x8 w0v, w1v;
-                if (kFmt == kFP8) {
-                    const uint32_t* u0 = (const uint32_t*)r0;
-                    const uint32_t* u1 = (const uint32_t*)r1;
-                    w0v = fp8x8_to_bf16x8(u0[2 * i], u0[2 * i + 1]);
-                    w1v = fp8x8_to_bf16x8(u1[2 * i], u1[2 * i + 1]);
-                } else if (kFmt == kMXFP4) {
-                    const uint32_t* u0 = (const uint32_t*)r0;
-                    const uint32_t* u1 = (const uint32_t*)r1;
-                    w0v = fp4x8_to_bf16x8(u0[i], f0);
-                    w1v = fp4x8_to_bf16x8(u1[i], f1);
-                } else {
-                    w0v = as_bf16x8(r0[i]);
-                    w1v = as_bf16x8(r1[i]);
-                }
                 const bf16x8 xv = as_bf16x8(xa[st][b][i]);
-                p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w0v, p0, 0, 0, 0);
-                p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, w1v, p1, 0, 0, 0);
+#pragma unroll
+                for (int g = 0; g < kG; ++g) {
+                    const uint32_t* u = (const uint32_t*)rw[g];
+                    const bf16x8 wv = kFmt == kFP8 ? fp8x8_to_bf16x8(u[2 * i], u[2 * i + 1])
+                                    : kFmt == kMXFP4 ? fp4x8_to_bf16x8(u[i], f[g])
+                                                     : as_bf16x8(rw[g][i]);
+                    p[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv, wv, p[g], 0, 0, 0);
+                }
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                acc0[r] = fmaf(p0[r], sg0[st], acc0[r]);
-                acc1[r] = fmaf(p1[r], sg1[st], acc1[r]);
-            }
+            for (int g = 0; g < kG; ++g)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[g][r] = fmaf(p[g][r], g < kG / 2 ? sg0[st] : sg1[st], acc[g][r]);
         }
     };
     // 2-stage ring: two stages in flight.  The steady-state loop issues its loads without
@@ -252,7 +260,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     // MXFP4: the first scale window's direct loads go first; at least the 2 * kStageLoads weight
     // and activation loads of stages 0 and 1 follow them, so waiting until only stage 1's are
     // outstanding also covers them.
-    constexpr int kStageLoads = 2 * kIns + 4 * kBPS;
+    constexpr int kStageLoads = kG * kIns + 4 * kBPS;
     fill_scales(0);
     load(0, 0);
     load(nst > 1 ? 1 : 0, 1);
@@ -275,18 +283,17 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     if (rest == 3) compute(0, s + 2, nb_last);
 
     if constexpr (kSplit > 1) {  // the sums of K parts 1.. join part 0's, in part order
-        __shared__ f32x4 red[kSplit - 1][kColWaves][2][kWave];
+        __shared__ f32x4 red[kSplit - 1][kColWaves][kG][kWave];
         if (kp > 0) {
-            red[kp - 1][cw][0][lane] = acc0;
-            red[kp - 1][cw][1][lane] = acc1;
+#pragma unroll
+            for (int g = 0; g < kG; ++g) red[kp - 1][cw][g][lane] = acc[g];
         }
         __syncthreads();
         if (kp > 0) return;
 #pragma unroll
-        for (int q = 0; q < kSplit - 1; ++q) {
-            acc0 += red[q][cw][0][lane];
-            acc1 += red[q][cw][1][lane];
-        }
+        for (int q = 0; q < kSplit - 1; ++q)
+#pragma unroll
+            for (int g = 0; g < kG; ++g) acc[g] += red[q][cw][g][lane];
     }
     // D layout of the 16x16 MFMA: lane holds rows 4*(lane/16)+r (grouped rows), column lane%16
 #pragma unroll
@@ -294,12 +301,16 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
         const int row = tile.row0 + kq * 4 + r;
         if (row >= tile.row1) continue;
         if (kPhase == 1) {
-            const float g = acc0[r], u = acc1[r];
-            const float hval = g / (1.0f + __expf(-g)) * u;
-            a.out[(size_t)row * a.N + n0 + m] = f32_to_bf16(hval);
+#pragma unroll
+            for (int g = 0; g < kG / 2; ++g) {
+                const float gt = acc[g][r], u = acc[g + kG / 2][r];
+                const float hval = gt / (1.0f + __expf(-gt)) * u;
+                a.out[(size_t)row * a.N + n0 + 16 * g + m] = f32_to_bf16(hval);
+            }
         } else {
-            a.out[(size_t)row * a.N + n0 + m] = f32_to_bf16(acc0[r]);
-            a.out[(size_t)row * a.N + n0 + 16 + m] = f32_to_bf16(acc1[r]);
+#pragma unroll
+            for (int g = 0; g < kG; ++g)
+                a.out[(size_t)row * a.N + n0 + 16 * g + m] = f32_to_bf16(acc[g][r]);
         }
     }
 }
@@ -319,33 +330,46 @@ static moe_status launch_phase(int phase, const GemmArgs& a, hipStream_t st) {
         if (w4_gemm_fits(phase, a)) return launch_gemm_w4(phase, a, st);
     }
     constexpr int W = kGemvWaves;
-    // FP8 gate/up: K split in 4 parts where the 128-blocks divide evenly, else 2, else none
-    // (measured at the DeepSeek-V3 decode shape: 0.425 ms unsplit, 0.411 ms in 4 parts; the down
-    // projection, 5544 workgroups of a quarter of the bytes, gained nothing; MXFP4 weights, whose
-    // per-wave scale copy does not shrink with the part, lost 28%)
+    // MXFP4: four weight groups a wave where the columns divide into whole tiles.
+    // K split of gate/up: FP8 weights in 4 parts where the 128-blocks divide evenly, else 2, else
+    // none (measured at the DeepSeek-V3 decode shape: 0.425 ms unsplit, 0.411 ms in 4 parts; the
+    // down projection, 5544 workgroups of a quarter of the bytes, gained nothing); MXFP4 weights
+    // with four groups a wave in 2 parts, so that each part's scales fit one window (0.246 ->
+    // 0.229 ms; with two groups a wave, whose window already holds 64 blocks, splitting lost 28%)
     const int kb = a.K / 128;
-    const int split = (phase != 1 || !a.fp8) ? 1 : kb % 4 == 0 ? 4 : kb % 2 == 0 ? 2 : 1;
-    const int cols = W / split * (phase == 1 ? 16 : 32);
+    const int G = a.fp4 && a.N % (W * (phase == 1 ? 32 : 64)) == 0 ? 4 : 2;
+    const int split = phase != 1 ? 1
+                    : a.fp8      ? (kb % 4 == 0 ? 4 : kb % 2 == 0 ? 2 : 1)
+                    : (a.fp4 && G == 4 && kb % 2 == 0) ? 2 : 1;
+    const int cols = W / split * (phase == 1 ? 8 : 16) * G;
     const int groups = (a.offsets ? a.n_groups : 1) + (a.extra_rows > 0 ? 1 : 0);
     const int64_t wgs = (int64_t)max_mtiles(a.rows + a.extra_rows, groups, kGemvBM) * (a.N / cols);
     if (wgs > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((wgs + 7) & ~int64_t(7))), block(W * 64);
-#define MOE_GEMV(F, P, G) gemv_kernel<F, P, G, W, 1><<<grid, block, 0, st>>>(a)
-#define MOE_GEMV_SPLIT(G)                                                          \
-    (split == 4   ? gemv_kernel<kFP8, 1, G, W, 4><<<grid, block, 0, st>>>(a)        \
-     : split == 2 ? gemv_kernel<kFP8, 1, G, W, 2><<<grid, block, 0, st>>>(a)        \
-                  : gemv_kernel<kFP8, 1, G, W, 1><<<grid, block, 0, st>>>(a))
+#define MOE_GEMV(F, P, GR) gemv_kernel<F, P, GR, W, 1, 2><<<grid, block, 0, st>>>(a)
+#define MOE_GEMV4(P, GR)                                                           \
+    (G == 2 ? gemv_kernel<kMXFP4, P, GR, W, 1, 2><<<grid, block, 0, st>>>(a)        \
+            : gemv_kernel<kMXFP4, P, GR, W, 1, 4><<<grid, block, 0, st>>>(a))
+#define MOE_GEMV4_SPLIT(GR)                                                        \
+    (split == 2 ? gemv_kernel<kMXFP4, 1, GR, W, 2, 4><<<grid, block, 0, st>>>(a)    \
+                : MOE_GEMV4(1, GR))
+#define MOE_GEMV_SPLIT(GR)                                                         \
+    (split == 4   ? gemv_kernel<kFP8, 1, GR, W, 4, 2><<<grid, block, 0, st>>>(a)    \
+     : split == 2 ? gemv_kernel<kFP8, 1, GR, W, 2, 2><<<grid, block, 0, st>>>(a)    \
+                  : gemv_kernel<kFP8, 1, GR, W, 1, 2><<<grid, block, 0, st>>>(a))
     const bool g = a.offsets != nullptr;
     if (phase == 1) {
         if (a.fp8) g ? MOE_GEMV_SPLIT(true) : MOE_GEMV_SPLIT(false);
-        else if (a.fp4) g ? MOE_GEMV(kMXFP4, 1, true) : MOE_GEMV(kMXFP4, 1, false);
+        else if (a.fp4) g ? MOE_GEMV4_SPLIT(true) : MOE_GEMV4_SPLIT(false);
         else g ? MOE_GEMV(kBF16, 1, true) : MOE_GEMV(kBF16, 1, false);
     } else {
         if (a.fp8) g ? MOE_GEMV(kFP8, 2, true) : MOE_GEMV(kFP8, 2, false);
-        else if (a.fp4) g ? MOE_GEMV(kMXFP4, 2, true) : MOE_GEMV(kMXFP4, 2, false);
+        else if (a.fp4) g ? MOE_GEMV4(2, true) : MOE_GEMV4(2, false);
         else g ? MOE_GEMV(kBF16, 2, true) : MOE_GEMV(kBF16, 2, false);
     }
 #undef MOE_GEMV
+#undef MOE_GEMV4
+#undef MOE_GEMV4_SPLIT
 #undef MOE_GEMV_SPLIT
     return launch_status();
 }
