@@ -110,6 +110,13 @@ typedef struct {
 moe_status moe_route(const float* scores, int32_t T, int32_t E, int32_t k, int32_t score_fn,
                      int32_t renorm, int32_t* topk_ids, float* topk_w, void* stream);
 
+/* Bytes of device workspace moe_permute needs for T*k assignments over E experts (host output):
+ * 0 up to 2048 assignments (one workgroup groups them), else a count table of
+ * ceil(T*k / 2048) x E int32 (one row per block of 2048 consecutive assignments).
+ * Errors: INVALID_ARG for a null `bytes`, T < 0, k < 1, E < 1; UNSUPPORTED for E >
+ * MOE_MAX_EXPERTS or T*k >= 2^31. */
+moe_status moe_permute_workspace_size(int32_t T, int32_t k, int32_t E, size_t* bytes);
+
 /* Grouping of the T*k assignments by expert [OSDI DSLP section "sorting"; KT 2.2].
  *   topk_ids : int32 [T][k], each row k distinct ids in [0, E) (as moe_route writes them).
  *   counts   : int32 [E] out, number of assignments per expert.
@@ -117,14 +124,21 @@ moe_status moe_route(const float* scores, int32_t T, int32_t E, int32_t k, int32
  *   perm     : int32 [T*k] out, perm[p] = flat index t*k+j of the p-th assignment in expert
  *              order; stable: within one expert the flat indices ascend (so do the tokens).
  *   inv      : int32 [T*k] out, inv[perm[p]] = p.
+ *   ws       : device workspace of ws_bytes >= moe_permute_workspace_size(T, k, E) bytes,
+ *              16-byte aligned, owned by the caller (may be NULL when that size is 0).  Its
+ *              contents on entry do not matter and are undefined after the call; it must not
+ *              be used by other work until the enqueued launches complete.
  * The result is unique and deterministic (no atomics decide an order).  Above 2048 assignments
- * the call is four launches and uses inv as its scratch until the last one writes it.  Ids
- * outside [0, E) are a precondition violation: they are skipped (not counted), and the perm
- * entries past offsets[E] and the inv entries of the skipped assignments are unspecified.
+ * the call is four launches over blocks of 2048 assignments: per-block expert counts into the
+ * workspace, one scan of them, per-block stable placement, the inverse.  Ids outside [0, E) are
+ * a precondition violation: they are skipped (not counted), and the perm entries past
+ * offsets[E] and the inv entries of the skipped assignments are unspecified.
  * Limits: E <= MOE_MAX_EXPERTS, T*k < 2^31.  Errors: INVALID_ARG for null pointers, T < 0,
- * k < 1, E < 1. */
+ * k < 1, E < 1, an unaligned ws; WORKSPACE when ws is NULL or ws_bytes is below the queried
+ * size. */
 moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
-                       int32_t* offsets, int32_t* perm, int32_t* inv, void* stream);
+                       int32_t* offsets, int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* moe_route followed by moe_permute in one launch, for decode-sized batches (T*k <= 2048): the
  * same outputs, bit for bit, as the two calls [A2 4.1 and OSDI DSLP "gating + sorting"]; one

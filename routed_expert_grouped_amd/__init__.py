@@ -21,7 +21,7 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_W_FP8_E4M3_B128, MOE_W_BF16, MOE_W_MXFP4_G32 = 0, 1, 2
 SCORE_FN = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
 
-EXPORTS = ("moe_route", "moe_permute", "moe_expert_gate_up", "moe_expert_down",
+EXPORTS = ("moe_route", "moe_permute_workspace_size", "moe_permute", "moe_expert_gate_up", "moe_expert_down",
            "moe_expert_gate_up_shared", "moe_expert_down_shared",
            "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine", "moe_quantize_act",
            "moe_expert_gate_up_a8", "moe_expert_down_a8", "moe_expert_ffn_a8_workspace_size",
@@ -56,7 +56,8 @@ def lib():
         P, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
         W = ctypes.POINTER(MoeExpertWeights)
         L.moe_route.argtypes = [P, i32, i32, i32, i32, i32, P, P, P]
-        L.moe_permute.argtypes = [P, i32, i32, i32, P, P, P, P, P]
+        L.moe_permute_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_permute.argtypes = [P, i32, i32, i32, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_route_permute.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.moe_expert_gate_up.argtypes = [P, i32, i32, P, P, W, P, P]
         L.moe_expert_down.argtypes = [P, i32, i32, P, W, P, P]
@@ -162,15 +163,30 @@ def moe_route_permute(scores, k: int, score_fn="sigmoid", renorm: int = 1, topk_
     return topk_ids, topk_w, counts, offsets, perm, inv
 
 
-def moe_permute(topk_ids, E: int, counts=None, offsets=None, perm=None, inv=None, stream=None):
+def moe_permute_workspace_size(T: int, k: int, E: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_permute_workspace_size",
+           lib().moe_permute_workspace_size(T, k, E, ctypes.byref(n)))
+    return n.value
+
+
+def moe_permute(topk_ids, E: int, counts=None, offsets=None, perm=None, inv=None, ws=None,
+                stream=None):
+    """Returns counts, offsets, perm, inv.  `ws` (uint8 device tensor) is the call's workspace;
+    None allocates one of moe_permute_workspace_size bytes (the caller must keep a passed one
+    untouched until the stream has run the call)."""
     T, k = topk_ids.shape
     dev = topk_ids.device
     counts = torch.empty(E, dtype=torch.int32, device=dev) if counts is None else counts
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
     perm = torch.empty(T * k, dtype=torch.int32, device=dev) if perm is None else perm
     inv = torch.empty(T * k, dtype=torch.int32, device=dev) if inv is None else inv
+    if ws is None:
+        need = moe_permute_workspace_size(T, k, E)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
     _check("moe_permute", lib().moe_permute(_p(topk_ids), T, k, E, _p(counts), _p(offsets),
-                                            _p(perm), _p(inv), _s(stream)))
+                                            _p(perm), _p(inv), _p(ws),
+                                            0 if ws is None else ws.numel(), _s(stream)))
     return counts, offsets, perm, inv
 
 
@@ -313,6 +329,12 @@ def moe_expert_ffn_a8(x, k: int, perm, offsets, w: MoeExpertWeights, y=None, ws=
     return y, ws
 
 
+def _permute_ws(T, k, E, device):
+    """moe_permute's workspace for T tokens (a 16-byte stand-in when none is needed)."""
+    return torch.empty(max(16, moe_permute_workspace_size(T, k, E)), dtype=torch.uint8,
+                       device=device)
+
+
 class MoeLayer:
     """Buffers and the call sequence of one MoE layer forward: route -> permute (one launch,
     moe_route_permute, for T*k <= 2048) -> routed gate/up -> routed down -> combine on the
@@ -357,6 +379,7 @@ class MoeLayer:
         self.offsets = torch.empty(E + 1, dtype=i32, device=d)
         self.perm = torch.empty(max(1, T * k), dtype=i32, device=d)
         self.inv = torch.empty(max(1, T * k), dtype=i32, device=d)
+        self.perm_ws = _permute_ws(T, k, E, d)
         if act == "fp8":
             self.ws = torch.empty(max(1, moe_expert_ffn_a8_workspace_size(T, k, self.w)),
                                   dtype=torch.uint8, device=d)
@@ -417,7 +440,7 @@ class MoeLayer:
         else:
             moe_route(scores, k, self.score_fn, self.renorm, self.topk_ids, self.topk_w, stream)
             moe_permute(self.topk_ids, self.E, self.counts, self.offsets, self.perm, self.inv,
-                        stream)
+                        self.perm_ws, stream)
 
     def _shared(self, x, st):
         if self.act == "fp8":
@@ -498,6 +521,7 @@ class MoeRankShare:
         self.offsets = torch.empty(E + 1, dtype=i32, device=d)
         self.perm = torch.empty(max(1, T * k), dtype=i32, device=d)
         self.inv = torch.empty(max(1, T * k), dtype=i32, device=d)
+        self.perm_ws = _permute_ws(T, k, E, d)
         self.h = torch.empty((max(1, T * k), I), dtype=torch.int16, device=d)
         self.y = torch.empty((max(1, T * k), H), dtype=torch.int16, device=d)
         self.out = torch.empty((max(1, T), H), dtype=torch.int16, device=d)
@@ -513,7 +537,7 @@ class MoeRankShare:
         else:
             moe_route(scores, k, self.score_fn, self.renorm, self.topk_ids, self.topk_w, stream)
             moe_permute(self.topk_ids, self.E, self.counts, self.offsets, self.perm, self.inv,
-                        stream)
+                        self.perm_ws, stream)
         if self.w is not None:
             offs = self.offsets[self.e0:]  # the local experts' slice of the grouping
             if gate_up_events is not None:

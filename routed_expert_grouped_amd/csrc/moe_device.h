@@ -109,7 +109,9 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
 // close in that range run at about the same time on the same L2.
 //
 // An optional extra group (extra_rows > 0) follows the n_groups groups: its rows start at
-// offsets[n_groups] and it has extra_rows of them.
+// extra_base and it has extra_rows of them.  extra_base is passed in rather than read from
+// offsets[n_groups], so that a slice of the grouping (one expert range, whose offsets[n_groups]
+// ends before the last grouped row) still puts the extra rows after all grouped rows.
 //
 // Within a group, logical tiles go in supertiles of up to kSuperM m-tiles: the m-tiles of one
 // supertile are the fastest index, its n-tiles the next.  Workgroups that read the same weight
@@ -127,7 +129,7 @@ struct Tile {
 
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int n_groups,
                                           int identity_rows, int BM, int n_tiles, Tile& t,
-                                          int extra_rows = 0) {
+                                          int extra_rows = 0, int extra_base = 0) {
     const int lane = lane_id();
     const int wg = (int)blockIdx.x;
     int total_m, incl = 0, local = 0;
@@ -184,7 +186,7 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
         for (int i = 0; i < G; ++i) {
             const int g = lane * G + i;
             if (g >= groups) break;
-            const int a = offsets[g], n = count(g);
+            const int a = g < n_groups ? offsets[g] : extra_base, n = count(g);
             const int tiles = (n + BM - 1) / BM;
             if (mt < m0 + tiles) {
                 group = g;

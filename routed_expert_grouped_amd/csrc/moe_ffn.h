@@ -31,7 +31,8 @@ struct GemmArgs {
     const int8_t* aexp;
     int aexp_pitch;
     // An extra group after the n_groups experts (the shared expert in the routed decode launch;
-    // GEMV only): extra_rows rows starting at grouped row `rows` (= offsets[n_groups]), row
+    // GEMV only): extra_rows rows starting at grouped row `rows` (after every grouped row, also
+    // when offsets is a slice of one expert range), row
     // rows + t holding token t, with its own weights (one expert's matrices and scales).
     int extra_rows;
     const void* xw0;

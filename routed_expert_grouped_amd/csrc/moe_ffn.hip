@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
     Tile tile;
     const int n_tiles = a.N / kCols;
     if (!find_tile(kGrouped ? a.offsets : nullptr, a.n_groups, a.rows, kGemvBM, n_tiles, tile,
-                   kGrouped ? a.extra_rows : 0))
+                   kGrouped ? a.extra_rows : 0, a.rows))
         return;
 
     const int lane = lane_id(), wave = uniform((int)(threadIdx.x >> 6));

@@ -17,9 +17,9 @@
 //           base + (lower peers in its chunk), and perm[slot] = its flat index;
 //   invert  inv[perm[p]] = p.
 // The result is the stable order by construction (ascending flat index within each expert).
-// The table lives in `inv` until the last launch overwrites it.  With B = ceil(n / kBlockN)
-// blocks it holds B * E <= n / 2 + E ints (kBlockN >= 2 * E), which is at most n for every
-// n >= 2 * E, so for every n > kSmallN = 2048 >= 2 * MOE_MAX_EXPERTS.
+// The table, B = ceil(n / kBlockN) rows of E ints, is the caller's workspace
+// (moe_permute_workspace_size); every entry is written by the hist launch before it is read, so
+// the workspace needs no clearing.
 // Up to kBlockThreads (1024) assignments one workgroup places them all at once, one a thread,
 // and up to kSmallN one wave walks them in order (both in moe_permute.h).
 #include "libmoe.h"
@@ -34,7 +34,6 @@ constexpr int kBlockChunks = 32;                 // 64-assignment chunks per blo
 constexpr int kBlockN = kBlockChunks * kWave;    // 2048 assignments per block
 constexpr int kWaveChunks = kBlockChunks / kPlaceWaves;
 constexpr int kHistThreads = 256;
-static_assert(kBlockN >= 2 * MOE_MAX_EXPERTS, "the per-block count table fits in inv");
 
 __global__ __launch_bounds__(kHistThreads) void permute_hist_kernel(const int32_t* __restrict__ ids,
                                                                     int n, int E,
@@ -183,18 +182,32 @@ __global__ __launch_bounds__(kWave) void permute_small_kernel(
     permute_wave(ids, n, E, nbits, cnt, counts, offsets, perm, inv);
 }
 
+// Bytes of the count table [B][E] for n assignments (0 when one workgroup groups them all).
+static size_t permute_table_bytes(int64_t n, int E) {
+    if (n <= kSmallN) return 0;
+    const int64_t B = (n + kBlockN - 1) / kBlockN;
+    return (size_t)B * (size_t)E * sizeof(int32_t);
+}
+
+static moe_status check_permute_sizes(int32_t T, int32_t k, int32_t E) {
+    if (T < 0 || k < 1 || E < 1) return MOE_ERR_INVALID_ARG;
+    if (E > MOE_MAX_EXPERTS || (int64_t)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
 static moe_status check_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                          const int32_t* counts, const int32_t* offsets, const int32_t* perm,
                          const int32_t* inv) {
-    if (T < 0 || k < 1 || E < 1) return MOE_ERR_INVALID_ARG;
-    if (E > MOE_MAX_EXPERTS || (int64_t)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
-    if (T == 0) return MOE_OK;
+    const moe_status s = check_permute_sizes(T, k, E);
+    if (s != MOE_OK || T == 0) return s;
     if (!topk_ids || !counts || !offsets || !perm || !inv) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
+// `table` holds permute_table_bytes(T * k, E) bytes (unused, may be NULL, up to kSmallN).
 static moe_status launch_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
-                          int32_t* offsets, int32_t* perm, int32_t* inv, hipStream_t st) {
+                          int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* table,
+                          hipStream_t st) {
     const int n = T * k;
     const int nbits = ceil_log2(E) > 0 ? ceil_log2(E) : 1;
     if (n <= kBlockThreads) {
@@ -208,7 +221,6 @@ static moe_status launch_permute(const int32_t* topk_ids, int32_t T, int32_t k, 
         return launch_status();
     }
     const int B = (int)(((int64_t)n + kBlockN - 1) / kBlockN);
-    int32_t* table = inv;  // [B][E], overwritten by the last launch
     permute_hist_kernel<<<dim3(B), dim3(kHistThreads), 0, st>>>(topk_ids, n, E, table);
     permute_scan_kernel<<<dim3(1), dim3(1024), 0, st>>>(table, B, E, counts, offsets);
     permute_place_kernel<<<dim3(B), dim3(kPlaceWaves * kWave), 0, st>>>(topk_ids, n, E, nbits,
@@ -222,10 +234,22 @@ static moe_status launch_permute(const int32_t* topk_ids, int32_t T, int32_t k, 
 
 using namespace moe;
 
+extern "C" moe_status moe_permute_workspace_size(int32_t T, int32_t k, int32_t E, size_t* bytes) {
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    const moe_status s = check_permute_sizes(T, k, E);
+    if (s != MOE_OK) return s;
+    *bytes = permute_table_bytes((int64_t)T * k, E);
+    return MOE_OK;
+}
+
 extern "C" moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                                   int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                                  void* stream) {
+                                  void* ws, size_t ws_bytes, void* stream) {
     const moe_status s = check_permute(topk_ids, T, k, E, counts, offsets, perm, inv);
     if (s != MOE_OK || T == 0) return s;
-    return launch_permute(topk_ids, T, k, E, counts, offsets, perm, inv, as_stream(stream));
+    const size_t need = permute_table_bytes((int64_t)T * k, E);
+    if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(ws)) return MOE_ERR_INVALID_ARG;
+    return launch_permute(topk_ids, T, k, E, counts, offsets, perm, inv,
+                          static_cast<int32_t*>(ws), as_stream(stream));
 }

@@ -1,10 +1,15 @@
 """The C-ABI library loads, exports every declared entry point, and rejects bad arguments on the
-host before anything is enqueued (no GPU needed: no call here reaches a kernel launch)."""
+host before anything is enqueued (no GPU needed: no call here reaches a kernel launch).
+
+The validation tests pass a fake device address that no call may dereference.  They run only
+where no GPU is visible: there a validation bug cannot turn into a device fault, and the same
+bug fails the test instead (the pointer is never mapped)."""
 import ctypes
 import os
 import re
 
 import pytest
+import torch
 
 import routed_expert_grouped_amd as moe
 
@@ -12,6 +17,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "libmoe.h")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH), reason="libmoe.so not built")
+
+# counting devices does not initialise the runtime
+cpu_only = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                              reason="fake device pointers: run only where no GPU is visible")
 
 # A non-null, 16-byte aligned address that is never dereferenced by the calls below: each of
 # them fails validation (or has T == 0) before any device work is enqueued.
@@ -46,6 +55,7 @@ def _w(dtype=0, n=4, H=256, I=128, ptr=FAKE, scales=True):
                                 s.value if s else None)
 
 
+@cpu_only
 def test_route_validation():
     L = moe.lib()
     st = None
@@ -59,16 +69,57 @@ def test_route_validation():
     assert L.moe_route(FAKE, 0, 8, 2, 0, 1, FAKE, FAKE, st) == moe.MOE_OK  # T == 0: no-op
 
 
+@cpu_only
 def test_permute_validation():
     L = moe.lib()
-    assert L.moe_permute(None, 4, 2, 8, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_permute(FAKE, 4, 0, 8, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_permute(FAKE, 4, 2, 0, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_permute(FAKE, 4, 2, 1025, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
-    assert L.moe_permute(FAKE, 1 << 28, 16, 8, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
-    assert L.moe_permute(FAKE, 0, 2, 8, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_OK
+    P = L.moe_permute
+    assert P(None, 4, 2, 8, FAKE, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert P(FAKE, 4, 0, 8, FAKE, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert P(FAKE, 4, 2, 0, FAKE, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert P(FAKE, 4, 2, 8, FAKE, FAKE, None, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert P(FAKE, 4, 2, 1025, FAKE, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_UNSUPPORTED
+    assert P(FAKE, 1 << 28, 16, 8, FAKE, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_UNSUPPORTED
+    assert P(FAKE, 0, 2, 8, FAKE, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_OK
 
 
+def _permute_ws(T, k, E):
+    n = ctypes.c_size_t(12345)
+    st = moe.lib().moe_permute_workspace_size(T, k, E, ctypes.byref(n))
+    return st, n.value
+
+
+def test_permute_workspace_size():
+    """No workspace up to 2048 assignments; above, one int32 count per (block of 2048, expert)."""
+    assert _permute_ws(16, 8, 256) == (moe.MOE_OK, 0)
+    assert _permute_ws(256, 8, 256) == (moe.MOE_OK, 0)        # 2048 assignments
+    assert _permute_ws(2049, 1, 256) == (moe.MOE_OK, 2 * 256 * 4)
+    assert _permute_ws(4096, 8, 256) == (moe.MOE_OK, 16 * 256 * 4)
+    assert _permute_ws(32768, 8, 256) == (moe.MOE_OK, 128 * 256 * 4)
+    assert _permute_ws(8192, 8, 384) == (moe.MOE_OK, 32 * 384 * 4)
+    assert _permute_ws(0, 8, 256) == (moe.MOE_OK, 0)
+    assert _permute_ws(-1, 8, 256)[0] == moe.MOE_ERR_INVALID_ARG
+    assert _permute_ws(4, 0, 256)[0] == moe.MOE_ERR_INVALID_ARG
+    assert _permute_ws(4, 2, 0)[0] == moe.MOE_ERR_INVALID_ARG
+    assert _permute_ws(4, 2, 1025)[0] == moe.MOE_ERR_UNSUPPORTED
+    assert _permute_ws(1 << 28, 16, 8)[0] == moe.MOE_ERR_UNSUPPORTED
+    assert moe.lib().moe_permute_workspace_size(4, 2, 8, None) == moe.MOE_ERR_INVALID_ARG
+
+
+@cpu_only
+def test_permute_workspace_errors():
+    """Above 2048 assignments a missing or short workspace is MOE_ERR_WORKSPACE and an unaligned
+    one INVALID_ARG, before anything is enqueued; up to 2048 none is needed."""
+    P = moe.lib().moe_permute
+    _, need = _permute_ws(4096, 8, 256)
+    assert P(FAKE, 4096, 8, 256, FAKE, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_WORKSPACE
+    assert P(FAKE, 4096, 8, 256, FAKE, FAKE, FAKE, FAKE, None, need, None) == moe.MOE_ERR_WORKSPACE
+    assert P(FAKE, 4096, 8, 256, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+             None) == moe.MOE_ERR_WORKSPACE
+    assert P(FAKE, 4096, 8, 256, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1004), need,
+             None) == moe.MOE_ERR_INVALID_ARG
+
+
+@cpu_only
 def test_expert_validation():
     L = moe.lib()
     gu, dn = L.moe_expert_gate_up, L.moe_expert_down
@@ -105,6 +156,7 @@ def test_expert_validation():
     assert dn(FAKE, 0, 2, FAKE, ctypes.byref(ok), FAKE, None) == moe.MOE_OK
 
 
+@cpu_only
 def test_shared_expert_calls_validation():
     """moe_expert_gate_up_shared / moe_expert_down_shared: the shared expert must be one expert
     of the routed experts' dtype and shape; perm and offsets are required."""
@@ -130,6 +182,7 @@ def test_shared_expert_calls_validation():
     assert dn(FAKE, 0, 2, FAKE, ctypes.byref(w), ctypes.byref(ws), FAKE, None) == moe.MOE_OK
 
 
+@cpu_only
 def test_ffn_workspace():
     L = moe.lib()
     w = _w()
@@ -144,6 +197,7 @@ def test_ffn_workspace():
     assert L.moe_expert_ffn(FAKE, 0, 2, FAKE, FAKE, ctypes.byref(w), FAKE, None, 0, None) == moe.MOE_OK
 
 
+@cpu_only
 def test_quantize_act_validation():
     q = moe.lib().moe_quantize_act
     assert q(None, 4, 256, FAKE, FAKE, 2, None) == moe.MOE_ERR_INVALID_ARG
@@ -159,6 +213,7 @@ def test_quantize_act_validation():
     assert moe.exp_pitch(7168) == 64 and moe.exp_pitch(2048) == 16 and moe.exp_pitch(640) == 16
 
 
+@cpu_only
 def test_route_permute_validation():
     L = moe.lib()
     f = L.moe_route_permute
@@ -172,6 +227,7 @@ def test_route_permute_validation():
     assert f(None, 0, 256, 8, 1, 1, None, None, None, None, None, None, None) == moe.MOE_OK
 
 
+@cpu_only
 def test_combine_partial_validation():
     L = moe.lib()
     f = L.moe_combine_partial
@@ -182,6 +238,7 @@ def test_combine_partial_validation():
     assert f(None, None, None, None, 0, 8, None, 0, 2, 256, None, None) == moe.MOE_OK
 
 
+@cpu_only
 def test_a8_phase_validation():
     L = moe.lib()
     gu, dn = L.moe_expert_gate_up_a8, L.moe_expert_down_a8
@@ -209,6 +266,7 @@ def test_a8_phase_validation():
     assert dn(None, None, 0, 0, 2, None, None, None, None) == moe.MOE_OK
 
 
+@cpu_only
 def test_ffn_a8_validation():
     L = moe.lib()
     w = _w(H=256, I=384)
@@ -244,6 +302,7 @@ def test_ffn_a8_validation():
     assert f(None, 0, 2, None, None, None, None, None, 0, None) == moe.MOE_OK
 
 
+@cpu_only
 def test_combine_validation():
     L = moe.lib()
     c = L.moe_combine
