@@ -75,6 +75,14 @@ def lib():
         L.oracle_expert_down.argtypes = [P, i32, P, ctypes.POINTER(_Weights), P, i32]
         L.oracle_max_threads.restype = i32
         L.oracle_max_threads.argtypes = [i32]
+        L.oracle_dequantize.restype = i32
+        L.oracle_dequantize.argtypes = [ctypes.POINTER(_Weights), i32, i32, P, i32]
+        L.oracle_silu_mul_bf16.restype = None
+        L.oracle_silu_mul_bf16.argtypes = [P, P, ctypes.c_long, P]
+        L.oracle_double_to_bf16_array.restype = None
+        L.oracle_double_to_bf16_array.argtypes = [P, ctypes.c_long, P]
+        L.oracle_quantize_dequantize.restype = None
+        L.oracle_quantize_dequantize.argtypes = [P, ctypes.c_long, i32]
         _lib = L
     return _lib
 
@@ -256,3 +264,142 @@ def bf16_bits_to_float(a) -> np.ndarray:
     """uint16 bf16 bit patterns -> float64 (host numpy)."""
     a = _np(a, np.uint16)
     return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------------ batched form
+
+
+def dequantize(ew, which: int, n_threads: int = 0) -> np.ndarray:
+    """Matrix `which` (0 gate [I, H], 1 up [I, H], 2 down [H, I]) of the single expert in `ew`
+    (an ExpertWeights-like object holding one expert), dequantised exactly into float64."""
+    keep = []
+    W = _weights(ew, keep)
+    if W.n != 1:
+        raise ValueError("dequantize takes one expert")
+    rows, cols = (W.H, W.I) if which == 2 else (W.I, W.H)
+    out = np.empty((rows, cols), np.float64)
+    if lib().oracle_dequantize(ctypes.byref(W), 0, int(which), _ptr(out), int(n_threads)):
+        raise ValueError("oracle_dequantize: invalid arguments")
+    return out
+
+
+def silu_mul_bf16(g, u) -> np.ndarray:
+    """bf16 bits of SiLU(g) * u element-wise (g, u float64 arrays of one shape)."""
+    g = np.ascontiguousarray(g, np.float64)
+    u = np.ascontiguousarray(u, np.float64)
+    h = np.empty(g.shape, np.uint16)
+    lib().oracle_silu_mul_bf16(_ptr(g), _ptr(u), g.size, _ptr(h))
+    return h
+
+
+def double_to_bf16_array(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib().oracle_double_to_bf16_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def quantize_dequantize(v) -> np.ndarray:
+    """The FP8 activation mode's 1x128 quantisation of rows of values (float64 [rows, K], each
+    exact in fp32), returned dequantised (a new array)."""
+    v = np.array(v, np.float64, copy=True, order="C")
+    lib().oracle_quantize_dequantize(_ptr(v), v.shape[0], v.shape[1])
+    return v
+
+
+def _expert_on_rows(ew, X, act_fp8, n_threads):
+    """One expert on activation rows X (float64 [n, H], already quantised in the FP8 mode):
+    returns (h bf16 bits [n, I], y float64 [n, H]).  g = X Wg^T, u = X Wu^T and y = h Wd^T are
+    float64 matrix products (the library's summation order instead of the plain loop's); the
+    activation, its bf16 rounding and the FP8 mode's quantisation of h are the oracle's own."""
+    Wg = dequantize(ew, 0, n_threads)
+    G = X @ Wg.T
+    del Wg
+    Wu = dequantize(ew, 1, n_threads)
+    U = X @ Wu.T
+    del Wu
+    hb = silu_mul_bf16(G, U)
+    del G, U
+    Hd = bf16_bits_to_float(hb)
+    if act_fp8:
+        Hd = quantize_dequantize(Hd)
+    Wd = dequantize(ew, 2, n_threads)
+    Y = Hd @ Wd.T
+    return hb, Y
+
+
+def moe_layer_batched(layer, rows=None, with_shared=True, want_h=False, want_y=False,
+                      n_threads: int = 0, act_fp8: bool = False, expert_range=None):
+    """The layer of moe_layer() for token rows `rows`, evaluated expert by expert: every expert
+    that the rows select runs once over all of its (token, slot) assignments, found by scanning
+    the rows' ids (no grouping is taken from anywhere), with its weights dequantised once and
+    float64 matrix products for the sums.  Same definition, same roundings (h to bf16, out to
+    bf16 from S + sum_j w_j y_j accumulated in double in that order) and same return dict as
+    moe_layer(); only the order of the float64 sums inside the products differs.  This makes
+    full-size layers cheap enough to check on every row."""
+    T, E, H, I, k = layer.T, layer.E, layer.H, layer.I, layer.k
+    r = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    n = len(r)
+    scores = _np(layer.scores, np.float32)[r]
+    ids, w = route(scores, k, layer.score_fn, layer.renorm)
+    xb = _np(layer.x, np.uint16)[r]
+    X = bf16_bits_to_float(xb)
+    if act_fp8:
+        X = quantize_dequantize(X)
+    e0, e1 = (0, E) if expert_range is None else map(int, expert_range)
+    y = np.zeros((n, k, H), np.float64)
+    h = np.zeros((n, k, I), np.uint16) if want_h else None
+    for e in np.unique(ids):
+        if not e0 <= e < e1:
+            continue
+        ti, tj = np.nonzero(ids == e)  # the assignments (row, slot) that select expert e
+        hb, Y = _expert_on_rows(layer.experts.select([int(e)]), X[ti], act_fp8, n_threads)
+        y[ti, tj] = Y
+        if want_h:
+            h[ti, tj] = hb
+    S = np.zeros((n, H), np.float64)
+    hS = None
+    if with_shared:
+        hS, S = _expert_on_rows(layer.shared.select([0]), X, act_fp8, n_threads)
+    acc = S.copy()
+    wd = w.astype(np.float64)
+    for j in range(k):
+        local = (ids[:, j] >= e0) & (ids[:, j] < e1)
+        acc += np.where(local, wd[:, j], 0.0)[:, None] * y[:, j]
+    res = dict(ids=ids, w=w, out=double_to_bf16_array(acc))
+    if want_h:
+        res["h"] = h
+        if with_shared:
+            res["hS"] = hS
+    if want_y:
+        res["y"] = y
+        res["S"] = S
+    return res
+
+
+def expert_gate_up_batched(x, token, slot, experts, n_threads: int = 0):
+    """expert_gate_up() evaluated slot by slot (each slot's rows together, float64 library
+    products); same definition and rounding."""
+    xb = _np(x, np.uint16)
+    tok, sl = np.asarray(token, np.int64), np.asarray(slot, np.int64)
+    h = np.zeros((len(tok), experts.gate.shape[1]), np.uint16)
+    for e in np.unique(sl):
+        p = np.nonzero(sl == e)[0]
+        one = experts.select([int(e)])
+        X = bf16_bits_to_float(xb[tok[p]])
+        G = X @ dequantize(one, 0, n_threads).T
+        U = X @ dequantize(one, 1, n_threads).T
+        h[p] = silu_mul_bf16(G, U)
+    return h
+
+
+def expert_down_batched(h, slot, experts, n_threads: int = 0):
+    """expert_down() evaluated slot by slot; same definition (y = Wd h in float64)."""
+    hb = _np(h, np.uint16)
+    sl = np.asarray(slot, np.int64)
+    H = experts.down.shape[1]
+    y = np.zeros((len(sl), H), np.float64)
+    for e in np.unique(sl):
+        p = np.nonzero(sl == e)[0]
+        y[p] = bf16_bits_to_float(hb[p]) @ dequantize(experts.select([int(e)]), 2, n_threads).T
+    return y

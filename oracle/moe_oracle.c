@@ -283,6 +283,12 @@ static double weight(const oracle_weights* W, const void* mat, const float* sc, 
     return fp8_table[((const uint8_t*)mat)[at]] * scale;
 }
 
+/* The activated product of one output column: bf16( SiLU(g) * u ), SiLU(g) = g / (1 + e^-g)
+ * (the article's "CPU fine-grained parallelism" section: activation of gate, times up). */
+static uint16_t silu_mul_bf16(double g, double u) {
+    return oracle_double_to_bf16(g / (1.0 + exp(-g)) * u);
+}
+
 /* Gate and up of expert slot x on the activations xd (length H, double):
  * h[n] = bf16(SiLU(g_n) * u_n) with g = Wg x, u = Wu x.  Writes the bf16 bits to h_out (if not
  * NULL) and their values to hd. */
@@ -295,8 +301,7 @@ static void gate_up_row(const oracle_weights* W, int x, const double* xd, uint16
             g += xd[c] * weight(W, W->gate, W->s_gate, x, I, H, n, c);
             u += xd[c] * weight(W, W->up, W->s_up, x, I, H, n, c);
         }
-        double a = g / (1.0 + exp(-g)) * u;
-        uint16_t hb = oracle_double_to_bf16(a);
+        uint16_t hb = silu_mul_bf16(g, u);
         if (h_out) h_out[n] = hb;
         hd[n] = oracle_bf16_to_double(hb);
     }
@@ -471,4 +476,45 @@ int oracle_max_threads(int n_threads) {
     (void)n_threads;
     return 1;
 #endif
+}
+
+/* ---------------------------------------------------------------- batched form ------------
+ * The pieces of the same definition for an evaluation that takes each expert's tokens
+ * together: the expert's matrices dequantised once (exact doubles), and the element-wise steps
+ * over whole arrays.  The sums themselves are formed by a library float64 matrix product; every
+ * other step is the code above. */
+
+/* Matrix `which` (0 gate, 1 up, 2 down) of expert slot x, dequantised into out, row-major
+ * [rows][cols] = [I][H] (gate, up) or [H][I] (down). */
+int oracle_dequantize(const oracle_weights* W, int x, int which, double* out, int n_threads) {
+    if (x < 0 || x >= W->n || which < 0 || which > 2) return ORACLE_ERR;
+    fill_fp8_table();
+    const void* mat = which == 0 ? W->gate : which == 1 ? W->up : W->down;
+    const float* sc = which == 0 ? W->s_gate : which == 1 ? W->s_up : W->s_down;
+    const int rows = which == 2 ? W->H : W->I, cols = which == 2 ? W->I : W->H;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int r = 0; r < rows; ++r)
+        for (int c = 0; c < cols; ++c)
+            out[(size_t)r * cols + c] = weight(W, mat, sc, x, rows, cols, r, c);
+    return ORACLE_OK;
+}
+
+/* h[i] = bf16( SiLU(g[i]) * u[i] ) for n values. */
+void oracle_silu_mul_bf16(const double* g, const double* u, long n, uint16_t* h) {
+    for (long i = 0; i < n; ++i) h[i] = silu_mul_bf16(g[i], u[i]);
+}
+
+/* bf16 bits of n doubles (round to nearest even, one step). */
+void oracle_double_to_bf16_array(const double* v, long n, uint16_t* out) {
+    for (long i = 0; i < n; ++i) out[i] = oracle_double_to_bf16(v[i]);
+}
+
+/* The FP8 activation mode's quantisation applied in place to rows of values [rows][K] (exact in
+ * fp32, K a multiple of 128): each 128-block replaced by its dequantised E4M3FN codes. */
+void oracle_quantize_dequantize(double* v, long rows, int K) {
+    for (long r = 0; r < rows; ++r)
+        for (int b = 0; b < K / 128; ++b) quantize_block(v + r * K + b * 128, 128, NULL);
 }

@@ -226,8 +226,9 @@ def _dense_brute_force(layer, ids, w, act_fp8=False):
     return acc, np.stack(hs, 1), np.stack(ys, 1), S, hS
 
 
-def _check_layer_against_dense(layer, act_fp8=False):
-    res = oracle.moe_layer(layer, want_h=True, want_y=True, act_fp8=act_fp8)
+def _check_layer_against_dense(layer, act_fp8=False, fn=None):
+    fn = oracle.moe_layer if fn is None else fn
+    res = fn(layer, want_h=True, want_y=True, act_fp8=act_fp8)
     acc, hs, ys, S, hS = _dense_brute_force(layer, res["ids"], res["w"], act_fp8)
     T = layer.T
     y_sel = ys[np.arange(T)[:, None], res["ids"]]  # [T, k, H]
@@ -557,3 +558,93 @@ def test_ffn_mxfp4_fp8_activations_dense_brute_force():
     res = _check_layer_against_dense(layer, act_fp8=True)
     plain = oracle.moe_layer(layer, act_fp8=False)
     assert np.any(plain["out"] != res["out"])
+
+
+# ----------------------------------------------------------------------------- batched form
+# oracle.moe_layer_batched evaluates the same definition expert by expert with float64 library
+# matrix products (what makes the full-size layers cheap to check on every row).  It is pinned
+# like the per-token form: against the dense brute force in every weight and activation mode,
+# and against the per-token form itself up to the order of the float64 sums.
+
+_MID = dict(T=24, H=384, I=256, E=6, k=3, score_fn="sigmoid", scores="uniform")
+
+
+@pytest.mark.parametrize("cfg,act_fp8", [
+    ("tiny", False), ("tiny_fp8", False),
+    (dict(_MID, wdtype="fp8"), True),
+    (dict(_MID, T=24, H=256, I=128, k=2, wdtype="mxfp4"), False),
+    (dict(_MID, wdtype="mxfp4"), True)])
+def test_batched_form_dense_brute_force(cfg, act_fp8):
+    layer = synth.make_layer(cfg, seed=4)
+    _check_layer_against_dense(layer, act_fp8=act_fp8, fn=oracle.moe_layer_batched)
+
+
+def test_batched_form_rectangular_scale_grid():
+    layer = synth.make_layer(dict(_MID, wdtype="fp8"), seed=3)
+    g = torch.Generator().manual_seed(5)
+    for ew in (layer.experts, layer.shared):
+        for s in (ew.s_gate, ew.s_up, ew.s_down):
+            s.mul_(torch.rand(s.shape, generator=g) * 4 + 0.25)
+    _check_layer_against_dense(layer, fn=oracle.moe_layer_batched)
+
+
+@pytest.mark.parametrize("act_fp8", [False, True])
+def test_batched_form_agrees_with_per_token_form(act_fp8):
+    """Many tokens per expert, a row subset in a scrambled order, and an expert range: the two
+    forms route identically, give the same h bits except where the float64 sums land on the two
+    sides of a bf16 tie (never more than one ulp), and y and out to float64 rounding."""
+    layer = synth.make_layer(dict(T=96, H=384, I=256, E=8, k=3, score_fn="sigmoid",
+                                  scores="uniform", wdtype="fp8"), seed=7)
+    rows = np.random.default_rng(1).permutation(96)[:70]
+    for er in (None, (2, 6)):
+        a = oracle.moe_layer(layer, rows=rows, want_h=True, want_y=True, act_fp8=act_fp8,
+                             expert_range=er)
+        b = oracle.moe_layer_batched(layer, rows=rows, want_h=True, want_y=True,
+                                     act_fp8=act_fp8, expert_range=er)
+        np.testing.assert_array_equal(a["ids"], b["ids"])
+        np.testing.assert_array_equal(a["w"], b["w"])
+        for key in ("h", "hS"):
+            ha, hb = oracle.bf16_bits_to_float(a[key]), oracle.bf16_bits_to_float(b[key])
+            assert np.mean(ha == hb) > 0.9999
+            np.testing.assert_allclose(hb, ha, rtol=2.0 ** -7, atol=0)
+        same = np.all(a["h"] == b["h"], axis=-1)
+        np.testing.assert_allclose(b["y"][same], a["y"][same], rtol=1e-9, atol=1e-13)
+        np.testing.assert_allclose(b["S"], a["S"], rtol=1e-9, atol=1e-13)
+        oa, ob = oracle.bf16_bits_to_float(a["out"]), oracle.bf16_bits_to_float(b["out"])
+        np.testing.assert_allclose(ob, oa, rtol=2.0 ** -7, atol=0)
+        assert np.mean(oa == ob) > 0.999
+        if er is not None:  # outside the range: nothing
+            local = (a["ids"] >= er[0]) & (a["ids"] < er[1])
+            assert not b["y"][~local].any() and not b["h"][~local].any()
+
+
+def test_batched_helpers():
+    """The element-wise pieces: dequantisation equals the FP8 code times its block's scale;
+    SiLU-times-up rounding and the double -> bf16 array rounding equal the scalar functions."""
+    layer = synth.make_layer(dict(_MID, wdtype="fp8"), seed=2)
+    one = layer.experts.select([3])
+    Wg, Wu, Wd = _dense_weights(one, layer.H, layer.I)
+    for which, ref in enumerate((Wg[0], Wu[0], Wd[0])):
+        np.testing.assert_array_equal(oracle.dequantize(one, which), ref)
+    rng = np.random.default_rng(3)
+    g, u = rng.standard_normal(500) * 4, rng.standard_normal(500)
+    h = oracle.silu_mul_bf16(g, u)
+    assert all(h[i] == oracle.double_to_bf16(g[i] / (1 + np.exp(-g[i])) * u[i]) for i in range(500))
+    v = rng.standard_normal(300) * np.exp2(rng.integers(-40, 40, 300))
+    assert list(oracle.double_to_bf16_array(v)) == [oracle.double_to_bf16(t) for t in v]
+
+
+@pytest.mark.parametrize("wdtype", ["fp8", "mxfp4"])
+def test_batched_phases_agree_with_per_row_phases(wdtype):
+    layer = synth.make_layer(dict(_MID, wdtype=wdtype), seed=5)
+    rng = np.random.default_rng(5)
+    token = rng.integers(0, layer.T, 80)
+    slot = rng.integers(0, layer.E, 80)
+    h = oracle.expert_gate_up(layer.x, token, slot, layer.experts)
+    hb = oracle.expert_gate_up_batched(layer.x, token, slot, layer.experts)
+    fa, fb = oracle.bf16_bits_to_float(h), oracle.bf16_bits_to_float(hb)
+    assert np.mean(fa == fb) > 0.999
+    np.testing.assert_allclose(fb, fa, rtol=2.0 ** -7, atol=0)
+    y = oracle.expert_down(h, slot, layer.experts)
+    yb = oracle.expert_down_batched(h, slot, layer.experts)
+    np.testing.assert_allclose(yb, y, rtol=1e-9, atol=1e-13)
