@@ -40,12 +40,57 @@ def mid(**over):
     return c
 
 
+GUARD = 4096  # bytes of sentinel before and after every output buffer of run_gpu
+SENTINEL = 0xA5
+
+
+def _guarded(L, name):
+    """Replace tensor attribute `name` of L by a view of the same shape inside a buffer with
+    GUARD sentinel bytes on both sides; returns the buffer."""
+    t = getattr(L, name)
+    nbytes = t.numel() * t.element_size()
+    buf = torch.full((nbytes + 2 * GUARD,), SENTINEL, dtype=torch.uint8, device=t.device)
+    setattr(L, name, buf[GUARD:GUARD + nbytes].view(t.dtype).view(t.shape))
+    return buf
+
+
+def _guard_layer(L):
+    """Guard every buffer the layer's calls write (and re-derive the views into them)."""
+    T, k, I = L.T, L.k, L.I
+    names = ["out", "topk_ids", "topk_w", "counts", "offsets", "perm", "inv", "perm_ws"]
+    if L.fused:
+        names += ["h_all", "y_all"]
+    elif L.act == "fp8":
+        names += ["ws", "y"] + (["sh_ws", "sh_y"] if L.sh_ws is not None else [])
+    else:
+        names += ["h", "y", "sh_h", "sh_y"]
+    bufs = {n: _guarded(L, n) for n in names}
+    if L.fused:
+        L.h, L.sh_h = L.h_all[:T * k], L.h_all[T * k:]
+        L.y, L.sh_y = L.y_all[:T * k], L.y_all[T * k:]
+    elif L.act == "fp8":
+        L.h = L.ws[:max(1, T * k) * I * 2].view(torch.int16).view(-1, I)
+        if L.sh_ws is not None:
+            L.sh_h = L.sh_ws[:max(1, T) * I * 2].view(torch.int16).view(-1, I)
+    return bufs
+
+
+def _check_guards(bufs):
+    for name, buf in bufs.items():
+        for side, part in (("before", buf[:GUARD]), ("after", buf[-GUARD:])):
+            bad = int((part != SENTINEL).sum())
+            assert bad == 0, f"{bad} guard bytes {side} {name} were overwritten"
+
+
 def run_gpu(layer, stream=None, act="bf16"):
-    """Run the full layer through the C ABI; return host copies of every intermediate."""
+    """Run the full layer through the C ABI; return host copies of every intermediate.  Every
+    buffer the calls write sits between sentinel bytes, which must be untouched afterwards."""
     L = moe.MoeLayer(layer.T, layer.H, layer.I, layer.E, layer.k, layer.experts, layer.shared,
                      layer.score_fn, layer.renorm, act=act)
+    bufs = _guard_layer(L)
     L.forward(layer.scores, layer.x, stream)
     torch.cuda.synchronize()
+    _check_guards(bufs)
     T, k = layer.T, layer.k
     c = lambda t: t.detach().cpu().numpy()
     return dict(ids=c(L.topk_ids), w=c(L.topk_w), counts=c(L.counts), offsets=c(L.offsets),
@@ -111,6 +156,57 @@ def a8_correction(ew, experts, h_gpu, h_ref, K):
     return out
 
 
+A8_MAX_DIFF_FRACTION = 5e-3  # of h positions whose quantised value differs between the sides
+
+
+def _ordered(bits):
+    """bf16 bit patterns -> integers ordered like the values (adjacent values differ by 1)."""
+    b = np.asarray(bits, np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+
+def _e4m3_spacing(v):
+    """Spacing of the E4M3FN grid at magnitudes v (float64, in units of the block scale):
+    2^(E-3) in the binade [2^E, 2^(E+1)), and 2^-9 below 2^-6 (the subnormals)."""
+    v = np.asarray(v, np.float64)
+    E = np.floor(np.log2(np.maximum(v, 2.0 ** -6)))
+    return np.exp2(E - 3)
+
+
+def check_a8_quantisation_steps(h_gpu, h_ref, K):
+    """Bounds on where and how far the two sides' quantised h may differ (the mechanism of the
+    layer comparison's correction).  Rounding to a grid is monotone, so two values a and b
+    round at most |a - b| plus one grid step apart, the step taken at the larger magnitude and on
+    the coarser of the two sides' grids (block exponents).  Asserted: every block whose exponent
+    differs has largest magnitudes at most one bf16 ulp apart; at every position,
+    |deq(h_gpu) - deq(h_ref)| <= |h_gpu - h_ref| + that step; and at most A8_MAX_DIFF_FRACTION
+    of the positions differ.  Returns (differing fraction, per-row budget: the norm over the
+    differing positions of |h_gpu - h_ref| + step, relative to the row's norm)."""
+    hg = np.asarray(h_gpu, np.uint16).reshape(-1, K)
+    hr = np.asarray(h_ref, np.uint16).reshape(-1, K)
+    eg, ag = block_exponents(hg, K)
+    er, ar = block_exponents(hr, K)
+    flip = eg != er  # [n, K/128]
+    assert np.all(np.abs(_ordered(ag[flip]) - _ordered(ar[flip])) <= 1), \
+        "a block exponent differs with block maxima more than one bf16 ulp apart"
+    qg, qr = quantise_dequantise(hg, K), quantise_dequantise(hr, K)
+    d = qg != qr
+    fg, fr = oracle.bf16_bits_to_float(hg), oracle.bf16_bits_to_float(hr)
+    emax = np.repeat(np.maximum(eg, er), 128, axis=1)[d].astype(np.float64)
+    scale = np.exp2(emax)
+    step = _e4m3_spacing(np.maximum(np.abs(fg[d]), np.abs(fr[d])) / scale) * scale
+    dh = np.abs(fg[d] - fr[d])
+    worst = np.abs(qg[d] - qr[d]) - (dh + step)
+    assert np.all(worst <= 1e-12 * step), \
+        f"quantised h differs by more than its h difference plus one E4M3 step ({worst.max():.3g})"
+    frac = float(d.mean())
+    assert frac <= A8_MAX_DIFF_FRACTION, f"{frac:.2e} of the quantised h positions differ"
+    budget = np.zeros(hg.shape)
+    budget[d] = dh + step
+    part = np.linalg.norm(budget, axis=1) / np.maximum(np.linalg.norm(fg, axis=1), 1e-30)
+    return frac, part
+
+
 def rel_l2_rows(got, ref):
     got = np.asarray(got, np.float64).reshape(-1, np.shape(got)[-1])
     ref = np.asarray(ref, np.float64).reshape(-1, np.shape(ref)[-1])
@@ -128,10 +224,15 @@ def assert_rows_close(name, got, ref, tol=ROW_TOL):
 
 
 def compare_with_oracle(layer, g, rows=None, routed=None, expert_slot=None, n_threads=0,
-                        act_fp8=False):
-    """Check GPU results `g` against the oracle on token rows `rows` (default all)."""
-    ref = oracle.moe_layer(layer, rows=rows, routed=routed, expert_slot=expert_slot,
-                           want_h=True, want_y=True, n_threads=n_threads, act_fp8=act_fp8)
+                        act_fp8=False, batched=False):
+    """Check GPU results `g` against the oracle on token rows `rows` (default all).  batched:
+    use the oracle's expert-by-expert form (full-size layers); else the per-token form."""
+    if batched:
+        ref = oracle.moe_layer_batched(layer, rows=rows, want_h=True, want_y=True,
+                                       n_threads=n_threads, act_fp8=act_fp8)
+    else:
+        ref = oracle.moe_layer(layer, rows=rows, routed=routed, expert_slot=expert_slot,
+                               want_h=True, want_y=True, n_threads=n_threads, act_fp8=act_fp8)
     T, k = layer.T, layer.k
     r = np.arange(T) if rows is None else np.asarray(rows)
     # routing: ids bit-exact, weights within W_TOL
@@ -147,7 +248,7 @@ def compare_with_oracle(layer, g, rows=None, routed=None, expert_slot=None, n_th
         np.testing.assert_array_equal(g["inv"], inv)
     pos = g["inv"].reshape(T, k)[r]  # grouped row of (t, j)
     f = oracle.bf16_bits_to_float
-    errs = {}
+    errs = {"rows": len(r)}
     errs["h"] = assert_rows_close("h", f(g["h"][pos.ravel()]), f(ref["h"]).reshape(-1, layer.I))
     errs["hS"] = assert_rows_close("shared h", f(g["hS"][r]), f(ref["hS"]))
     y_got, y_ref = f(g["y"][pos.ravel()]), ref["y"].reshape(-1, layer.H)
@@ -158,18 +259,35 @@ def compare_with_oracle(layer, g, rows=None, routed=None, expert_slot=None, n_th
         errs["S"] = assert_rows_close("shared", S_got, S_ref)
         errs["out"] = assert_rows_close("out", out_got, out_ref)
         return errs
-    # the exact effect of the two sides' h quantisations on y, S and out (see a8_correction)
+    # The two sides' h may quantise one step apart where they differ by a bf16 ulp: bound
+    # where and how far, then add the exact effect of those steps to the oracle's y, S and out
+    # (see a8_correction) before the usual per-row bound.
+    h_g, h_r = g["h"][pos.ravel()], ref["h"].reshape(-1, layer.I)
+    frac, part = check_a8_quantisation_steps(h_g, h_r, layer.I)
+    fracS, partS = check_a8_quantisation_steps(g["hS"][r], ref["hS"], layer.I)
     jr = g["ids"][r].reshape(-1)  # expert of each checked (t, j)
     slots = jr if expert_slot is None else np.asarray(expert_slot)[jr]
     ew = routed if routed is not None else layer.experts
-    dy = a8_correction(ew, slots, g["h"][pos.ravel()], ref["h"].reshape(-1, layer.I), layer.I)
+    dy = a8_correction(ew, slots, h_g, h_r, layer.I)
     dS = a8_correction(layer.shared, np.zeros(len(r), np.int64), g["hS"][r], ref["hS"], layer.I)
     w = ref["w"].astype(np.float64)
     dout = dS + np.einsum("tj,tjh->th", w, dy.reshape(len(r), k, -1))
     errs["y"] = assert_rows_close("y", y_got, y_ref + dy)
     errs["S"] = assert_rows_close("shared", S_got, S_ref + dS)
     errs["out"] = assert_rows_close("out", out_got, out_ref + dout)
+    # Without the correction: the dequantised h of a row moves by at most its budget (the h
+    # difference plus one E4M3 step at each differing position), so y moves by about that much
+    # relative to the row (a factor 2 covers the spread of the random weights' column norms).
+    # Rows must stay within the bar plus that.
+    bound_y = ROW_TOL + 2 * part
+    raw_y = rel_l2_rows(y_got, y_ref)
+    assert np.all(raw_y <= bound_y), f"uncorrected y row {int(np.argmax(raw_y - bound_y))}"
+    raw_S = rel_l2_rows(S_got, S_ref)
+    assert np.all(raw_S <= ROW_TOL + 2 * partS), "uncorrected shared output"
     errs["corrected_rows"] = float(np.mean(np.any(dy != 0, axis=1)))
+    errs["quantised_h_diff_fraction"] = max(frac, fracS)
+    errs["uncorrected_y_max"] = float(raw_y.max())
+    errs["uncorrected_out_max"] = float(rel_l2_rows(out_got, out_ref).max())
     return errs
 
 
@@ -184,3 +302,32 @@ def compare_sampled(layer, g, rows, n_threads=0, act_fp8=False):
     slot[used] = np.arange(len(used), dtype=np.int32)
     return compare_with_oracle(layer, g, rows=rows, routed=layer.experts.select(used),
                                expert_slot=slot, n_threads=n_threads, act_fp8=act_fp8)
+
+
+# Grouped-row offsets, within each expert, of the first and last rows of the kernels' m-tiles:
+# 16 (decode kernel), 32 (its two-tile groups), 128, 160 and 256 rows (the prefill GEMMs).
+TILE_ROWS = (16, 32, 128, 160, 256)
+
+
+def stratified_tokens(layer, g, min_tokens=512, seed=0):
+    """Tokens whose assignments cover, for every expert with rows, the first and last grouped
+    row of the expert and of every m-tile of every kernel tile height (TILE_ROWS), topped up
+    with seeded random tokens to at least min_tokens.  Through the rows they own, these tokens
+    reach every (expert, m-tile) of every tiling, on both sides of each tile boundary."""
+    offsets, perm, k = g["offsets"], g["perm"], layer.k
+    pos = []
+    for e in range(layer.E):
+        o, n = int(offsets[e]), int(offsets[e + 1] - offsets[e])
+        if n == 0:
+            continue
+        pos += [o, o + n - 1]
+        for bm in TILE_ROWS:
+            m = np.arange(bm, n, bm)
+            pos += list(o + m - 1) + list(o + m)
+    tokens = set((perm[np.asarray(pos, np.int64)] // k).tolist())
+    rng = np.random.default_rng(seed)
+    for t in rng.permutation(layer.T):
+        if len(tokens) >= min_tokens:
+            break
+        tokens.add(int(t))
+    return sorted(tokens)

@@ -131,15 +131,6 @@ def test_a8_dsv3_decode_full():
     compare_sampled(layer, g, rows=list(range(layer.T)), act_fp8=True)
 
 
-@pytest.mark.parametrize("cfg,rows", [("dsv3_prefill", [0, 1, 2048, 4095]),
-                                      ("kimi_k2", [0, 4097, 8191]),
-                                      ("dsv3_long_zipf", [0, 12345, 32767])])
-def test_a8_large_layers_sampled_rows(cfg, rows):
-    layer = layer_for(cfg)
-    g = run_gpu(layer, act="fp8")
-    compare_sampled(layer, g, rows=rows, act_fp8=True)
-
-
 def _dequant_bits(codes, exps):
     """bf16 bits of code * 2^e, exactly: the activations that quantised rows stand for."""
     v = codes.view(torch.float8_e4m3fn).to(torch.float32)
@@ -158,12 +149,12 @@ def _padded(exps, pitch):
     (mid(T=200, E=8, k=2), None),                      # every row; ragged m-tiles
     (mid(T=300, H=2560, I=256, E=4, k=2), None),      # 32-byte exponent pitch, deep m-tile stacks
     (mid(T=120, H=256, I=1152, E=3, k=1), None),      # odd number of 128-blocks in phase 2
-    ("dsv3_prefill", [0, 1, 777, 2048, 4095]),          # full size, sampled tokens
+    ("dsv3_prefill", None),                             # full size, every assignment
 ])
 def test_a8_phases_exact_inputs(cfg, rows, wdtype):
     """The FP8-code GEMMs (FP8 or MXFP4 weights) on quantised activations drawn directly (codes
     and exponents), against the oracle's phases on the values they stand for: no quantisation
-    on either side."""
+    on either side.  Every assignment's row of h and y is compared."""
     layer = layer_for(cfg, wdtype=wdtype) if isinstance(cfg, str) else layer_for(dict(cfg, wdtype=wdtype))
     T, H, I, E, k = layer.T, layer.H, layer.I, layer.E, layer.k
     ids = synth.random_topk_ids(T, E, k, seed=21)
@@ -182,15 +173,20 @@ def test_a8_phases_exact_inputs(cfg, rows, wdtype):
     torch.cuda.synchronize()
     flat = np.arange(T * k) if rows is None else np.array([t * k + j for t in rows for j in range(k)])
     experts = ids.numpy().reshape(-1)[flat]
-    used = sorted(set(experts.tolist()))
-    slot = np.searchsorted(used, experts)
-    sub = layer.experts.select(used)
     f = oracle.bf16_bits_to_float
-    h_ref = oracle.expert_gate_up(_dequant_bits(xc, xe), flat // k, slot, sub)
+    big = T * k > 4096  # the oracle's expert-by-expert form at full size (weights read in place)
+    if big:
+        gate_up, down = oracle.expert_gate_up_batched, oracle.expert_down_batched
+        slot, sub = experts, layer.experts
+    else:
+        gate_up, down = oracle.expert_gate_up, oracle.expert_down
+        used = sorted(set(experts.tolist()))
+        slot = np.searchsorted(used, experts)
+        sub = layer.experts.select(used)
+    h_ref = gate_up(_dequant_bits(xc, xe), flat // k, slot, sub)
     assert_rows_close("h", f(h.cpu().numpy().view(np.uint16)[inv[flat]]), f(h_ref))
     p = inv[flat]  # grouped rows of the checked assignments
-    y_ref = oracle.expert_down(_dequant_bits(hc[torch.from_numpy(p)], he[torch.from_numpy(p)]),
-                               slot, sub)
+    y_ref = down(_dequant_bits(hc[torch.from_numpy(p)], he[torch.from_numpy(p)]), slot, sub)
     assert_rows_close("y", f(y.cpu().numpy().view(np.uint16)[p]), y_ref)
 
 

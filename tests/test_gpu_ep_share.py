@@ -57,22 +57,56 @@ def test_rank_partials_and_their_sum(cfg, G):
     assert_rows_close("sum of the shares", total, f(oracle.moe_layer(layer)["out"]))
 
 
-@pytest.mark.parametrize("cfg,rows", [("dsv3_decode", None), ("dsv3_prefill", [0, 1, 2048, 4095])])
-def test_rank_share_at_full_size(cfg, rows):
-    """Rank 0 of 8 (32 of the 256 experts) at the DeepSeek-V3 shapes; sampled tokens at
-    prefill (the oracle gets only the local experts those tokens select)."""
+@pytest.mark.parametrize("cfg", ["dsv3_decode", "dsv3_prefill"])
+def test_rank_share_at_full_size(cfg):
+    """Rank 0 of 8 (32 of the 256 experts) at the DeepSeek-V3 shapes, every token (the oracle's
+    expert-by-expert form at prefill; the local experts' weights are read in place)."""
     layer = layer_for(cfg)
     e0, e1, _, _ = _ranges(layer, 8, 0)
     ids, part, _ = _run(layer, 8, 0)
-    r = np.arange(layer.T) if rows is None else np.asarray(rows)
-    sel = ids[r]
-    used = sorted(set(sel[(sel >= e0) & (sel < e1)].tolist()))
-    slot = np.full(layer.E, -1, np.int32)
-    slot[used] = np.arange(len(used), dtype=np.int32)
-    ref = oracle.moe_layer(layer, rows=r, routed=layer.experts.select(used), expert_slot=slot,
-                           with_shared=False, expert_range=(e0, e1))
-    np.testing.assert_array_equal(sel, ref["ids"])
-    assert_rows_close("partial", f(part[r]), f(ref["out"]))
+    ref = oracle.moe_layer_batched(layer, with_shared=False, expert_range=(e0, e1))
+    np.testing.assert_array_equal(ids, ref["ids"])
+    assert_rows_close("partial", f(part), f(ref["out"]))
+    local = ((ids >= e0) & (ids < e1)).any(axis=1)
+    assert not part[~local].any()
+
+
+@pytest.mark.parametrize("cfg,G", [("dsv3_decode", 8), (mid(T=24, E=16, k=4), 4),
+                                   (mid(T=37, E=64, k=8, wdtype="mxfp4"), 8)])
+def test_shared_expert_calls_on_an_expert_slice(cfg, G):
+    """moe_expert_gate_up_shared / moe_expert_down_shared on one rank's slice of the grouping
+    (offsets + e0, weights of experts e0..e1-1): the shared expert's rows come after every
+    grouped row (row T*k + t is token t) whichever slice is passed, and equal the separate
+    identity-grouped calls bit for bit; the slice's routed rows equal the separate routed calls
+    on the same slice."""
+    layer = layer_for(cfg, seed=1)
+    T, k = layer.T, layer.k
+    ids, _ = moe.moe_route(layer.scores, k, layer.score_fn, layer.renorm)
+    _, offsets, perm, _ = moe.moe_permute(ids, layer.E)
+    ws = moe.expert_weights(layer.shared)
+    h_s = moe.moe_expert_gate_up(layer.x, 1, None, None, ws)
+    y_s = moe.moe_expert_down(h_s, T, 1, None, ws)
+    for r in range(G):
+        e0, e1, _, _ = _ranges(layer, G, r)
+        if e1 == e0:
+            continue
+        local = moe.expert_slice(layer.experts, e0, e1)
+        w = moe.expert_weights(local)
+        offs = offsets[e0:]
+        h_all = torch.zeros((T * k + T, layer.I), dtype=torch.int16, device="cuda")
+        y_all = torch.zeros((T * k + T, layer.H), dtype=torch.int16, device="cuda")
+        moe.moe_expert_gate_up_shared(layer.x, k, perm, offs, w, ws, h_all)
+        moe.moe_expert_down_shared(h_all, T, k, offs, w, ws, y_all)
+        h_r = torch.zeros((T * k, layer.I), dtype=torch.int16, device="cuda")
+        y_r = torch.zeros((T * k, layer.H), dtype=torch.int16, device="cuda")
+        moe.moe_expert_gate_up(layer.x, k, perm, offs, w, h_r)
+        moe.moe_expert_down(h_r, T, k, offs, w, y_r)
+        torch.cuda.synchronize()
+        assert torch.equal(h_all[T * k:], h_s) and torch.equal(y_all[T * k:], y_s), r
+        a, b = int(offsets[e0]), int(offsets[e1])
+        assert torch.equal(h_all[a:b], h_r[a:b]) and torch.equal(y_all[a:b], y_r[a:b]), r
+        # rows of the other ranks' experts are not written
+        assert not h_all[:a].any() and not h_all[b:T * k].any(), r
 
 
 def test_partial_combine_full_range_is_the_combine_and_ranges_add_up():

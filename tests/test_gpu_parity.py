@@ -10,7 +10,8 @@ import torch
 import oracle
 import routed_expert_grouped_amd as moe
 import synth
-from gpu_util import DEV, compare_sampled, compare_with_oracle, layer_for, mid, run_gpu
+from gpu_util import (DEV, assert_rows_close, compare_sampled, compare_with_oracle, layer_for, mid,
+                      run_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -198,24 +199,6 @@ def test_dsv3_decode_full():
     compare_sampled(layer, g, rows=list(range(layer.T)))
 
 
-@pytest.mark.parametrize("cfg,rows", [("dsv3_prefill", [0, 1, 777, 2048, 4095]),
-                                      ("kimi_k2", [0, 4097, 8191]),
-                                      ("dsv3_long_zipf", [0, 12345, 32767])])
-def test_large_layers_sampled_rows(cfg, rows):
-    layer = layer_for(cfg)
-    g = run_gpu(layer)
-    counts, offsets, perm, inv = oracle.permute(g["ids"], layer.E)
-    # grouping of the whole layer is bit-exact against the oracle's permutation of the GPU ids;
-    # the routing of the sampled rows is checked against the oracle in compare_sampled
-    np.testing.assert_array_equal(g["counts"], counts)
-    np.testing.assert_array_equal(g["perm"], perm)
-    np.testing.assert_array_equal(g["inv"], inv)
-    rid, rw = oracle.route(layer.scores.cpu().numpy(), layer.k, layer.score_fn, layer.renorm)
-    np.testing.assert_array_equal(g["ids"], rid)
-    assert np.max(np.abs(g["w"].astype(np.float64) - rw)) <= 1e-6
-    compare_sampled(layer, g, rows=rows)
-
-
 @pytest.mark.parametrize("cfg,over", [("tiny_fp8", {}), ("tiny", {}), ("dsv3_decode", {}),
                                       ("dsv3_decode", {"wdtype": "mxfp4"}),
                                       (mid(T=37, E=64, k=8), {}),            # GEMV: one grid
@@ -249,3 +232,53 @@ def test_shared_expert_in_the_routed_launches_is_the_separate_calls(cfg, over):
             r = oracle.bf16_bits_to_float(ref.cpu())
             rel = np.linalg.norm(g - r, axis=1) / np.linalg.norm(r, axis=1)
             assert rel.max() <= 1e-2, rel.max()
+
+
+@pytest.mark.parametrize("T,k,E", [(300, 8, 256), (4096, 8, 256), (8192, 8, 384)])
+def test_permute_workspace_contents_do_not_matter(T, k, E):
+    """The grouping above 2048 assignments keeps its count table in the caller's workspace;
+    whatever the workspace holds on entry, the result is the oracle's, and nothing outside the
+    queried size is written."""
+    ids = synth.random_topk_ids(T, E, k, seed=T)
+    need = moe.moe_permute_workspace_size(T, k, E)
+    assert need == (0 if T * k <= 2048 else -(-T * k // 2048) * E * 4)
+    ref = oracle.permute(ids.numpy(), E)
+    for fill in (0x00, 0x7F, 0xFF):
+        buf = torch.full((need + 2 * 4096,), fill, dtype=torch.uint8, device=DEV)
+        ws = buf[4096:4096 + need] if need else None
+        got = moe.moe_permute(ids.to(DEV), E, ws=ws)
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            np.testing.assert_array_equal(a.cpu().numpy(), b)
+        assert bool((buf[:4096] == fill).all()) and bool((buf[4096 + need:] == fill).all())
+
+
+@pytest.mark.parametrize("cfg", ["tiny", "tiny_fp8", mid(), mid(T=37, E=64, k=8),
+                                 mid(wdtype="mxfp4")])
+def test_expert_ffn_call_against_the_oracle(cfg):
+    """moe_expert_ffn (both expert phases in one call, h in the caller's workspace) through the
+    C ABI: h and y of every assignment against the oracle, and equal to the two phase calls bit
+    for bit."""
+    layer = layer_for(cfg, seed=2)
+    T, k = layer.T, layer.k
+    ids, w_ = moe.moe_route(layer.scores, k, layer.score_fn, layer.renorm)
+    _, offsets, perm, inv = moe.moe_permute(ids, layer.E)
+    w = moe.expert_weights(layer.experts)
+    need = moe.moe_expert_ffn_workspace_size(T, k, w)
+    assert need == T * k * layer.I * 2
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device=DEV)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_expert_ffn(layer.x, k, perm, offsets, w, ws=ws[:need - 1])
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    y, _ = moe.moe_expert_ffn(layer.x, k, perm, offsets, w, ws=ws)
+    h2 = moe.moe_expert_gate_up(layer.x, k, perm, offsets, w)
+    y2 = moe.moe_expert_down(h2, T, k, offsets, w)
+    torch.cuda.synchronize()
+    h = ws.view(torch.int16).view(T * k, layer.I)
+    assert torch.equal(h, h2) and torch.equal(y, y2)
+    ref = oracle.moe_layer(layer, want_h=True, want_y=True)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref["ids"])
+    pos = inv.cpu().numpy()  # grouped row of flat assignment t*k+j
+    f = oracle.bf16_bits_to_float
+    assert_rows_close("h", f(h.cpu().numpy().view(np.uint16)[pos]), f(ref["h"]).reshape(-1, layer.I))
+    assert_rows_close("y", f(y.cpu().numpy().view(np.uint16)[pos]), ref["y"].reshape(-1, layer.H))
