@@ -20,7 +20,12 @@ host.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_decode] [--no-cpu]
                     [--prefill dsv3_prefill] [--a8 dsv3_prefill] [--mxfp4 dsv3_decode]
                     [--mxfp4-prefill dsv3_prefill] [--w4a8 dsv3_prefill] [--ep-ranks 0]
-                    [--extra tiny,dsv3_long_zipf,kimi_k2] [--vendor-ref]
+                    [--extra tiny,dsv3_long_zipf,dsv3_long_zipf/fp8/fp8,...] [--vendor-ref]
+
+Every workload is timed over the same --steps layer steps.  "extra" holds, by default, the tiny
+layer and the two MFMA-bound prefill layers (T = 32768 with Zipf routing, and Kimi-K2 at
+T = 8192) with bf16 activations and in the FP8-activation mode (FP8 and MXFP4 weights), each with
+its gate/up roofline against the peak of its own operand type.
 """
 from __future__ import annotations
 
@@ -38,7 +43,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
+MALL_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
 METRIC = "MoE-layer tokens/s at T=16 and T=4096; % of HBM BW / FP8 MFMA peak"
+# the tiny layer, and the two layers where the expert GEMMs are MFMA-bound (the long Zipf-routed
+# prefill and Kimi-K2) with bf16 and with FP8 activations, FP8 and MXFP4 weights
+DEFAULT_EXTRA = ("tiny,dsv3_long_zipf,dsv3_long_zipf/fp8/fp8,dsv3_long_zipf/mxfp4/fp8,"
+                 "kimi_k2,kimi_k2/fp8/fp8,kimi_k2/mxfp4/fp8")
 
 
 # ------------------------------------------------------------------ algorithmic accounting
@@ -350,7 +360,8 @@ def vendor_reference(steps: int = 10):
 
 
 def cpu_baseline(layer, rows, n_threads: int):
-    """The oracle on `rows` of the same layer, wall-clock on the host (inputs copied first)."""
+    """The oracle (its per-token form, as it stands) on `rows` of the same layer, wall-clock on
+    the host (inputs copied first)."""
     import numpy as np
 
     import oracle
@@ -409,6 +420,8 @@ def run_workload(name: str, steps: int, warmup: int, seed: int = 0, act: str = "
     else:
         roof = dict(bound="mfma", achieved=round(tf, 1), peak=mfma_peak, unit="TFLOP/s",
                     frac=round(tf / mfma_peak, 4))
+    if lb < MALL_BYTES:  # the whole layer stays in the caches: launch-bound, no roofline claim
+        roof = dict(bound="launch", note="layer fits the on-chip caches; launch-bound")
     roof.update(traffic=counter_traffic(name + ("_a8" if a8 else "") +
                                         ("_mxfp4" if wd == "mxfp4" else "")),
                 kernel="gate_up_a8 (routed, FP8 activations)" if a8 else "gate_up (routed)",
@@ -445,9 +458,9 @@ def main(argv=None):
                     help="workload also run with MXFP4 weights and bf16 activations ('' to skip)")
     ap.add_argument("--w4a8", default="dsv3_prefill",
                     help="workload also run with MXFP4 weights and FP8 activations ('' to skip)")
-    ap.add_argument("--extra", default="",
-                    help="comma-separated further workloads to report under 'extra' (e.g. "
-                         "tiny,dsv3_long_zipf,kimi_k2; off by default)")
+    ap.add_argument("--extra", default=DEFAULT_EXTRA,
+                    help="comma-separated further workloads to report under 'extra', each "
+                         "name[/weights[/activations]] ('' to skip)")
     ap.add_argument("--ep-ranks", type=int, default=0,
                     help="also time rank 0's share of the decode and prefill layers under expert "
                          "parallelism over this many ranks (off by default: its smaller launches "
@@ -488,6 +501,17 @@ def main(argv=None):
         cpu = dict(value=round(len(rows) / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
                    sample=f"{len(rows)} tokens of the {a.workload} layer (all experts they select "
                           f"+ shared), {dt:.2f} s wall", cpu=cpu_model())
+        # one thread: the tiny layer whole, and 4 tokens of the decode layer
+        import synth
+
+        single = {}
+        tiny = synth.make_layer("tiny", seed=0, device="cuda")
+        for name, lay, rws in (("tiny", tiny, list(range(tiny.T))), (a.workload, layer, [0, 1, 2, 3])):
+            dt1, th1 = cpu_baseline(lay, rws, 1)
+            single[name] = dict(value=round(len(rws) / dt1, 3), unit="tokens/s", cores=th1,
+                                sample=f"{len(rws)} tokens of the {name} layer, {dt1:.3f} s wall")
+        cpu["single_thread"] = single
+        del tiny
     ep = {}
     if a.ep_ranks:
         ep[a.workload] = run_rank_share(layer, a.ep_ranks, 0, a.steps, a.warmup)
@@ -496,38 +520,56 @@ def main(argv=None):
     if a.mxfp4:
         torch.cuda.empty_cache()
         _, mx = run_workload(a.mxfp4, a.steps, a.warmup, wdtype="mxfp4")
+    # every further workload is timed over the same `steps` layer steps as the headline one
+    S, W = a.steps, a.warmup
     prefill = a8 = None
     if a.prefill:
         torch.cuda.empty_cache()
-        player, prefill = run_workload(a.prefill, max(3, a.steps // 2), max(1, a.warmup // 2))
+        player, prefill = run_workload(a.prefill, S, W)
+        if not a.no_cpu:  # the oracle on a bounded sample of the prefill layer
+            rows = list(range(0, player.T, max(1, player.T // 64)))[:64]
+            dt, threads = cpu_baseline(player, rows, a.cpu_threads)
+            prefill["cpu_baseline"] = dict(
+                value=round(len(rows) / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{len(rows)} evenly spaced tokens of the {a.prefill} layer (all experts "
+                       f"they select + shared), {dt:.2f} s wall")
         if a.ep_ranks:
-            ep[a.prefill] = run_rank_share(player, a.ep_ranks, 0, max(3, a.steps // 2),
-                                           max(1, a.warmup // 2))
+            ep[a.prefill] = run_rank_share(player, a.ep_ranks, 0, S, W)
         if a.a8 == a.prefill:  # same layer, FP8 activations
-            _, a8 = run_workload(a.a8, max(3, a.steps // 2), max(1, a.warmup // 2), act="fp8",
-                                 layer=player)
+            _, a8 = run_workload(a.a8, S, W, act="fp8", layer=player)
         del player
     if a.a8 and a8 is None:
         torch.cuda.empty_cache()
-        _, a8 = run_workload(a.a8, max(3, a.steps // 2), max(1, a.warmup // 2), act="fp8")
+        _, a8 = run_workload(a.a8, S, W, act="fp8")
     mxp = w4 = None
     if a.mxfp4_prefill:
         torch.cuda.empty_cache()
-        mlayer, mxp = run_workload(a.mxfp4_prefill, max(3, a.steps // 2), max(1, a.warmup // 2),
-                                   wdtype="mxfp4")
+        mlayer, mxp = run_workload(a.mxfp4_prefill, S, W, wdtype="mxfp4")
         if a.w4a8 == a.mxfp4_prefill:  # same layer, FP8 activations
-            _, w4 = run_workload(a.w4a8, max(3, a.steps // 2), max(1, a.warmup // 2), act="fp8",
-                                 layer=mlayer)
+            _, w4 = run_workload(a.w4a8, S, W, act="fp8", layer=mlayer)
         del mlayer
     if a.w4a8 and w4 is None:
         torch.cuda.empty_cache()
-        _, w4 = run_workload(a.w4a8, max(3, a.steps // 2), max(1, a.warmup // 2), act="fp8",
-                             wdtype="mxfp4")
+        _, w4 = run_workload(a.w4a8, S, W, act="fp8", wdtype="mxfp4")
     extra = {}
-    for name in [w for w in a.extra.split(",") if w]:
-        torch.cuda.empty_cache()
-        _, r = run_workload(name, max(3, a.steps // 2), max(1, a.warmup // 2))
-        extra[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+    specs = [w for w in a.extra.split(",") if w]
+    layers = {}
+    for spec in specs:
+        # name[/weights][/activations]: e.g. dsv3_long_zipf, kimi_k2/fp8/fp8, dsv3_long_zipf/mxfp4/fp8
+        parts = spec.split("/")
+        name, wd = parts[0], (parts[1] if len(parts) > 1 else None)
+        act = parts[2] if len(parts) > 2 else "bf16"
+        import synth
+
+        key = (name, wd or synth.CONFIGS[name]["wdtype"])
+        if key not in layers:  # a layer is drawn once for all of its modes
+            layers.clear()
+            torch.cuda.empty_cache()
+            over = {} if wd is None else {"wdtype": wd}
+            layers[key] = synth.make_layer(name, seed=0, device="cuda", **over)
+        _, r = run_workload(name, S, W, act=act, layer=layers[key])
+        extra[spec] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+    layers.clear()
     vref = None
     if a.vendor_ref:
         torch.cuda.empty_cache()
