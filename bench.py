@@ -145,6 +145,124 @@ def counter_traffic(workload: str):
     return rec.get("traffic_bytes")
 
 
+# ------------------------------------------------------------------ profiler summaries
+# rocprofv3 writes per-dispatch CSV rows; these turn them into the short records under
+# profiles/ (the counter traffic that `roofline.traffic` reads, and text summaries).
+
+GATE_UP_RE = (r"moe::(gemv_kernel<\d+, 1, true|gemm_kernel<(true|false), 1, true|"
+              r"gemm_fp8_wide_kernel<1, true|gemm_fp8_q256_kernel<1, true|gemm_a8_kernel<1, true|"
+              r"gemm_w4_kernel<1, true)")
+SIMDS = 1024  # MI355X: 256 CUs x 4 SIMDs
+XCDS = 8
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def pmc_per_kernel(d):
+    """{kernel name: {"dispatches": n, counter: mean per dispatch}} from a --pmc run's CSV."""
+    acc = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        k = r["Kernel_Name"]
+        e = acc.setdefault(k, {"_disp": set()})
+        e["_disp"].add(r["Dispatch_Id"])
+        e.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = {}
+    for k, e in acc.items():
+        n = len(e.pop("_disp"))
+        out[k] = {"dispatches": n, **{c: sum(v) / len(v) for c, v in e.items()}}
+    return out
+
+
+def summarize_traffic(key, fetch_dir, write_dir, commands):
+    """profiles/gate_up_<key>_traffic.json from one FETCH_SIZE and one WRITE_SIZE run of one
+    workload (bench.py --only ... --copy-probe-mib 1024): the routed gate/up kernel's KiB per
+    dispatch, each scaled by the known bytes of the 1 GiB device copy over what the same counter
+    read for it."""
+    import re
+
+    fetch, write = pmc_per_kernel(fetch_dir), pmc_per_kernel(write_dir)
+    copy = [k for k in fetch if "copyBuffer" in k]
+    if not copy:
+        raise SystemExit("no copy kernel in the FETCH_SIZE run (use --copy-probe-mib 1024)")
+    copy_f = fetch[copy[0]]["FETCH_SIZE"]
+    copy_w = next(v["WRITE_SIZE"] for k, v in write.items() if "copyBuffer" in k)
+    probe = 1 << 30
+    ff, wf = probe / 1024 / copy_f, probe / 1024 / copy_w
+    gu = [k for k in fetch if re.search(GATE_UP_RE, k)]
+    if len(gu) != 1:
+        raise SystemExit(f"expected one routed gate/up kernel, found {gu}")
+    k = gu[0]
+    rec = dict(copy_probe_bytes=probe, copy_fetch_kib=copy_f, copy_write_kib=copy_w,
+               fetch_factor=ff, write_factor=wf, kernel=k, dispatches=fetch[k]["dispatches"],
+               fetch_kib=fetch[k]["FETCH_SIZE"], write_kib=write[k]["WRITE_SIZE"],
+               traffic_bytes=int(round(fetch[k]["FETCH_SIZE"] * 1024 * ff +
+                                       write[k]["WRITE_SIZE"] * 1024 * wf)),
+               source_files=kernel_sources(k), source_digest=source_digest(kernel_sources(k)),
+               commands=commands,
+               note="counters in KiB per dispatch, averaged over the dispatches of the kernel; "
+                    "each scaled by (known bytes of a 1 GiB device copy) / (what the same counter "
+                    "read for that copy)")
+    path = os.path.join(ROOT, "profiles", f"gate_up_{key}_traffic.json")
+    json.dump(rec, open(path, "w"), indent=1)
+    return path
+
+
+def summarize_stats(stats_csv_dir, out, header):
+    """A text table of rocprofv3 --stats kernel statistics (libmoe kernels)."""
+    rows = _csv_rows(stats_csv_dir, "kernel_stats.csv")
+    rows = [r for r in rows if "moe::" in r["Name"]]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [header, "", "kernel" + " " * 58 + "calls     avg_us     min_us     max_us  total_%"]
+    for r in rows:
+        name = r["Name"] if len(r["Name"]) <= 62 else r["Name"][:59] + "..."
+        lines.append(f"{name:62s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                     f"{float(r['Percentage']):8.2f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+    return out
+
+
+def summarize_pmc(out, header, runs):
+    """A text summary of counter runs: for each (label, directory), the libmoe kernels' counters
+    per dispatch and the derived figures (MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES over all SIMDs /
+    (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs); MFMA FLOP = MOPS x 512; TA/TD busy over GUI cycles)."""
+    lines = [header, ""]
+    for label, d in runs:
+        lines.append(f"== {label}  ({d})")
+        for k, v in sorted(pmc_per_kernel(d).items(), key=lambda kv: kv[0]):
+            if "moe::" not in k:
+                continue
+            lines.append(f"  {k}   [{v['dispatches']} dispatches]")
+            gui = v.get("GRBM_GUI_ACTIVE")
+            per_xcd = gui / XCDS if gui else None
+            for c in sorted(c for c in v if c != "dispatches"):
+                lines.append(f"      {c:36s} {v[c]:.6g}")
+            if per_xcd and "SQ_VALU_MFMA_BUSY_CYCLES" in v:
+                lines.append(f"      -> MFMA busy {100 * v['SQ_VALU_MFMA_BUSY_CYCLES'] / (per_xcd * SIMDS):.1f}%"
+                             f" of {per_xcd:.0f} cycles")
+            for c, what in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", "bf16"), ("SQ_INSTS_VALU_MFMA_MOPS_F8", "fp8")):
+                if v.get(c):
+                    lines.append(f"      -> {what} MFMA FLOP per dispatch {v[c] * 512:.4g}")
+            if per_xcd and v.get("SQ_INSTS_MFMA") and v.get("SQ_INSTS_VALU"):
+                lines.append(f"      -> VALU instructions per MFMA {v['SQ_INSTS_VALU'] / v['SQ_INSTS_MFMA']:.2f}")
+            for c in ("TA_BUSY_avr", "TD_TD_BUSY_sum", "TCP_PENDING_STALL_CYCLES_sum",
+                      "TCP_TCP_TA_DATA_STALL_CYCLES_sum"):
+                if per_xcd and c in v:
+                    lines.append(f"      -> {c} / GUI cycles {v[c] / per_xcd:.3g}")
+        lines.append("")
+    open(out, "w").write("\n".join(lines) + "\n")
+    return out
+
+
 # ------------------------------------------------------------------ timing
 
 def time_layer(layer, steps: int, warmup: int, act: str = "bf16"):
@@ -473,7 +591,29 @@ def main(argv=None):
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB 5 times (a known-size "
                          "kernel that calibrates the HBM byte counters of a profiler run)")
+    ap.add_argument("--only", default="",
+                    help="run just this workload (name[/weights[/activations]]) and print its "
+                         "result: the form the counter runs under a profiler use")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("KEY", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/gate_up_KEY_traffic.json from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE) of `--only` and exit (no GPU)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
+                    help="OUT HEADER LABEL=DIR ...: write a text summary of --pmc runs and exit")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("DIR", "OUT", "HEADER"),
+                    help="write a text table of a --stats run's kernel statistics and exit")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --summarize-traffic: the profiler commands, recorded in the file")
     a = ap.parse_args(argv)
+    if a.summarize_traffic:
+        print(summarize_traffic(*a.summarize_traffic, commands=a.command))
+        return 0
+    if a.summarize_pmc:
+        out, header, *runs = a.summarize_pmc
+        print(summarize_pmc(out, header, [tuple(r.split("=", 1)) for r in runs]))
+        return 0
+    if a.summarize_stats:
+        print(summarize_stats(*a.summarize_stats))
+        return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -489,6 +629,17 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if a.only:
+        parts = a.only.split("/")
+        import synth
+
+        over = {} if len(parts) < 2 else {"wdtype": parts[1]}
+        lay = synth.make_layer(parts[0], seed=0, device="cuda", **over)
+        _, r = run_workload(parts[0], a.steps, a.warmup,
+                            act=parts[2] if len(parts) > 2 else "bf16", layer=lay)
+        print(json.dumps({"only": a.only, **{k: (round(v, 4) if isinstance(v, float) else v)
+                                               for k, v in r.items()}}))
+        return 0
     probe = read_probe()
     layer, main_res = run_workload(a.workload, a.steps, a.warmup)
     if probe and main_res["roofline"]["unit"] == "GB/s":
