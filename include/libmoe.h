@@ -140,6 +140,23 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                        int32_t* offsets, int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* moe_permute for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same call and results without
+ * the workspace arguments.  The count table lives in a static device array of the library,
+ * MOE_PERMUTE_NOALLOC_MAX_BYTES large, which each GPU the library runs on holds from the first
+ * call there until the process ends (that first call on a device also looks up the array's
+ * address, with the device current; it allocates nothing).  The current device must be the
+ * device of `stream` and of the buffers.  Every call on one GPU shares that GPU's array, so
+ * calls whose launches can overlap on one GPU (other streams, other threads) race and must be
+ * ordered by the caller; the array needs no clearing between calls.  Errors as for moe_permute,
+ * plus UNSUPPORTED when the table, ceil(T*k / 2048) * E int32 above 2048 assignments, exceeds
+ * the array (e.g. more than 2,097,152 assignments at E = 256), and DEVICE when the address
+ * lookup fails. */
+#define MOE_PERMUTE_NOALLOC_MAX_BYTES (1u << 20)
+moe_status moe_permute_noalloc(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                               int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                               void* stream);
+
 /* moe_route followed by moe_permute in one launch, for decode-sized batches (T*k <= 2048): the
  * same outputs, bit for bit, as the two calls [A2 4.1 and OSDI DSLP "gating + sorting"]; one
  * workgroup routes the tokens (a wave per token) and one of its waves then groups the

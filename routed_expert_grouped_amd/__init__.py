@@ -25,7 +25,8 @@ EXPORTS = ("moe_route", "moe_permute_workspace_size", "moe_permute", "moe_expert
            "moe_expert_gate_up_shared", "moe_expert_down_shared",
            "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine", "moe_quantize_act",
            "moe_expert_gate_up_a8", "moe_expert_down_a8", "moe_expert_ffn_a8_workspace_size",
-           "moe_expert_ffn_a8", "moe_combine_partial", "moe_route_permute", "moe_status_string")
+           "moe_expert_ffn_a8", "moe_combine_partial", "moe_route_permute",
+           "moe_permute_noalloc", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -58,6 +59,7 @@ def lib():
         L.moe_route.argtypes = [P, i32, i32, i32, i32, i32, P, P, P]
         L.moe_permute_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_permute.argtypes = [P, i32, i32, i32, P, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_permute_noalloc.argtypes = [P, i32, i32, i32, P, P, P, P, P]
         L.moe_route_permute.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.moe_expert_gate_up.argtypes = [P, i32, i32, P, P, W, P, P]
         L.moe_expert_down.argtypes = [P, i32, i32, P, W, P, P]
@@ -187,6 +189,19 @@ def moe_permute(topk_ids, E: int, counts=None, offsets=None, perm=None, inv=None
     _check("moe_permute", lib().moe_permute(_p(topk_ids), T, k, E, _p(counts), _p(offsets),
                                             _p(perm), _p(inv), _p(ws),
                                             0 if ws is None else ws.numel(), _s(stream)))
+    return counts, offsets, perm, inv
+
+
+PERMUTE_NOALLOC_MAX_BYTES = 1 << 20  # MOE_PERMUTE_NOALLOC_MAX_BYTES
+
+
+def moe_permute_noalloc(topk_ids, E: int, counts, offsets, perm, inv, stream=None):
+    """moe_permute with the library's static count table instead of a workspace (the caller
+    passes every output buffer; nothing is allocated here or in the call)."""
+    T, k = topk_ids.shape
+    _check("moe_permute_noalloc",
+           lib().moe_permute_noalloc(_p(topk_ids), T, k, E, _p(counts), _p(offsets), _p(perm),
+                                     _p(inv), _s(stream)))
     return counts, offsets, perm, inv
 
 

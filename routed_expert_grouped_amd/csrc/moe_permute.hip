@@ -22,6 +22,8 @@
 // the workspace needs no clearing.
 // Up to kBlockThreads (1024) assignments one workgroup places them all at once, one a thread,
 // and up to kSmallN one wave walks them in order (both in moe_permute.h).
+#include <mutex>
+
 #include "libmoe.h"
 #include "moe_device.h"
 #include "moe_host.h"
@@ -252,4 +254,50 @@ extern "C" moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k,
     if (need > 0 && !aligned16(ws)) return MOE_ERR_INVALID_ARG;
     return launch_permute(topk_ids, T, k, E, counts, offsets, perm, inv,
                           static_cast<int32_t*>(ws), as_stream(stream));
+}
+
+// ------------------------------------------------------------------ no-allocation variant
+//
+// moe_permute_noalloc keeps the count table in `scratch`, a static device array of this library
+// (each GPU the library runs on holds its own copy until the process ends).  In host code the
+// array's name is not a device address: the address is looked up once per device, with that
+// device current, and only the looked-up pointer is ever handed to kernels.
+static __device__ __align__(256) int32_t scratch[MOE_PERMUTE_NOALLOC_MAX_BYTES / sizeof(int32_t)];
+
+namespace moe {
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static int32_t* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+static moe_status scratch_on_current_device(int32_t** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_DEVICE;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return MOE_ERR_DEVICE;
+        g_scratch[dev] = static_cast<int32_t*>(p);
+    }
+    *out = g_scratch[dev];
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" moe_status moe_permute_noalloc(const int32_t* topk_ids, int32_t T, int32_t k,
+                                          int32_t E, int32_t* counts, int32_t* offsets,
+                                          int32_t* perm, int32_t* inv, void* stream) {
+    const moe_status s = check_permute(topk_ids, T, k, E, counts, offsets, perm, inv);
+    if (s != MOE_OK || T == 0) return s;
+    if (permute_table_bytes((int64_t)T * k, E) > MOE_PERMUTE_NOALLOC_MAX_BYTES)
+        return MOE_ERR_UNSUPPORTED;
+    int32_t* table = nullptr;
+    const moe_status a = scratch_on_current_device(&table);
+    if (a != MOE_OK) return a;
+    return launch_permute(topk_ids, T, k, E, counts, offsets, perm, inv, table,
+                          as_stream(stream));
 }

@@ -48,6 +48,10 @@ int main() {
     expect(moe_permute(nullptr, 4, 2, 8, Fi, Fi, Fi, Fi, nullptr, 0, nullptr),
            MOE_ERR_INVALID_ARG, "permute null");
     expect(moe_permute(Fi, 0, 2, 8, Fi, Fi, Fi, Fi, nullptr, 0, nullptr), MOE_OK, "permute T 0");
+    expect(moe_permute_noalloc(Fi, 300000, 8, 1024, Fi, Fi, Fi, Fi, nullptr), MOE_ERR_UNSUPPORTED,
+           "noalloc beyond the array");
+    expect(moe_permute_noalloc(nullptr, 4, 2, 8, Fi, Fi, Fi, Fi, nullptr), MOE_ERR_INVALID_ARG,
+           "noalloc null");
     expect(moe_route_permute(Ff, 300, 256, 8, 1, 1, Fi, Ff, Fi, Fi, Fi, Fi, nullptr),
            MOE_ERR_UNSUPPORTED, "route_permute above 2048");
 

@@ -1,0 +1,64 @@
+"""moe_permute_noalloc (the grouping with its count table in the library's static device array,
+for callers that cannot allocate) through the C ABI, against moe_permute with a caller
+workspace and against the oracle: bit-exact, on consecutive calls whose sizes shrink (the array
+keeps the previous call's table), up to the largest table the array holds."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routed_expert_grouped_amd as moe
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _buffers(T, k, E, fill):
+    i32 = torch.int32
+    return (torch.full((E,), fill, dtype=i32, device=DEV),
+            torch.full((E + 1,), fill, dtype=i32, device=DEV),
+            torch.full((T * k,), fill, dtype=i32, device=DEV),
+            torch.full((T * k,), fill, dtype=i32, device=DEV))
+
+
+def _noalloc(ids, E, fill):
+    T, k = ids.shape
+    counts, offsets, perm, inv = _buffers(T, k, E, fill)
+    st = moe.lib().moe_permute_noalloc(
+        ctypes.c_void_p(ids.data_ptr()), T, k, E, ctypes.c_void_p(counts.data_ptr()),
+        ctypes.c_void_p(offsets.data_ptr()), ctypes.c_void_p(perm.data_ptr()),
+        ctypes.c_void_p(inv.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    return st, (counts, offsets, perm, inv)
+
+
+def test_noalloc_matches_the_workspace_call_on_shrinking_inputs():
+    # the largest table the array holds (256 blocks x 1024 experts x 4 bytes = 1 MiB), then
+    # smaller and smaller inputs: each call must not depend on what the previous one left
+    cases = [(65536, 8, 1024), (32768, 8, 256), (4096, 8, 256), (300, 8, 256), (16, 8, 256)]
+    for T, k, E in cases:
+        ids = synth.random_topk_ids(T, E, k, seed=T + E).to(DEV)
+        table = 0 if T * k <= 2048 else -(-T * k // 2048) * E * 4
+        assert table <= moe.PERMUTE_NOALLOC_MAX_BYTES
+        st, got = _noalloc(ids, E, fill=-7)
+        assert st == moe.MOE_OK, moe.moe_status_string(st)
+        want = moe.moe_permute(ids, E)
+        torch.cuda.synchronize()
+        ref = oracle.permute(ids.cpu().numpy(), E)
+        for a, b, r in zip(got, want, ref):
+            np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy())
+            np.testing.assert_array_equal(a.cpu().numpy(), r)
+
+
+def test_noalloc_rejects_a_table_beyond_the_array():
+    """One block more than the array holds is UNSUPPORTED, checked before anything is enqueued
+    (the output buffers keep their contents)."""
+    T, k, E = 257 * 2048 // 8, 8, 1024  # 257 blocks of 2048 assignments
+    ids = torch.zeros((T, k), dtype=torch.int32, device=DEV)
+    st, bufs = _noalloc(ids, E, fill=-7)
+    torch.cuda.synchronize()
+    assert st == moe.MOE_ERR_UNSUPPORTED
+    assert all(bool((b == -7).all()) for b in bufs)
