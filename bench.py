@@ -190,11 +190,19 @@ def summarize_traffic(key, fetch_dir, write_dir, commands):
     import re
 
     fetch, write = pmc_per_kernel(fetch_dir), pmc_per_kernel(write_dir)
-    copy = [k for k in fetch if "copyBuffer" in k]
-    if not copy:
-        raise SystemExit("no copy kernel in the FETCH_SIZE run (use --copy-probe-mib 1024)")
-    copy_f = fetch[copy[0]]["FETCH_SIZE"]
-    copy_w = next(v["WRITE_SIZE"] for k, v in write.items() if "copyBuffer" in k)
+
+    def probe_copies(d, counter):
+        # the device copies of the 1 GiB probe: the copy kernel's largest dispatches (the same
+        # kernel also serves the run's small host <-> device copies)
+        vals = [float(r["Counter_Value"]) for r in _csv_rows(d, "counter_collection.csv")
+                if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        if not vals:
+            raise SystemExit(f"no copy kernel in the {counter} run (use --copy-probe-mib 1024)")
+        big = [v for v in vals if v >= 0.9 * max(vals)]
+        return sum(big) / len(big)
+
+    copy_f = probe_copies(fetch_dir, "FETCH_SIZE")
+    copy_w = probe_copies(write_dir, "WRITE_SIZE")
     probe = 1 << 30
     ff, wf = probe / 1024 / copy_f, probe / 1024 / copy_w
     gu = [k for k in fetch if re.search(GATE_UP_RE, k)]
@@ -609,7 +617,7 @@ def main(argv=None):
         return 0
     if a.summarize_pmc:
         out, header, *runs = a.summarize_pmc
-        print(summarize_pmc(out, header, [tuple(r.split("=", 1)) for r in runs]))
+        print(summarize_pmc(out, header, [tuple(r.rsplit("=", 1)) for r in runs]))
         return 0
     if a.summarize_stats:
         print(summarize_stats(*a.summarize_stats))
