@@ -172,13 +172,17 @@ def pmc_per_kernel(d):
     acc = {}
     for r in _csv_rows(d, "counter_collection.csv"):
         k = r["Kernel_Name"]
-        e = acc.setdefault(k, {"_disp": set()})
-        e["_disp"].add(r["Dispatch_Id"])
+        e = acc.setdefault(k, {"_disp": {}})
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            e["_disp"][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        else:
+            e["_disp"][r["Dispatch_Id"]] = 0
         e.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     out = {}
     for k, e in acc.items():
-        n = len(e.pop("_disp"))
-        out[k] = {"dispatches": n, **{c: sum(v) / len(v) for c, v in e.items()}}
+        disp = e.pop("_disp")
+        out[k] = {"dispatches": len(disp), "duration_ns": sum(disp.values()) / len(disp),
+                  **{c: sum(v) / len(v) for c, v in e.items()}}
     return out
 
 
@@ -254,6 +258,9 @@ def summarize_pmc(out, header, runs):
             per_xcd = gui / XCDS if gui else None
             for c in sorted(c for c in v if c != "dispatches"):
                 lines.append(f"      {c:36s} {v[c]:.6g}")
+            if per_xcd and v.get("duration_ns", 0) > 50e3:  # (short dispatches: too few cycles)
+                lines.append(f"      -> duration {v['duration_ns'] / 1e3:.1f} us under the counters; "
+                             f"clock {per_xcd / v['duration_ns']:.2f} GHz")
             if per_xcd and "SQ_VALU_MFMA_BUSY_CYCLES" in v:
                 lines.append(f"      -> MFMA busy {100 * v['SQ_VALU_MFMA_BUSY_CYCLES'] / (per_xcd * SIMDS):.1f}%"
                              f" of {per_xcd:.0f} cycles")
@@ -266,6 +273,11 @@ def summarize_pmc(out, header, runs):
                       "TCP_TCP_TA_DATA_STALL_CYCLES_sum"):
                 if per_xcd and c in v:
                     lines.append(f"      -> {c} / GUI cycles {v[c] / per_xcd:.3g}")
+            if v.get("TCP_TCC_READ_REQ_sum") and "TCP_TCC_READ_REQ_LATENCY_sum" in v:
+                lines.append(f"      -> L1->L2 read latency "
+                             f"{v['TCP_TCC_READ_REQ_LATENCY_sum'] / v['TCP_TCC_READ_REQ_sum']:.0f} cycles")
+            if v.get("SQ_INSTS_MFMA") and "SQ_VALU_MFMA_COEXEC_CYCLES" in v and per_xcd:
+                lines.append(f"      -> MFMA/VALU co-execution {100 * v['SQ_VALU_MFMA_COEXEC_CYCLES'] / (per_xcd * SIMDS):.1f}% of SIMD cycles")
         lines.append("")
     open(out, "w").write("\n".join(lines) + "\n")
     return out

@@ -304,24 +304,28 @@ def compare_sampled(layer, g, rows, n_threads=0, act_fp8=False):
                                expert_slot=slot, n_threads=n_threads, act_fp8=act_fp8)
 
 
-# Grouped-row offsets, within each expert, of the first and last rows of the kernels' m-tiles:
-# 16 (decode kernel), 32 (its two-tile groups), 128, 160 and 256 rows (the prefill GEMMs).
-TILE_ROWS = (16, 32, 128, 160, 256)
+# Heights of the kernels' m-tiles, by regime: few rows per expert (T*k <= 32*E) run the decode
+# kernel's 16-row m-tiles (two of them per 32 rows); many rows run the prefill GEMMs, whose
+# m-tiles are 128, 160 or 256 rows made of 32-row MFMA subtiles.
+TILE_ROWS_FEW = (16, 32)
+TILE_ROWS_MANY = (32, 128, 160, 256)
 
 
 def stratified_tokens(layer, g, min_tokens=512, seed=0):
     """Tokens whose assignments cover, for every expert with rows, the first and last grouped
-    row of the expert and of every m-tile of every kernel tile height (TILE_ROWS), topped up
-    with seeded random tokens to at least min_tokens.  Through the rows they own, these tokens
-    reach every (expert, m-tile) of every tiling, on both sides of each tile boundary."""
+    row of the expert and of every m-tile (and 32-row subtile) of every tile height the layer's
+    kernels use (TILE_ROWS_FEW or TILE_ROWS_MANY), topped up with seeded random tokens to at
+    least min_tokens.  Through the rows they own, these tokens reach every (expert, m-tile) of
+    every tiling, on both sides of each tile boundary."""
     offsets, perm, k = g["offsets"], g["perm"], layer.k
+    heights = TILE_ROWS_FEW if layer.T * k <= 32 * layer.E else TILE_ROWS_MANY
     pos = []
     for e in range(layer.E):
         o, n = int(offsets[e]), int(offsets[e + 1] - offsets[e])
         if n == 0:
             continue
         pos += [o, o + n - 1]
-        for bm in TILE_ROWS:
+        for bm in heights:
             m = np.arange(bm, n, bm)
             pos += list(o + m - 1) + list(o + m)
     tokens = set((perm[np.asarray(pos, np.int64)] // k).tolist())

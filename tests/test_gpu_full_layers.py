@@ -4,9 +4,10 @@ DeepSeek-V3 prefill (T = 4096, 256 experts) is checked on every token row; Kimi-
 384 experts) and the long Zipf-routed layer (T = 32768, 19 experts touched, the hottest with
 32768 assignments) on a stratified token set (gpu_util.stratified_tokens): for every expert
 with rows, the tokens that own the first and last grouped row of the expert and of every
-m-tile of every kernel tile height (16, 32, 128, 160, 256 rows), topped up with seeded random
-tokens to at least 512.  Every (expert, m-tile) of every tiling is thereby reached on both
-sides of each tile boundary, across all of its column tiles (whole rows are compared).
+m-tile and 32-row MFMA subtile of every tile height the prefill GEMMs use (32, 128, 160, 256
+rows), topped up with seeded random tokens to at least 512.  Every (expert, m-tile) of every
+tiling is thereby reached on both sides of each tile boundary, across all of its column tiles
+(whole rows are compared).
 
 Whole-layer routing (ids bit-exact, weights within 1e-6) and grouping (counts, offsets, perm,
 inv bit-exact) are checked on every token in every case.  The float bars are the layer's:
