@@ -146,7 +146,7 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
  * MOE_PERMUTE_NOALLOC_MAX_BYTES large, which each GPU the library runs on holds from the first
  * call there until the process ends (that first call on a device also looks up the array's
  * address, with the device current; it allocates nothing).  The current device must be the
- * device of `stream` and of the buffers.  Every call on one GPU shares that GPU's array, so
+ * device of `stream` (else INVALID_ARG) and of the buffers.  Every call on one GPU shares that GPU's array, so
  * calls whose launches can overlap on one GPU (other streams, other threads) race and must be
  * ordered by the caller; the array needs no clearing between calls.  Errors as for moe_permute,
  * plus UNSUPPORTED when the table, ceil(T*k / 2048) * E int32 above 2048 assignments, exceeds

@@ -270,11 +270,18 @@ constexpr int kMaxDevices = 64;
 static std::mutex g_scratch_mutex;
 static int32_t* g_scratch[kMaxDevices] = {};
 
-// Device address of `scratch` on the current device (looked up on the first call there).
-static moe_status scratch_on_current_device(int32_t** out) {
+// Device address of `scratch` on the current device (looked up on the first call there), which
+// must be the device `stream` belongs to (else INVALID_ARG: the kernels would run on the
+// stream's device with another device's address).
+static moe_status scratch_on_current_device(hipStream_t stream, int32_t** out) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_DEVICE;
     if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    if (stream != nullptr) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MOE_ERR_DEVICE;
+        if (sdev != dev) return MOE_ERR_INVALID_ARG;
+    }
     std::lock_guard<std::mutex> lock(g_scratch_mutex);
     if (g_scratch[dev] == nullptr) {
         void* p = nullptr;
@@ -296,7 +303,7 @@ extern "C" moe_status moe_permute_noalloc(const int32_t* topk_ids, int32_t T, in
     if (permute_table_bytes((int64_t)T * k, E) > MOE_PERMUTE_NOALLOC_MAX_BYTES)
         return MOE_ERR_UNSUPPORTED;
     int32_t* table = nullptr;
-    const moe_status a = scratch_on_current_device(&table);
+    const moe_status a = scratch_on_current_device(as_stream(stream), &table);
     if (a != MOE_OK) return a;
     return launch_permute(topk_ids, T, k, E, counts, offsets, perm, inv, table,
                           as_stream(stream));

@@ -25,13 +25,14 @@ def _buffers(T, k, E, fill):
             torch.full((T * k,), fill, dtype=i32, device=DEV))
 
 
-def _noalloc(ids, E, fill):
+def _noalloc(ids, E, fill, stream=None):
     T, k = ids.shape
     counts, offsets, perm, inv = _buffers(T, k, E, fill)
+    stream = torch.cuda.current_stream() if stream is None else stream
     st = moe.lib().moe_permute_noalloc(
         ctypes.c_void_p(ids.data_ptr()), T, k, E, ctypes.c_void_p(counts.data_ptr()),
         ctypes.c_void_p(offsets.data_ptr()), ctypes.c_void_p(perm.data_ptr()),
-        ctypes.c_void_p(inv.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        ctypes.c_void_p(inv.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
     return st, (counts, offsets, perm, inv)
 
 
@@ -43,8 +44,11 @@ def test_noalloc_matches_the_workspace_call_on_shrinking_inputs():
         ids = synth.random_topk_ids(T, E, k, seed=T + E).to(DEV)
         table = 0 if T * k <= 2048 else -(-T * k // 2048) * E * 4
         assert table <= moe.PERMUTE_NOALLOC_MAX_BYTES
-        st, got = _noalloc(ids, E, fill=-7)
+        side = torch.cuda.Stream()  # a stream of its own (the current device's): same result
+        side.wait_stream(torch.cuda.current_stream())
+        st, got = _noalloc(ids, E, fill=-7, stream=side if T == 4096 else None)
         assert st == moe.MOE_OK, moe.moe_status_string(st)
+        torch.cuda.synchronize()
         want = moe.moe_permute(ids, E)
         torch.cuda.synchronize()
         ref = oracle.permute(ids.cpu().numpy(), E)
