@@ -282,3 +282,39 @@ def test_expert_ffn_call_against_the_oracle(cfg):
     f = oracle.bf16_bits_to_float
     assert_rows_close("h", f(h.cpu().numpy().view(np.uint16)[pos]), f(ref["h"]).reshape(-1, layer.I))
     assert_rows_close("y", f(y.cpu().numpy().view(np.uint16)[pos]), ref["y"].reshape(-1, layer.H))
+
+
+@pytest.mark.parametrize("T,k,H,E", [(300, 8, 7168, 256), (77, 13, 512, 40), (16, 8, 7168, 256),
+                                     (5, 32, 256, 64)])
+def test_combine_is_the_slot_ordered_fp32_fma_sum(T, k, H, E):
+    """moe_combine and moe_combine_partial bit for bit against the sum they state: fp32 fused
+    multiply-adds S + w_0 y_0 + ... + w_{k-1} y_{k-1} in slot order (skipping other ranks'
+    experts in the partial form), rounded to bf16.  Emulated exactly in float64: each product
+    of an fp32 weight and a bf16 value, plus the fp32 accumulator, is exact in double, so
+    rounding it to fp32 is the fused operation.  k = 13 and 32 leave a partial chunk of the
+    kernel's 8-row load groups."""
+    rng = np.random.default_rng(T * k)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    inv = rng.permutation(T * k).astype(np.int32)
+    y = torch.from_numpy(rng.standard_normal((T * k, H)).astype(np.float32)).to(torch.bfloat16)
+    S = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16)
+    d = lambda a: (a if torch.is_tensor(a) else torch.from_numpy(a)).to(DEV)
+    yb, Sb = d(y.view(torch.int16)), d(S.view(torch.int16))
+    out = moe.moe_combine(yb, d(inv), d(w), Sb, T, k, H)
+    e0, e1 = 3, E // 2
+    part = moe.moe_combine_partial(yb, d(inv), d(ids), d(w), e0, e1, None, T, k, H)
+    torch.cuda.synchronize()
+    yf, Sf = y.double().numpy(), S.double().numpy()
+
+    def fma_sum(acc, lo, hi):
+        acc = acc.astype(np.float32)
+        for j in range(k):
+            sel = (ids[:, j] >= lo) & (ids[:, j] < hi)
+            nxt = (w[:, j:j + 1].astype(np.float64) * yf[inv[np.arange(T) * k + j]]
+                   + acc.astype(np.float64)).astype(np.float32)
+            acc = np.where(sel[:, None], nxt, acc)
+        return torch.from_numpy(acc).to(torch.bfloat16).view(torch.int16).numpy()
+
+    np.testing.assert_array_equal(out.cpu().numpy(), fma_sum(Sf, 0, E))
+    np.testing.assert_array_equal(part.cpu().numpy(), fma_sum(np.zeros((T, H)), e0, e1))
