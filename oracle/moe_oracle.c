@@ -251,9 +251,12 @@ typedef struct {
     const float *s_gate, *s_up, *s_down;
 } oracle_weights;
 
-/* The 256 E4M3FN values, tabulated once from oracle_fp8_e4m3fn_to_double (a cache of that
- * function, so the inner loops do not call ldexp per weight). */
+/* The 256 E4M3FN values, the 16 E2M1 values and the 256 E8M0 values, tabulated once from
+ * oracle_fp8_e4m3fn_to_double, oracle_fp4_e2m1_to_double and oracle_e8m0_to_double (a cache of
+ * those functions, so the inner loops do not call ldexp per weight). */
 static double fp8_table[256];
+static double fp4_table[16];
+static double e8m0_table[256];
 static int fp8_table_ready = 0;
 
 static void fill_fp8_table(void) {
@@ -263,6 +266,8 @@ static void fill_fp8_table(void) {
     {
         if (!fp8_table_ready) {
             for (int i = 0; i < 256; ++i) fp8_table[i] = oracle_fp8_e4m3fn_to_double((uint8_t)i);
+            for (int i = 0; i < 16; ++i) fp4_table[i] = oracle_fp4_e2m1_to_double((uint8_t)i);
+            for (int i = 0; i < 256; ++i) e8m0_table[i] = oracle_e8m0_to_double((uint8_t)i);
             fp8_table_ready = 1;
         }
     }
@@ -277,7 +282,7 @@ static double weight(const oracle_weights* W, const void* mat, const float* sc, 
         const uint8_t b = ((const uint8_t*)mat)[at / 2];
         const uint8_t code = (c & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15);
         const uint8_t s = ((const uint8_t*)sc)[at / 32];
-        return oracle_fp4_e2m1_to_double(code) * oracle_e8m0_to_double(s);
+        return fp4_table[code] * e8m0_table[s];
     }
     double scale = sc[((size_t)x * (rows / 128) + r / 128) * (cols / 128) + c / 128];
     return fp8_table[((const uint8_t*)mat)[at]] * scale;
