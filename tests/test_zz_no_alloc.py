@@ -66,3 +66,37 @@ def test_noalloc_rejects_a_table_beyond_the_array():
     torch.cuda.synchronize()
     assert st == moe.MOE_ERR_UNSUPPORTED
     assert all(bool((b == -7).all()) for b in bufs)
+
+
+def test_noalloc_in_a_graph():
+    """The call captured into a HIP graph (the use it is for: nothing to allocate while
+    capturing) replays to moe_permute's result, also after new ids are copied into the captured
+    input and with other eager work between the replays."""
+    T, k, E = 4096, 8, 256
+    ids = synth.random_topk_ids(T, E, k, seed=5).to(DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st, _ = _noalloc(ids, E, fill=0)  # first call on the device outside the capture
+    torch.cuda.synchronize()
+    assert st == moe.MOE_OK
+    outs = _buffers(T, k, E, fill=-7)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cur = torch.cuda.current_stream()
+        st = moe.lib().moe_permute_noalloc(
+            ctypes.c_void_p(ids.data_ptr()), T, k, E, *[ctypes.c_void_p(b.data_ptr()) for b in outs],
+            ctypes.c_void_p(cur.cuda_stream))
+    assert st == moe.MOE_OK, moe.moe_status_string(st)
+    for rep in range(4):
+        if rep == 3:  # new inputs, copied into the captured buffer
+            ids.copy_(synth.random_topk_ids(T, E, k, seed=6).to(DEV))
+        for b in outs:
+            b.fill_(-7)
+        junk = torch.randn(1 << 20, device=DEV).sum()  # unrelated eager work
+        graph.replay()
+        torch.cuda.synchronize()
+        want = oracle.permute(ids.cpu().numpy(), E)
+        for a, r in zip(outs, want):
+            np.testing.assert_array_equal(a.cpu().numpy(), r)
+        del junk
