@@ -104,12 +104,15 @@ def kernel_sources(kernel: str) -> list:
     """Sources (relative to the repository root) of the translation unit a libmoe gate/up kernel
     is compiled in, with the headers it includes: moe_ffn.hip (GEMV kernels and the launches),
     moe_gemm.hip (bf16-activation GEMM, with the launch choice of moe_gemm_wide.hip's 160 x 512
-    tiles), moe_gemm_a8.hip (FP8-activation GEMM) or moe_gemm_w4.hip (MXFP4 weights, bf16
-    activations)."""
+    tiles), moe_gemm_a8.hip (FP8-activation GEMM, and the launch choice of the W4A8 GEMM in
+    moe_gemm_w4a8.hip) or moe_gemm_w4.hip (MXFP4 weights, bf16 activations)."""
     if "gemv_kernel" in kernel:
         names = ["moe_device.h", "moe_ffn.h", "moe_ffn.hip", "moe_host.h", "moe_lds.h"]
     elif "gemm_a8_kernel" in kernel:
         names = ["moe_device.h", "moe_ffn.h", "moe_gemm_a8.hip", "moe_host.h", "moe_lds.h"]
+    elif "gemm_w4a8_kernel" in kernel:
+        names = ["moe_device.h", "moe_ffn.h", "moe_gemm_a8.hip", "moe_gemm_w4a8.hip", "moe_host.h",
+                 "moe_lds.h"]
     elif "gemm_fp8_wide_kernel" in kernel:
         names = ["moe_device.h", "moe_ffn.h", "moe_ffn.hip", "moe_gemm.hip", "moe_gemm_wide.hip",
                  "moe_host.h", "moe_lds.h"]
@@ -151,7 +154,7 @@ def counter_traffic(workload: str):
 
 GATE_UP_RE = (r"moe::(gemv_kernel<\d+, 1, true|gemm_kernel<(true|false), 1, true|"
               r"gemm_fp8_wide_kernel<1, true|gemm_fp8_q256_kernel<1, true|gemm_a8_kernel<1, true|"
-              r"gemm_w4_kernel<1, true)")
+              r"gemm_w4_kernel<1, true|gemm_w4a8_kernel<1, true)")
 SIMDS = 1024  # MI355X: 256 CUs x 4 SIMDs
 XCDS = 8
 

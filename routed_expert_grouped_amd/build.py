@@ -16,9 +16,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC,
          # packed fp32 VALU forms are kept out of the generated code
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         # MFMA accumulators in VGPRs: the block-scale FMAs read them without AGPR copies
-         "-mllvm", "-amdgpu-mfma-vgpr-form"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# MFMA accumulators in VGPRs: the block-scale FMAs read them without AGPR copies.  The W4A8 GEMM
+# rescales nothing and keeps its sums in the accumulation registers instead.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+AGPR_FORM_FILES = {"moe_gemm_w4a8.hip"}
 
 
 # per-file additions: the 4-bit GEMM with bf16 activations is scheduled for instruction-level
@@ -29,7 +31,8 @@ FILE_FLAGS = {"moe_gemm_w4.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 def flags_for(src: str) -> list:
     """The hipcc flags one source is compiled with."""
-    return FLAGS + FILE_FLAGS.get(os.path.basename(src), [])
+    name = os.path.basename(src)
+    return FLAGS + ([] if name in AGPR_FORM_FILES else VGPR_FORM) + FILE_FLAGS.get(name, [])
 
 
 def sources():

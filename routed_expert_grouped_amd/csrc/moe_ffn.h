@@ -61,6 +61,11 @@ constexpr int kA8MaxPitch = kA8MaxK / 128;
 bool a8_gemm_fits(int phase, const GemmArgs& a);
 moe_status launch_gemm_a8(int phase, const GemmArgs& a, hipStream_t st);
 
+// MXFP4 weights with FP8 activations (W4A8): the one-wave-per-SIMD GEMM (moe_gemm_w4a8.hip),
+// for the shapes a8_gemm_fits accepts
+bool w4a8_gemm_fits(int phase, const GemmArgs& a);
+moe_status launch_gemm_w4a8(int phase, const GemmArgs& a, hipStream_t st);
+
 // FP8 weights, bf16 activations: the 160 x 512 tile GEMM (moe_gemm_wide.hip)
 bool wide_gemm_fits(int phase, const GemmArgs& a);
 moe_status launch_gemm_wide(int phase, const GemmArgs& a, hipStream_t st);

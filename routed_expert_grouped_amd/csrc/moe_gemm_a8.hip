@@ -24,16 +24,12 @@
 // apply per 32-long K group: group g of row (column) l % 32 takes the E8M0 byte of lane
 // l % 32 + 32 g.
 //
-// MXFP4 weights (kW4): the B operand is E2M1 codes, 16 bytes a lane holding the 32 K values
-// [32 h, 32 h + 32) of the step, first code in the low nibble -- one MX scale group, so the
-// weights' own E8M0 scales go into the instruction's B scale operand and nothing is rescaled
-// (W4A8: both operands' scales are powers of two applied exactly to the products).  A weight
-// slot is then 256 K (still 128 bytes of each row, whole lines), four compute stages, with
-// the slot's E8M0 scales (256 rows x 8 bytes) loaded directly to LDS beside it, one 4-byte load
-// per wave.  Activation rows are 64 bytes in LDS,
-// four 16-byte chunks, chunk c at slot c ^ ((row >> 2) & 3); weight rows are 128 bytes, eight
-// chunks, chunk c at slot c ^ ((row >> 1) & 7).  Either way the fragment reads (chunks h and
-// 2 + h of a step, for 32 consecutive rows) are free of bank conflicts.
+// Activation rows are 64 bytes in LDS, four 16-byte chunks, chunk c at slot c ^ ((row >> 2) & 3);
+// weight rows are 128 bytes, eight chunks, chunk c at slot c ^ ((row >> 1) & 7), so that 16
+// consecutive rows' reads of one chunk land in distinct 16-byte bank groups.
+//
+// MXFP4 weights with FP8 activations (W4A8) have a kernel of their own (moe_gemm_w4a8.hip); this
+// launcher hands them to it.
 #include "libmoe.h"
 #include "moe_device.h"
 #include "moe_ffn.h"
@@ -54,7 +50,7 @@ constexpr int kARing = 3;    // activation slots
 constexpr int kBRing = 3;    // weight slots
 constexpr int kEPart = 16;   // scale blocks per exponent part
 constexpr int kE8M0One = 127;  // E8M0 encoding of 1.0
-constexpr int kFmtFP8 = 0, kFmtFP4 = 4;  // operand formats of the scaled MFMA (E4M3, E2M1)
+constexpr int kFmtFP8 = 0;   // operand format of the scaled MFMA (E4M3)
 
 __device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
     i32x8 r = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
@@ -62,20 +58,19 @@ __device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
     return r;
 }
 
-template <int kPhase, bool kGrouped, bool kW4>
+template <int kPhase, bool kGrouped>
 __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
     constexpr int kAStage = kA8M * kA8K;   // 16 KB
     constexpr int kBSlot = kA8N * 128;     // 32 KB: 128 bytes of each weight row
     constexpr int kEBytes = kA8M * 16;     // 4 KB
-    constexpr int kBK = kW4 ? 2 * kA8BK : kA8BK;  // K per weight slot
-    constexpr int kSPS = kBK / kA8K;              // compute stages per weight slot (2 or 4)
-    constexpr int kBL = kW4 ? 5 : 4;              // loads per wave per weight slot
-    constexpr int kPeriod = kARing * kSPS;        // stages after which the slot pattern repeats
+    constexpr int kBK = kA8BK;        // K per weight slot
+    constexpr int kSPS = kBK / kA8K;  // compute stages per weight slot
+    constexpr int kBL = 4;            // loads per wave per weight slot
+    constexpr int kPeriod = kARing * kSPS;  // stages after which the slot pattern repeats
     __shared__ __attribute__((aligned(1024))) uint8_t sA[kARing][kAStage];
     __shared__ __attribute__((aligned(1024))) uint8_t sB[kBRing][kBSlot];
     __shared__ __attribute__((aligned(1024))) uint8_t sE[2][kEBytes];  // [row][16 blocks]
-    __shared__ float sScale[2][kW4 ? 1 : kA8MaxPitch];
-    __shared__ __attribute__((aligned(16))) uint8_t sMX[kW4 ? kBRing : 1][kW4 ? kA8N * 8 : 16];
+    __shared__ float sScale[2][kA8MaxPitch];
 
     constexpr int kCols = kPhase == 1 ? kA8N / 2 : kA8N;
     Tile tile;
@@ -87,8 +82,7 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
     const int e = tile.group;
     const int c0 = tile.nt * kCols;
     const int K = a.K, kblocks = K / 128, nq = 2 * kblocks;
-    const int nslots = (K + kBK - 1) / kBK;
-    const bool half_last = kW4 && K % kBK != 0;  // (kW4) the last slot holds 128 K
+    const int nslots = K / kBK;
     const int cpr = a.aexp_pitch >> 4;  // 16-byte parts of an exponent row (1..4)
     const int fr = lane & 31, half = lane >> 5;
     const uint8_t* act = (const uint8_t*)a.act;
@@ -110,11 +104,8 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
     }
     // weight loads: instruction i (0..3) of wave w fills slot rows 8 (4 w + i) + lane / 8, slot
     // lane % 8 holding chunk slot ^ ((row >> 1) & 7); phase 1 rows 0..127 gate, 128..255 up.
-    // (kW4) In a last slot of 128 K the chunks past its 64 bytes reload its first half (never
-    // read), so every load stays inside the row.
-    const size_t row_bytes = kW4 ? (size_t)K / 2 : (size_t)K;
+    const size_t row_bytes = (size_t)K;
     const uint8_t* bsrc[4];
-    bool bhi[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 8 * (4 * wave + i) + (lane >> 3);
@@ -129,24 +120,6 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
         }
         const int chunk = (lane & 7) ^ ((r >> 1) & 7);
         bsrc[i] = base + ((size_t)e * a.N + wr) * row_bytes + (chunk << 4);
-        bhi[i] = chunk >= 4;
-    }
-    // (kW4) E8M0 weight scales [N][K/32]: wave w's 4-byte load fills slot rows 32 w + lane / 2,
-    // groups 4 (lane % 2) .. + 3 of the slot (8 bytes a row); in a last slot of 128 K the odd
-    // lanes reload the even lanes' dword
-    const uint8_t* msrc = nullptr;
-    if constexpr (kW4) {
-        const int r = 32 * wave + (lane >> 1);
-        const uint8_t* base;
-        int wr;
-        if (kPhase == 1) {
-            base = (const uint8_t*)(r < 128 ? a.s0 : a.s1);
-            wr = c0 + (r & 127);
-        } else {
-            base = (const uint8_t*)a.s0;
-            wr = c0 + r;
-        }
-        msrc = base + ((size_t)e * a.N + wr) * (size_t)(K / 32) + 4 * (lane & 1);
     }
     // exponent parts: waves 0..3 each fill rows 64 w + lane (16 bytes: blocks 16 p .. 16 p + 15)
     const uint32_t eoff = src_row((64 * wave + lane) & (kA8M - 1)) * (uint32_t)cpr;
@@ -162,12 +135,9 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
     };
     auto issue_b = [&](int sl) {  // weight slot sl (kBL loads)
         uint8_t* dst = sB[sl % kBRing];
-        const bool part = half_last && sl == nslots - 1;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            lds_dma16(bsrc[i] + (size_t)sl * 128 - (part && bhi[i] ? 64 : 0), dst + 8 * (4 * wave + i) * 128);
-        if constexpr (kW4)
-            lds_dma4(msrc + (size_t)sl * 8 - (part && (lane & 1) ? 4 : 0), &sMX[sl % kBRing][256 * wave]);
+            lds_dma16(bsrc[i] + (size_t)sl * 128, dst + 8 * (4 * wave + i) * 128);
     };
     auto issue_e = [&](int part) {  // waves 0..3 (whole waves)
         if (wave < 4)
@@ -176,7 +146,7 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
 
     // weight block scales: phase 1 [0] gate, [1] up of block-row c0/128; phase 2 block-rows
     // c0/128 and c0/128 + 1 (the tile's 256 rows)
-    if (!kW4 && tid < kblocks) {
+    if (tid < kblocks) {
         const size_t srow = ((size_t)e * (a.N / 128) + c0 / 128) * kblocks;
         sScale[0][tid] = a.s0[srow + tid];
         sScale[1][tid] = kPhase == 1 ? a.s1[srow + tid] : a.s0[srow + kblocks + tid];
@@ -186,7 +156,7 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
 
     const int nvalid = (tile.row1 - tile.row0 + 31) >> 5;  // filled 32-row subtiles (1..8)
     const int mine = (nvalid > wm) + (nvalid > wm + 2) + (nvalid > wm + 4) + (nvalid > wm + 6);
-    int aaddr[4][2], baddr[2][4][2], eaddr[4], mxaddr[2];
+    int aaddr[4][2], baddr[2][kSPS][2], eaddr[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         const int r = (wm + 2 * mi) * 32 + fr;
@@ -197,23 +167,19 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
         const int r = (kPhase == 1 ? ni * 128 + wn * 32 : wn * 64 + ni * 32) + fr;
-        mxaddr[ni] = r * 8 + half;  // (kW4) this lane's K group of stage hs: byte 2 hs
 #pragma unroll
         for (int hs = 0; hs < kSPS; ++hs)  // compute stage within the weight slot
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                // FP8: chunks 4 hs + 2 j + half; FP4: chunk 2 hs + half (16 code bytes a lane)
-                const int chunk = kW4 ? 2 * hs + half : 4 * hs + 2 * j + half;
+                const int chunk = 4 * hs + 2 * j + half;
                 baddr[ni][hs][j] = r * 128 + ((chunk ^ ((r >> 1) & 7)) << 4);
             }
     }
     bool any_zero = false;
     __syncthreads();  // weight scales staged
-    if (!kW4) {
-        for (int b = lane; b < kblocks; b += kWave)
-            any_zero |= sScale[sg0][b] == 0.0f || sScale[sg1][b] == 0.0f;
-        any_zero = __ballot(any_zero) != 0;
-    }
+    for (int b = lane; b < kblocks; b += kWave)
+        any_zero |= sScale[sg0][b] == 0.0f || sScale[sg1][b] == 0.0f;
+    any_zero = __ballot(any_zero) != 0;
 
     f32x16 acc[4][2];
 #pragma unroll
@@ -279,7 +245,7 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
         }
         if (kA && q + 2 < nq) issue_a(q + 2);
         if (NS == 0) return;
-        if (!kW4 && HS == 0) {  // first half of scale block kb
+        if (HS == 0) {  // first half of scale block kb
             const float s0 = sScale[sg0][kb], s1 = sScale[sg1][kb];
             if (kMask) {
                 const bool z0 = s0 == 0.0f, z1 = s1 == 0.0f;
@@ -305,22 +271,15 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
         const uint8_t* B = sB[(ST / kSPS) % kBRing];
         // every fragment of the stage is read before the first MFMA
         i32x8 fb[2], fa[NS > 0 ? NS : 1];
-        int sb[2] = {kE8M0One, kE8M0One};  // (kW4) E8M0 scales of the weight columns' K group
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
-            if constexpr (kW4) {
-                sb[ni] = sMX[(ST / kSPS) % kBRing][mxaddr[ni] + 2 * HS];
-                const u32x4 zero = {0u, 0u, 0u, 0u};
-                fb[ni] = join(*(const u32x4*)&B[baddr[ni][HS][0]], zero);
-            } else {
-                u32x4 lo = *(const u32x4*)&B[baddr[ni][HS][0]];
-                u32x4 hi = *(const u32x4*)&B[baddr[ni][HS][1]];
-                if (kMask) {
-                    lo &= ni == 0 ? m0 : m1;
-                    hi &= ni == 0 ? m0 : m1;
-                }
-                fb[ni] = join(lo, hi);
+            u32x4 lo = *(const u32x4*)&B[baddr[ni][HS][0]];
+            u32x4 hi = *(const u32x4*)&B[baddr[ni][HS][1]];
+            if (kMask) {
+                lo &= ni == 0 ? m0 : m1;
+                hi &= ni == 0 ? m0 : m1;
             }
+            fb[ni] = join(lo, hi);
         }
 #pragma unroll
         for (int mi = 0; mi < NS; ++mi)
@@ -330,8 +289,7 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
                 acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    fa[mi], fb[ni], acc[mi][ni], kFmtFP8, kW4 ? kFmtFP4 : kFmtFP8, 0, sc[mi], 0,
-                    kW4 ? sb[ni] : kE8M0One);
+                    fa[mi], fb[ni], acc[mi][ni], kFmtFP8, kFmtFP8, 0, sc[mi], 0, kE8M0One);
     };
     auto run = [&](auto ns_tag, auto mask_tag, auto a_tag) {
         issue_e(0);
@@ -342,7 +300,7 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
             issue_a(1);  // nq >= 2
         }
         // the slots of stage q are q % 3 (activations) and (q / kSPS) % 3 (weights): period
-        // kPeriod (6, or 12 for kW4)
+        // kPeriod = 6
         for (int q = 0; q < nq; q += kPeriod) {
             stage(q, std::integral_constant<int, 0>{}, ns_tag, mask_tag, a_tag);
             if (q + 1 < nq) stage(q + 1, std::integral_constant<int, 1>{}, ns_tag, mask_tag, a_tag);
@@ -350,21 +308,13 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
             if (q + 3 < nq) stage(q + 3, std::integral_constant<int, 3>{}, ns_tag, mask_tag, a_tag);
             if (q + 4 < nq) stage(q + 4, std::integral_constant<int, 4>{}, ns_tag, mask_tag, a_tag);
             if (q + 5 < nq) stage(q + 5, std::integral_constant<int, 5>{}, ns_tag, mask_tag, a_tag);
-            if constexpr (kPeriod > 6) {
-                if (q + 6 < nq) stage(q + 6, std::integral_constant<int, 6>{}, ns_tag, mask_tag, a_tag);
-                if (q + 7 < nq) stage(q + 7, std::integral_constant<int, 7>{}, ns_tag, mask_tag, a_tag);
-                if (q + 8 < nq) stage(q + 8, std::integral_constant<int, 8>{}, ns_tag, mask_tag, a_tag);
-                if (q + 9 < nq) stage(q + 9, std::integral_constant<int, 9>{}, ns_tag, mask_tag, a_tag);
-                if (q + 10 < nq) stage(q + 10, std::integral_constant<int, 10>{}, ns_tag, mask_tag, a_tag);
-                if (q + 11 < nq) stage(q + 11, std::integral_constant<int, 11>{}, ns_tag, mask_tag, a_tag);
-            }
         }
     };
     using MY = std::integral_constant<bool, true>;
     using MN = std::integral_constant<bool, false>;
     // the K loop for this wave's filled-subtile count, zero-scale masking and activation loads
     auto dispatch = [&](auto a_tag) {
-        if (!kW4 && any_zero && mine > 0)
+        if (any_zero && mine > 0)
             run(std::integral_constant<int, 4>{}, MY{}, a_tag);  // rare: all 4 subtiles (unfilled ones are never stored)
         else if (mine == 4)
             run(std::integral_constant<int, 4>{}, MN{}, a_tag);
@@ -381,7 +331,7 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
         dispatch(std::true_type{});
     else
         dispatch(std::false_type{});
-    if (!kW4) rescale(u0, u1, std::integral_constant<int, 4>{});
+    rescale(u0, u1, std::integral_constant<int, 4>{});
 
     // D layout of the 32x32 MFMA: value x of a lane is row 8*(x/4) + 4*(lane/32) + x%4 of the
     // subtile, column lane%32
@@ -417,6 +367,7 @@ bool a8_gemm_fits(int phase, const GemmArgs& a) {
 
 moe_status launch_gemm_a8(int phase, const GemmArgs& a, hipStream_t st) {
     if (!a8_gemm_fits(phase, a)) return MOE_ERR_UNSUPPORTED;
+    if (a.fp4) return launch_gemm_w4a8(phase, a, st);
     const int cols = phase == 1 ? kA8N / 2 : kA8N;
     const int groups = a.offsets ? a.n_groups : 1;
     const int64_t mt = ((int64_t)a.rows + kA8M - 1) / kA8M + std::min<int64_t>(groups, a.rows);
@@ -424,8 +375,7 @@ moe_status launch_gemm_a8(int phase, const GemmArgs& a, hipStream_t st) {
     if (wgs > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((wgs + 7) & ~int64_t(7))), block(512);
     const bool g = a.offsets != nullptr;
-#define MOE_A8(P, G) a.fp4 ? gemm_a8_kernel<P, G, true><<<grid, block, 0, st>>>(a) \
-                           : gemm_a8_kernel<P, G, false><<<grid, block, 0, st>>>(a)
+#define MOE_A8(P, G) gemm_a8_kernel<P, G><<<grid, block, 0, st>>>(a)
     if (phase == 1) g ? MOE_A8(1, true) : MOE_A8(1, false);
     else g ? MOE_A8(2, true) : MOE_A8(2, false);
 #undef MOE_A8

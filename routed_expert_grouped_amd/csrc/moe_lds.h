@@ -33,4 +33,19 @@ __device__ __forceinline__ void lds_dma4(const void* src, const void* lds) {
                  : "memory", "m0");
 }
 
+// The same two loads with the LDS byte address given directly (a wave-uniform value).
+__device__ __forceinline__ void lds_dma16_at(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void lds_dma4_at(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+
 }  // namespace moe

@@ -20,11 +20,11 @@ from routed_expert_grouped_amd import build
 
 SRCS = [os.path.join(build.CSRC, f)
         for f in ("moe_gemm.hip", "moe_gemm_wide.hip", "moe_gemm_a8.hip", "moe_gemm_w4.hip",
-                  "moe_ffn.hip")]
+                  "moe_gemm_w4a8.hip", "moe_ffn.hip")]
 # the GEMMs with direct-to-LDS loads (and their instantiation counts: 2 phases x (grouped,
-# identity), x (FP8, MXFP4 weights) for the FP8-activation GEMM)
-KERNELS = {"gemm_fp8_q256_kernel": 4, "gemm_fp8_wide_kernel": 4, "gemm_a8_kernel": 8,
-           "gemm_w4_kernel": 4}
+# identity))
+KERNELS = {"gemm_fp8_q256_kernel": 4, "gemm_fp8_wide_kernel": 4, "gemm_a8_kernel": 4,
+           "gemm_w4_kernel": 4, "gemm_w4a8_kernel": 4}
 
 pytestmark = pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not available")
 
@@ -158,7 +158,6 @@ def _issue_model(K, sps, per_slot, per_stage, load_a):
 
 @pytest.mark.parametrize("kernel,sps,per_slot,per_stage", [
     ("FP8-activation GEMM, FP8 weights", 2, 4, 2),
-    ("FP8-activation GEMM, MXFP4 weights", 4, 5, 2),
     ("4-bit GEMM, bf16 activations", 2, 3, 4),
 ])
 @pytest.mark.parametrize("load_a", [False, True])
@@ -168,5 +167,45 @@ def test_gemm_waits_cover_exactly_the_needed_loads(kernel, sps, per_slot, per_st
     every K the kernel takes."""
     for K in range(128, 8192 + 1, 128):
         for seq, n, need in _issue_model(K, sps, per_slot, per_stage, load_a):
+            newest = max(i for i, x in enumerate(seq) if x in need)
+            assert n == len(seq) - 1 - newest, (K, n, len(seq) - 1 - newest)
+
+
+B_PARTS = (0, 3, 6, 8, 10)  # the W4A8 GEMM's weight slot: loads [B_PARTS[j], B_PARTS[j + 1]) in part j
+
+
+def _issue_model_w4a8(K, na):
+    """The one-wave-per-SIMD W4A8 GEMM's loads in issue order, as its source states them, and each
+    stage's wait: prologue exponent parts 0, 1 (those that exist), weight slots 0, 1 and part 0 of
+    slot 2, activation stages 0, 1, 2 (na loads each); at stage q, after the wait: exponent part
+    q / 32 + 2 when q % 32 == 31 (if it exists), part (q + 1) % 4 of weight slot (q + 1) / 4 + 2,
+    activation stage q + 3 (both issued past the end of K too: they reload into free slots).
+    Yields (loads issued so far, the wait before reading stage s's fragments, the loads stage s
+    reads), s = 0 (the prologue's wait) and s = q + 1."""
+    nq, nparts = K // 64, -(-(K // 128) // 16)
+    seq = [("E", 0)] + ([("E", 1)] if nparts > 1 else [])
+    seq += [("B", 0)] * 10 + [("B", 1)] * 10 + [("B", 2)] * B_PARTS[1]
+    for d in range(3):
+        seq += [("A", d)] * na
+    yield list(seq), 2 * na, {("A", 0), ("B", 0), ("E", 0)}
+    for q in range(nq):
+        if q + 1 < nq:  # the kernel's wait immediate
+            n = (na + (B_PARTS[q % 4 + 1] - B_PARTS[q % 4] if q > 0 else 0)
+                 + (1 if q % 32 == 0 and q > 0 and q // 32 + 1 < nparts else 0))
+            yield list(seq), n, {("A", q + 1), ("B", (q + 1) // 4), ("E", (q + 1) // 32)}
+        if q % 32 == 31 and q // 32 + 2 < nparts:
+            seq += [("E", q // 32 + 2)]
+        j = (q + 1) % 4
+        seq += [("B", (q + 1) // 4 + 2)] * (B_PARTS[j + 1] - B_PARTS[j])
+        seq += [("A", q + 3)] * na
+
+
+@pytest.mark.parametrize("na", [1, 2, 3, 4])
+def test_w4a8_waits_cover_exactly_the_needed_loads(na):
+    """As above for the W4A8 GEMM, whose waves all issue na loads per activation stage (na = the
+    64-row blocks holding tile rows) and whose waits come before reading the next stage's
+    fragments: every wait leaves exactly the loads issued after the newest one it needs."""
+    for K in range(128, 8192 + 1, 128):
+        for seq, n, need in _issue_model_w4a8(K, na):
             newest = max(i for i, x in enumerate(seq) if x in need)
             assert n == len(seq) - 1 - newest, (K, n, len(seq) - 1 - newest)
