@@ -14,26 +14,26 @@
 //     other set, so no MFMA waits for an LDS read.  A 128 x 128 wave tile reads 12 KB of
 //     fragments a stage for 16 MFMAs, where 128 x 64 wave tiles read 10 KB for 8.
 //
-// LDS (158 KB) holds the operands in the same swizzled rows as the 8-wave kernel:
-//   activations  16 KB stages of 64 K (256 rows x 64 bytes), 3 slots;
-//   weights      32 KB slots of 256 K (256 rows x 128 bytes of E2M1 codes), 3 slots, each with
-//                its E8M0 scales (256 rows x 8 bytes);
+// LDS (140 KB) holds every operand row as whole 128-byte lines, eight 16-byte chunks, chunk c at
+// slot c ^ ((row >> 1) & 7):
+//   activations  32 KB slots of 128 K (256 rows x 128 bytes: two compute stages), 2 slots;
+//   weights      32 KB slots of 256 K (256 rows x 128 bytes of E2M1 codes: four stages), 2 slots,
+//                each with its E8M0 scales (256 rows x 8 bytes);
 //   exponents    4 KB parts of 16 blocks (256 rows x 16 bytes), 2 slots.
-// Activation rows are four 16-byte chunks, chunk c at slot c ^ ((row >> 2) & 3); weight rows eight
-// chunks, chunk c at slot c ^ ((row >> 1) & 7).
 //
-// Loads (direct to LDS, in this order within a stage; waits count them by hand):
-//   prologue   exponent parts 0, 1 (those that exist), weight slots 0, 1 and part 0 of slot 2,
-//              activation stages 0, 1, 2;
+// Loads (direct to LDS, in this order within a stage; waits count them by hand).  Every wave
+// issues 2 nA loads per activation slot (nA = 64-row blocks holding tile rows, the same for all
+// waves), 10 per weight slot in two parts of 5, and 1 per exponent part:
+//   prologue   exponent parts 0, 1 (those that exist), weight slot 0, part 0 of weight slot 1,
+//              activation slots 0, 1;
 //   stage q    after the barrier: exponent part q / 32 + 2 when q % 32 == 31 (if it exists);
-//              part (q + 1) % 4 of weight slot (q + 1) / 4 + 2 (a slot is 4 parts of 3, 3, 2, 2
-//              loads); activation stage q + 3.
-// Past the end of K a weight load reloads the last slot and an activation load stage nq - 1, into
-// ring slots that no stage reads again.
-// A ring slot is refilled from the stage after the one that read its last fragments, behind the
-// barrier that every wave passes only once it has read them.  Every wave issues nA loads per
-// activation stage (nA = 64-row blocks holding tile rows, the same for all waves), 10 per weight
-// slot and 1 per exponent part.
+//              part 0 of weight slot q / 4 + 2 when q % 4 == 3, part 1 of weight slot q / 4 + 1
+//              when q % 4 == 0; activation slot (q + 3) / 2 when q is odd.
+// Past the end of K a weight load reloads the last slot and an activation load the last slot,
+// into ring slots that no stage reads again.  A ring slot is refilled in the stage after the one
+// whose fragments were its last, behind the barrier that every wave passes only once it has read
+// them: activation slot d + 2 two stages before its first fragments are read, weight slot s + 2
+// three and four stages before.
 #include "libmoe.h"
 #include "moe_device.h"
 #include "moe_ffn.h"
@@ -51,13 +51,14 @@ typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));
 constexpr int kM = 256;      // rows per m-tile
 constexpr int kN = 256;      // weight rows per tile
 constexpr int kSK = 64;      // K per compute stage (one MFMA step)
+constexpr int kAK = 128;     // K per activation slot
 constexpr int kSlotK = 256;  // K per weight slot
+constexpr int kSPA = kAK / kSK;      // stages per activation slot
 constexpr int kSPS = kSlotK / kSK;   // stages per weight slot
-constexpr int kRing = 3;             // activation stages and weight slots in LDS
+constexpr int kRing = 2;             // activation and weight slots in LDS
 constexpr int kEPart = 16;           // 128-long blocks per exponent part
 constexpr int kBL = 10;              // loads a wave per weight slot: 8 code, 2 scale
-// a weight slot's loads go out in four parts, one a stage: loads [kBPartStart[j], kBPartStart[j + 1])
-constexpr int kBPartStart[5] = {0, 3, 6, 8, 10};
+constexpr int kBPart = kBL / 2;      // a weight slot goes out in two parts of 5 loads
 constexpr int kPeriod = kRing * kSPS;  // stages after which the slot pattern repeats
 constexpr int kOne = 127;              // E8M0 encoding of 1.0
 constexpr int kFmtFP8 = 0, kFmtFP4 = 4;
@@ -112,7 +113,7 @@ __device__ __forceinline__ void wait_loads(int n) {
 
 template <int kPhase, bool kGrouped>
 __global__ __launch_bounds__(256, 1) void gemm_w4a8_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t sA[kRing][kM * kSK];
+    __shared__ __attribute__((aligned(1024))) uint8_t sA[kRing][kM * 128];
     __shared__ __attribute__((aligned(1024))) uint8_t sB[kRing][kN * 128];
     __shared__ __attribute__((aligned(1024))) uint8_t sE[2][kM * 16];
     __shared__ __attribute__((aligned(16))) uint8_t sMX[kRing][kN * 8];
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a8_kernel(GemmArgs a) {
     const int lane = lane_id(), wave = uniform((int)threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int e = tile.group, c0 = tile.nt * kCols;
-    const int K = a.K, nq = K / kSK, nslots = (K + kSlotK - 1) / kSlotK;
+    const int K = a.K, nq = K / kSK, nslots = (K + kSlotK - 1) / kSlotK, nd = K / kAK;
     const int nparts = (K / 128 + kEPart - 1) / kEPart;
     const bool half_last = K % kSlotK != 0;  // the last weight slot holds 128 K
     const int cpr = a.aexp_pitch >> 4;       // 16-byte parts of an exponent row
@@ -138,14 +139,14 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a8_kernel(GemmArgs a) {
         const int p = tile.row0 + r < tile.row1 ? tile.row0 + r : tile.row0;
         return (kPhase == 1 && kGrouped) ? (uint32_t)(a.perm[p] / a.k) : (uint32_t)p;
     };
-    // activation loads: instruction i of every wave fills stage rows 64 i + 16 wave + lane / 4,
-    // slot lane % 4 (sources in 16-byte units: the host keeps the codes below 64 GB)
-    uint32_t aoff[4];
+    // activation loads: instruction i (0 .. 2 nA - 1) of every wave fills slot rows
+    // 32 i + 8 wave + lane / 8, slot lane % 8, whose chunk (lane % 8) ^ ((4 wave + lane / 16) % 8)
+    // does not depend on i (sources in 16-byte units: the host keeps the codes below 64 GB)
+    const uint32_t achunk = (uint32_t)((lane & 7) ^ ((4 * wave + (lane >> 4)) & 7));
+    uint32_t aoff[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 64 * i + 16 * wave + (lane >> 2);
-        aoff[i] = src_row(r) * (uint32_t)(K / 16) + (uint32_t)((lane & 3) ^ ((r >> 2) & 3));
-    }
+    for (int i = 0; i < 8; ++i)
+        aoff[i] = src_row(32 * i + 8 * wave + (lane >> 3)) * (uint32_t)(K / 16) + achunk;
     // weight loads: instruction i (0..7) fills slot rows 64 wave + 8 i + lane / 8, slot lane % 8
     // (phase 1: rows 0..127 gate, 128..255 up, so a wave's 64 rows lie in one matrix).  The chunk
     // of a lane, (lane % 8) ^ ((row >> 1) & 7) = (lane % 8) ^ (4 (i % 2) + lane / 16), takes two
@@ -173,18 +174,17 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a8_kernel(GemmArgs a) {
     const uint32_t eoff = src_row(64 * wave + lane) * (uint32_t)cpr;
 
     // LDS byte addresses of this wave's load destinations (ring slot 0)
-    const uint32_t ldsA = lds_addr(&sA[0][0]) + 16 * wave * kSK;
+    const uint32_t ldsA = lds_addr(&sA[0][0]) + 8 * wave * 128;
     const uint32_t ldsB = lds_addr(&sB[0][0]) + 64 * wave * 128;
     const uint32_t ldsM = lds_addr(&sMX[0][0]) + 64 * wave * 8;
     const uint32_t ldsE = lds_addr(&sE[0][0]) + 64 * wave * 16;
-    const uint8_t* aptr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) aptr[i] = act + (size_t)aoff[i] * 16;
 
-    // one load of activation stage q into ring slot R (instruction i)
-    auto load_a = [&](int q, auto r_tag, auto i_tag) {
+    // one load of activation slot d into ring slot R (instruction I); a slot past the last one
+    // reloads the last one (into a free ring slot, never read)
+    auto load_a = [&](int d, auto r_tag, auto i_tag) {
         constexpr int R = decltype(r_tag)::value, I = decltype(i_tag)::value;
-        lds_dma16_at(aptr[I] + (size_t)q * kSK, ldsA + R * kM * kSK + 64 * I * kSK);
+        lds_dma16_at(act + (size_t)aoff[I] * 16 + (size_t)min(d, nd - 1) * kAK,
+                     ldsA + R * kM * 128 + 32 * I * 128);
     };
     // one load of weight slot s into ring slot R (I < 8: codes, 8..9: E8M0 scales); a slot past
     // the last one reloads the last one (into a free ring slot, never read)
@@ -206,11 +206,16 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a8_kernel(GemmArgs a) {
         lds_dma16_at((const uint8_t*)a.aexp + ((size_t)eoff + p) * 16, ldsE + (p & 1) * kM * 16);
     };
 
-    // per-lane parts of the fragment addresses (the subtile and ring parts are constants)
-    uint32_t xa[2], xb[kSPS], xm, xe;
+    // per-lane parts of the fragment addresses (the subtile and ring parts are constants); the
+    // swizzle (row >> 1) & 7 of a fragment row is (fr >> 1) & 7, its subtile starting at a
+    // multiple of 32 rows
+    uint32_t xa[kSPA][2], xb[kSPS], xm, xe;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-        xa[j] = lds_addr(&sA[0][0]) + (wm * 32 + fr) * kSK + (((2 * j + half) ^ ((fr >> 2) & 3)) << 4);
+    for (int h = 0; h < kSPA; ++h)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            xa[h][j] = lds_addr(&sA[0][0]) + (wm * 32 + fr) * 128 +
+                       (((4 * h + 2 * j + half) ^ ((fr >> 1) & 7)) << 4);
     const int bbase = kPhase == 1 ? 64 * wn : 128 * wn;
 #pragma unroll
     for (int hs = 0; hs < kSPS; ++hs)
@@ -241,9 +246,9 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a8_kernel(GemmArgs a) {
     };
     auto read_a = [&](int q, auto st_tag, auto mi_tag) {
         constexpr int ST = decltype(st_tag)::value, MI = decltype(mi_tag)::value;
-        constexpr int S = ST & 1, R = ST % kRing;
-        const uint32_t off = R * kM * kSK + 2 * MI * 32 * kSK;
-        fa[S][MI] = join2(lds_read16(xa[0] + off), lds_read16(xa[1] + off));
+        constexpr int S = ST & 1, H = ST % kSPA, R = (ST / kSPA) % kRing;
+        const uint32_t off = R * kM * 128 + 2 * MI * 32 * 128;
+        fa[S][MI] = join2(lds_read16(xa[H][0] + off), lds_read16(xa[H][1] + off));
         const int kb = q >> 1;
         sc[S][MI] = lds_read_i8(xe + ((kb / kEPart) & 1) * kM * 16 + (kb & (kEPart - 1)) +
                                 2 * MI * 32 * 16);
@@ -258,51 +263,60 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a8_kernel(GemmArgs a) {
 
     // Stage q (ST = q mod kPeriod): its first two MFMAs; the wait for this wave's loads of stage
     // q + 1 and the barrier; exponent part q / 32 + 2 when q % 32 == 31 (if it exists); then the
-    // other MFMAs with the rest of the stage's work between them, in order: part
-    // (q + 1) % 4 of weight slot (q + 1) / 4 + 2, activation stage q + 3, the reads of stage
-    // q + 1's fragments.  Past the end of K the loads reload the last weight slot or activation
-    // stage into ring slots just freed and the reads fetch fragments no MFMA uses, so that part
-    // of the stage has no branches.
-    // The newest load that stage q + 1 needs is activation stage q + 1 (its weight slot's last
-    // part and its exponent part were issued before it); the loads issued after it are those of
-    // stage q - 1: exponent part (q - 1) / 32 + 2 if it was issued, a part of a weight slot
-    // (none before stage 0) and activation stage q + 2.
+    // other MFMAs with the rest of the stage's work between them, in order: a part of a weight
+    // slot (q % 4 == 3 or 0), activation slot (q + 3) / 2 (q odd), the reads of stage q + 1's
+    // fragments.  Past the end of K the loads reload the last slots into ring slots just freed
+    // and the reads fetch fragments no MFMA uses, so that part of the stage has no branches.
+    // The newest load that stage q + 1 needs is activation slot D = (q + 1) / 2, issued last in
+    // stage 2 D - 3 (or in the prologue, D < 2); its weight slot and exponent part went out before
+    // it.  The loads issued after it are: for q == 0, activation slot 1 (prologue); for q odd,
+    // those of stage q - 1 (even): a weight part when q - 1 == 0 mod 4; for q even, those of
+    // stages q - 2 (even: a weight part when q - 2 == 0 mod 4) and q - 1 (odd: an exponent part if
+    // one was issued, a weight part when q - 1 == 3 mod 4, 2 nA activation loads).  Together:
+    // q == 0: 2 nA; q even: 2 nA + 5 (+ 1); q == 1 mod 4: 5; q == 3 mod 4: 0.
     auto stage = [&](int q, auto st_tag, auto na_tag, auto ns_tag) {
         constexpr int ST = decltype(st_tag)::value, NA = decltype(na_tag)::value;
         constexpr int NS = decltype(ns_tag)::value;
         constexpr int ST1 = (ST + 1) % kPeriod;
-        constexpr int JB = (ST + 1) % kSPS;                       // weight-slot part issued here
-        constexpr int RB = ((ST1 / kSPS) + 2) % kRing;            // its ring slot
-        constexpr int B0 = kBPartStart[JB], NB = kBPartStart[JB + 1] - B0;
+        // weight part issued here: part 0 of slot q / 4 + 2 (ST % 4 == 3) or part 1 of slot
+        // q / 4 + 1 (ST % 4 == 0), ring slot = slot % 2
+        constexpr int JB = ST % kSPS == kSPS - 1 ? 0 : (ST % kSPS == 0 ? 1 : -1);
+        constexpr int RB = JB == 0 ? (ST / kSPS) % kRing : ((ST / kSPS) + 1) % kRing;
+        constexpr int NB = JB >= 0 ? kBPart : 0;
+        constexpr int NAL = ST % 2 == 1 ? 2 * NA : 0;        // activation loads issued here
+        constexpr int RA = ((ST + 3) / kSPA) % kRing;        // their ring slot
         constexpr int NM = 4 * NS;  // MFMAs
-        constexpr int NT = NB + NA + 4 + NS;  // work items between MFMAs
+        constexpr int NT = NB + NAL + 4 + NS;  // work items between MFMAs
         constexpr int GAPS = NM > 2 ? NM - 2 : 1;
         constexpr int PER = (NT + GAPS - 1) / GAPS;  // items before each of MFMAs 2..
-        constexpr int NBPREV = kBPartStart[ST % kSPS + 1] - kBPartStart[ST % kSPS];
         if constexpr (NM > 0) mfma(st_tag, std::integral_constant<int, 0>{});
         if constexpr (NM > 1) mfma(st_tag, std::integral_constant<int, 1>{});
         __builtin_amdgcn_sched_barrier(0);
         if (q + 1 < nq) {
-            wait_loads(NA + (q > 0 ? NBPREV : 0) +
-                       ((q & 31) == 0 && q > 0 && q / 32 + 1 < nparts ? 1 : 0));
+            if constexpr (ST % 2 == 1)
+                wait_loads(ST % kSPS == 1 ? kBPart : 0);
+            else
+                wait_loads(q == 0 ? 2 * NA
+                                  : 2 * NA + kBPart +
+                                        ((q & 31) == 0 && q / 32 + 1 < nparts ? 1 : 0));
             __syncthreads();
         }
         if ((q & 31) == 31 && q / 32 + 2 < nparts) load_e(q / 32 + 2);
         __builtin_amdgcn_sched_barrier(0);
-        const int aq = min(q + 3, nq - 1);
-        const int sb_ = (q + 1) / kSPS + 2;
+        const int sb_ = q / kSPS + (JB == 0 ? 2 : 1);
+        const int da = (q + 3) / kSPA;
         // reads in the order the next stage's first MFMAs use them: n-subtile 0, m-subtile 0,
         // n-subtiles 1..3, m-subtiles 1..
         auto item = [&](auto t_tag) {
-            constexpr int T = decltype(t_tag)::value, U = T - NB - NA;
+            constexpr int T = decltype(t_tag)::value, U = T - NB - NAL;
             constexpr int BI = U == 0 ? 0 : (NS > 0 && U <= 4 ? U - 1 : U);  // n-subtile of read U
             constexpr int AI = U == 1 ? 0 : U - 4;                            // m-subtile of read U
             constexpr bool kIsB = U == 0 || (NS > 0 ? (U >= 2 && U <= 4) : U < 4);
             if constexpr (T < NB) {
-                load_b(sb_, std::integral_constant<int, RB>{}, std::integral_constant<int, B0 + T>{});
-            } else if constexpr (T < NB + NA) {
-                load_a(aq, std::integral_constant<int, ST % kRing>{},
-                       std::integral_constant<int, T - NB>{});
+                load_b(sb_, std::integral_constant<int, RB>{},
+                       std::integral_constant<int, (JB == 1 ? kBPart : 0) + T>{});
+            } else if constexpr (T < NB + NAL) {
+                load_a(da, std::integral_constant<int, RA>{}, std::integral_constant<int, T - NB>{});
             } else if constexpr (T < NT && kIsB) {
                 read_b(std::integral_constant<int, ST1>{}, std::integral_constant<int, BI>{});
             } else if constexpr (T < NT) {
@@ -325,15 +339,12 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a8_kernel(GemmArgs a) {
         constexpr int NA = decltype(na_tag)::value;
         using R0 = std::integral_constant<int, 0>;
         using R1 = std::integral_constant<int, 1>;
-        using R2 = std::integral_constant<int, 2>;
         load_e(0);
         if (nparts > 1) load_e(1);
         static_for<kBL>([&](auto i) { load_b(0, R0{}, i); });
-        static_for<kBL>([&](auto i) { load_b(1, R1{}, i); });
-        static_for<kBPartStart[1]>([&](auto i) { load_b(2, R2{}, i); });  // part 0 of slot 2
-        static_for<NA>([&](auto i) { load_a(0, R0{}, i); });
-        static_for<NA>([&](auto i) { load_a(1, R1{}, i); });  // nq >= 2
-        static_for<NA>([&](auto i) { load_a(min(2, nq - 1), R2{}, i); });
+        static_for<kBPart>([&](auto i) { load_b(1, R1{}, i); });  // part 0 of slot 1
+        static_for<2 * NA>([&](auto i) { load_a(0, R0{}, i); });
+        static_for<2 * NA>([&](auto i) { load_a(1, R1{}, i); });
         wait_loads(2 * NA);
         __syncthreads();
         static_for<4>([&](auto ni) { read_b(R0{}, ni); });
@@ -347,10 +358,6 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a8_kernel(GemmArgs a) {
             if (q + 5 < nq) stage(q + 5, std::integral_constant<int, 5>{}, na_tag, ns_tag);
             if (q + 6 < nq) stage(q + 6, std::integral_constant<int, 6>{}, na_tag, ns_tag);
             if (q + 7 < nq) stage(q + 7, std::integral_constant<int, 7>{}, na_tag, ns_tag);
-            if (q + 8 < nq) stage(q + 8, std::integral_constant<int, 8>{}, na_tag, ns_tag);
-            if (q + 9 < nq) stage(q + 9, std::integral_constant<int, 9>{}, na_tag, ns_tag);
-            if (q + 10 < nq) stage(q + 10, std::integral_constant<int, 10>{}, na_tag, ns_tag);
-            if (q + 11 < nq) stage(q + 11, std::integral_constant<int, 11>{}, na_tag, ns_tag);
         }
     };
     // nA: 64-row blocks holding tile rows; this wave's filled m-subtiles: wm + 2 mi < nvalid

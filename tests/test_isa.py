@@ -171,38 +171,40 @@ def test_gemm_waits_cover_exactly_the_needed_loads(kernel, sps, per_slot, per_st
             assert n == len(seq) - 1 - newest, (K, n, len(seq) - 1 - newest)
 
 
-B_PARTS = (0, 3, 6, 8, 10)  # the W4A8 GEMM's weight slot: loads [B_PARTS[j], B_PARTS[j + 1]) in part j
-
-
 def _issue_model_w4a8(K, na):
     """The one-wave-per-SIMD W4A8 GEMM's loads in issue order, as its source states them, and each
-    stage's wait: prologue exponent parts 0, 1 (those that exist), weight slots 0, 1 and part 0 of
-    slot 2, activation stages 0, 1, 2 (na loads each); at stage q, after the wait: exponent part
-    q / 32 + 2 when q % 32 == 31 (if it exists), part (q + 1) % 4 of weight slot (q + 1) / 4 + 2,
-    activation stage q + 3 (both issued past the end of K too: they reload into free slots).
-    Yields (loads issued so far, the wait before reading stage s's fragments, the loads stage s
-    reads), s = 0 (the prologue's wait) and s = q + 1."""
+    stage's wait: prologue exponent parts 0, 1 (those that exist), weight slot 0 (10 loads) and
+    part 0 of weight slot 1 (5), activation slots 0, 1 (128 K, 2 na loads each); at stage q, after
+    the wait: exponent part q / 32 + 2 when q % 32 == 31 (if it exists), part 0 of weight slot
+    q / 4 + 2 when q % 4 == 3, part 1 of weight slot q / 4 + 1 when q % 4 == 0, activation slot
+    (q + 3) / 2 when q is odd (weight and activation loads are issued past the end of K too: they
+    reload into free slots).  Yields (loads issued so far, the wait before reading stage s's
+    fragments, the loads stage s reads), s = 0 (the prologue's wait) and s = q + 1."""
     nq, nparts = K // 64, -(-(K // 128) // 16)
     seq = [("E", 0)] + ([("E", 1)] if nparts > 1 else [])
-    seq += [("B", 0)] * 10 + [("B", 1)] * 10 + [("B", 2)] * B_PARTS[1]
-    for d in range(3):
-        seq += [("A", d)] * na
+    seq += [("B", 0)] * 10 + [("B", 1)] * 5 + [("A", 0)] * (2 * na) + [("A", 1)] * (2 * na)
     yield list(seq), 2 * na, {("A", 0), ("B", 0), ("E", 0)}
     for q in range(nq):
         if q + 1 < nq:  # the kernel's wait immediate
-            n = (na + (B_PARTS[q % 4 + 1] - B_PARTS[q % 4] if q > 0 else 0)
-                 + (1 if q % 32 == 0 and q > 0 and q // 32 + 1 < nparts else 0))
-            yield list(seq), n, {("A", q + 1), ("B", (q + 1) // 4), ("E", (q + 1) // 32)}
+            if q % 2:
+                n = 5 if q % 4 == 1 else 0
+            else:
+                n = 2 * na if q == 0 else (2 * na + 5 + (1 if q % 32 == 0 and q // 32 + 1 < nparts
+                                                          else 0))
+            yield list(seq), n, {("A", (q + 1) // 2), ("B", (q + 1) // 4), ("E", (q + 1) // 32)}
         if q % 32 == 31 and q // 32 + 2 < nparts:
             seq += [("E", q // 32 + 2)]
-        j = (q + 1) % 4
-        seq += [("B", (q + 1) // 4 + 2)] * (B_PARTS[j + 1] - B_PARTS[j])
-        seq += [("A", q + 3)] * na
+        if q % 4 == 3:
+            seq += [("B", q // 4 + 2)] * 5
+        if q % 4 == 0:
+            seq += [("B", q // 4 + 1)] * 5
+        if q % 2:
+            seq += [("A", (q + 3) // 2)] * (2 * na)
 
 
 @pytest.mark.parametrize("na", [1, 2, 3, 4])
 def test_w4a8_waits_cover_exactly_the_needed_loads(na):
-    """As above for the W4A8 GEMM, whose waves all issue na loads per activation stage (na = the
+    """As above for the W4A8 GEMM, whose waves all issue 2 na loads per activation slot (na = the
     64-row blocks holding tile rows) and whose waits come before reading the next stage's
     fragments: every wait leaves exactly the loads issued after the newest one it needs."""
     for K in range(128, 8192 + 1, 128):
