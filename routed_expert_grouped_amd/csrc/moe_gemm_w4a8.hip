@@ -60,7 +60,6 @@ constexpr int kEPart = 16;           // 128-long blocks per exponent part
 constexpr int kBL = 10;              // loads a wave per weight slot: 8 code, 2 scale
 constexpr int kBPart = kBL / 2;      // a weight slot goes out in two parts of 5 loads
 constexpr int kPeriod = kRing * kSPS;  // stages after which the slot pattern repeats
-constexpr int kOne = 127;              // E8M0 encoding of 1.0
 constexpr int kFmtFP8 = 0, kFmtFP4 = 4;
 
 __device__ __forceinline__ i32x8 widen(u32x4 lo) {
@@ -94,8 +93,8 @@ __device__ __forceinline__ int lds_read_u8(uint32_t addr) {
     return *(const __attribute__((address_space(3))) uint8_t*)(size_t)addr;
 }
 
-__device__ __forceinline__ int lds_read_i8(uint32_t addr) {
-    return *(const __attribute__((address_space(3))) int8_t*)(size_t)addr;
+__device__ __forceinline__ uint32_t lds_read_u32(uint32_t addr) {
+    return *(const __attribute__((address_space(3))) uint32_t*)(size_t)addr;
 }
 
 // s_waitcnt vmcnt(n) for a run-time n (0..15)
@@ -235,7 +234,11 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a8_kernel(GemmArgs a) {
 
     // two fragment sets: stage q's MFMAs read set q % 2 while set (q + 1) % 2 is filled
     i32x8 fa[2][4], fb[2][4];
-    int sc[2][4], sb[2][4];  // exponent e of the activation rows (E8M0 byte 127 + e); E8M0 bytes
+    // activation exponents: one 4-byte word per m-subtile row holds the exponents e of four
+    // 128-long blocks (eight stages), read once per eight stages; sc8 holds them as E8M0 bytes
+    // (127 + e), the MFMA picking the block's byte by op_sel.  E8M0 weight scales: a byte a stage.
+    uint32_t se[4], sc8[4];
+    int sb[2][4];
 
     // fragment reads of stage q (ST = q mod kPeriod) into set ST % 2: n-subtile ni, m-subtile mi
     auto read_b = [&](auto st_tag, auto ni_tag) {
@@ -249,15 +252,18 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a8_kernel(GemmArgs a) {
         constexpr int S = ST & 1, H = ST % kSPA, R = (ST / kSPA) % kRing;
         const uint32_t off = R * kM * 128 + 2 * MI * 32 * 128;
         fa[S][MI] = join2(lds_read16(xa[H][0] + off), lds_read16(xa[H][1] + off));
-        const int kb = q >> 1;
-        sc[S][MI] = lds_read_i8(xe + ((kb / kEPart) & 1) * kM * 16 + (kb & (kEPart - 1)) +
-                                2 * MI * 32 * 16);
+        if constexpr (ST % 8 == 0) {  // first stage of four blocks: their exponents
+            const int kb = q >> 1;      // a multiple of 4
+            se[MI] = lds_read_u32(xe + ((kb / kEPart) & 1) * kM * 16 + (kb & (kEPart - 1)) +
+                                  2 * MI * 32 * 16);
+        }
     };
     auto mfma = [&](auto st_tag, auto j_tag) {
         constexpr int S = decltype(st_tag)::value & 1, J = decltype(j_tag)::value;
         constexpr int MI = J / 4, NI = J % 4;
+        constexpr int ST = decltype(st_tag)::value;
         acc[MI][NI] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fa[S][MI], fb[S][NI], acc[MI][NI], kFmtFP8, kFmtFP4, 0, kOne + sc[S][MI], 0,
+            fa[S][MI], fb[S][NI], acc[MI][NI], kFmtFP8, kFmtFP4, (ST / 2) % 4, (int)sc8[MI], 0,
             sb[S][NI]);
     };
 
@@ -289,6 +295,12 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a8_kernel(GemmArgs a) {
         constexpr int NT = NB + NAL + 4 + NS;  // work items between MFMAs
         constexpr int GAPS = NM > 2 ? NM - 2 : 1;
         constexpr int PER = (NT + GAPS - 1) / GAPS;  // items before each of MFMAs 2..
+        if constexpr (ST % 8 == 0) {
+            // int8 e -> E8M0 127 + e in every byte: e ^ 0x80 is e + 128 in [1, 255] (e >= -127),
+            // so subtracting 1 from each byte borrows nothing across bytes
+#pragma unroll
+            for (int mi = 0; mi < NS; ++mi) sc8[mi] = (se[mi] ^ 0x80808080u) - 0x01010101u;
+        }
         if constexpr (NM > 0) mfma(st_tag, std::integral_constant<int, 0>{});
         if constexpr (NM > 1) mfma(st_tag, std::integral_constant<int, 1>{});
         __builtin_amdgcn_sched_barrier(0);
