@@ -82,6 +82,8 @@ def test_mxfp4_dsv3_decode_full():
     mid(T=200, H=2560, E=8, k=2, wdtype="mxfp4"),               # 10 slots, 32-byte exponent rows
     mid(T=160, H=640, E=8, k=2, wdtype="mxfp4"),                # 2.5 slots; phase 2 dequantises
     mid(T=144, H=8192, I=256, E=2, k=2, wdtype="mxfp4"),        # K = 8192, the GEMM's largest
+    mid(T=200, H=256, I=128, E=2, k=1, wdtype="mxfp4"),         # smallest K: 256 (one weight
+                                                                # slot), 128 (two stages)
     mid(T=200, H=16384, I=256, E=4, k=2, wdtype="mxfp4"),       # phase 1 dequantises (K > 8192)
     mid(T=37, E=64, k=8, wdtype="mxfp4"),                       # few rows: dequantise + GEMV
 ])
