@@ -196,6 +196,10 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
     float u0 = 0.0f, u1 = 0.0f;
     uint32_t m0 = ~0u, m1 = ~0u;
     int sc[4] = {kE8M0One, kE8M0One, kE8M0One, kE8M0One};  // E8M0 activation scales of the block
+    // the E8M0 scales of four blocks per m-subtile row, read as one word every fourth block
+    // (int8 e -> 127 + e in every byte: e ^ 0x80 = e + 128 is at least 1 for e >= -127, so
+    // subtracting 1 from each byte borrows nothing across bytes); block kb takes byte kb % 4
+    uint32_t sw[4] = {0u, 0u, 0u, 0u};
     // rescales the accumulators of the first NS m-subtiles (the others are never stored)
     auto rescale = [&](float r0, float r1, auto ns_tag) {
         constexpr int NS = decltype(ns_tag)::value;
@@ -263,9 +267,14 @@ __global__ __launch_bounds__(512, 1) void gemm_a8_kernel(GemmArgs a) {
             }
         }
         if ((ST & 1) == 0) {  // first stage of 128-long block kb: its activation exponents
-            const uint8_t* E = sE[(kb / kEPart) & 1] + (kb & (kEPart - 1));
+            if ((kb & 3) == 0) {
+                const uint8_t* E = sE[(kb / kEPart) & 1] + (kb & (kEPart - 1));
 #pragma unroll
-            for (int mi = 0; mi < NS; ++mi) sc[mi] = kE8M0One + (int)(int8_t)E[eaddr[mi]];
+                for (int mi = 0; mi < NS; ++mi)
+                    sw[mi] = (*(const uint32_t*)&E[eaddr[mi]] ^ 0x80808080u) - 0x01010101u;
+            }
+#pragma unroll
+            for (int mi = 0; mi < NS; ++mi) sc[mi] = (int)(sw[mi] >> (8 * (kb & 3)));
         }
         const uint8_t* A = sA[ST % kARing];
         const uint8_t* B = sB[(ST / kSPS) % kBRing];
