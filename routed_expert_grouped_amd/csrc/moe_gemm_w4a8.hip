@@ -1,18 +1,17 @@
 // moe_gemm_w4a8.hip -- the grouped expert GEMM with FP8 activations and MXFP4 weights (W4A8),
 // one wave per SIMD.
 //
-// The arithmetic is that of the FP8-activation GEMM with 4-bit weights in moe_gemm_a8.hip: E4M3FN
-// activation codes with one power-of-two scale per row and 128-long K block, E2M1 weight codes
-// with their E8M0 scale per 32-long K group, both scales applied by
-// v_mfma_scale_f32_32x32x64_f8f6f4 itself, fp32 sums.  Nothing is rescaled, so the sums never
-// pass through the vector ALU until the epilogue.  What differs is the layout of the work on a
-// CU:
+// E4M3FN activation codes with one power-of-two scale per row and 128-long K block (the
+// FP8-activation mode's quantisation, moe_quant.hip) times E2M1 weight codes with their E8M0 scale
+// per 32-long K group, both scales applied by v_mfma_scale_f32_32x32x64_f8f6f4 itself, fp32 sums.
+// Nothing is rescaled (unlike FP8 weights with fp32 block scales, moe_gemm_a8.hip), so the sums
+// never pass through the vector ALU until the epilogue, and the work is laid out on a CU as:
 //   * 4 waves, one per SIMD, each computing 128 rows x 128 weight rows of the 256 x 256 tile:
 //     16 MFMAs a 64-long stage.  The 256 fp32 sums sit in the accumulation registers, which
 //     leaves the vector registers free for two sets of operand fragments.
 //   * While a stage's MFMAs run, the wave reads the next stage's fragments from LDS into the
 //     other set, so no MFMA waits for an LDS read.  A 128 x 128 wave tile reads 12 KB of
-//     fragments a stage for 16 MFMAs, where 128 x 64 wave tiles read 10 KB for 8.
+//     fragments a stage for 16 MFMAs (a 128 x 64 one would read 10 KB for 8).
 //
 // LDS (140 KB) holds every operand row as whole 128-byte lines, eight 16-byte chunks, chunk c at
 // slot c ^ ((row >> 1) & 7):
@@ -60,6 +59,8 @@ constexpr int kEPart = 16;           // 128-long blocks per exponent part
 constexpr int kBL = 10;              // loads a wave per weight slot: 8 code, 2 scale
 constexpr int kBPart = kBL / 2;      // a weight slot goes out in two parts of 5 loads
 constexpr int kPeriod = kRing * kSPS;  // stages after which the slot pattern repeats
+// an activation exponent word covers four blocks, eight stages: one loop period
+static_assert(kPeriod == 8, "the exponent words are read at the first stage of each period");
 constexpr int kFmtFP8 = 0, kFmtFP4 = 4;
 
 __device__ __forceinline__ i32x8 widen(u32x4 lo) {
