@@ -18,12 +18,26 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+// fp32 -> bf16, round to nearest even, by gfx950's conversion instruction (v_cvt_pk_bf16_f32); a
+// NaN stays a NaN.  The bit-level form (add 0x7fff + lsb, keep the high half) rounds every finite
+// value the same way, but its NaN test costs a branch per value.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (one conversion instruction), a in the low half
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// SiLU(g) * u: g / (1 + e^-g) with the hardware reciprocal (about 1 ulp) in place of the IEEE
+// division; the result is rounded to bf16 next
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // Eight OCP E4M3FN codes (two little-endian words) -> eight bf16 values, exactly: every E4M3FN

@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(GemmArgs a) {
 #pragma unroll
             for (int g = 0; g < kG / 2; ++g) {
                 const float gt = acc[g][r], u = acc[g + kG / 2][r];
-                const float hval = gt / (1.0f + __expf(-gt)) * u;
+                const float hval = silu_mul(gt, u);
                 a.out[(size_t)row * a.N + n0 + 16 * g + m] = f32_to_bf16(hval);
             }
         } else {

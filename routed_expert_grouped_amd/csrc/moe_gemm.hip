@@ -213,10 +213,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
             uint16_t* o = a.out + (size_t)p * a.N + c0 + fr;
             if (kPhase == 1) {
                 const float g = acc[mi][0][r], u = acc[mi][1][r];
-                o[wn * 32] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+                o[wn * 32] = f32_to_bf16(silu_mul(g, u));
             } else {
-                o[wn * 64] = f32_to_bf16(acc[mi][0][r]);
-                o[wn * 64 + 32] = f32_to_bf16(acc[mi][1][r]);
+                const uint32_t b = f32x2_to_bf16x2(acc[mi][0][r], acc[mi][1][r]);
+                o[wn * 64] = (uint16_t)b;
+                o[wn * 64 + 32] = (uint16_t)(b >> 16);
             }
         }
     }
@@ -463,10 +464,11 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_q256_kernel(GemmArgs a) {
             uint16_t* o = a.out + (size_t)p * a.N + c0 + fr;
             if (kPhase == 1) {
                 const float g = acc[mi][0][x], u = acc[mi][1][x];
-                o[wn * 32] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+                o[wn * 32] = f32_to_bf16(silu_mul(g, u));
             } else {
-                o[wn * 64] = f32_to_bf16(acc[mi][0][x]);
-                o[wn * 64 + 32] = f32_to_bf16(acc[mi][1][x]);
+                const uint32_t b = f32x2_to_bf16x2(acc[mi][0][x], acc[mi][1][x]);
+                o[wn * 64] = (uint16_t)b;
+                o[wn * 64 + 32] = (uint16_t)(b >> 16);
             }
         }
     }

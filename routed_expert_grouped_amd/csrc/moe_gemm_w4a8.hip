@@ -90,14 +90,6 @@ __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
     return *(const __attribute__((address_space(3))) u32x4*)(size_t)addr;
 }
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// two floats to bf16, round to nearest even (v_cvt_pk_bf16_f32), first in the low half
-__device__ __forceinline__ uint32_t to_bf16x2(f32x2 v) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
 __device__ __forceinline__ int lds_read_u8(uint32_t addr) {
     return *(const __attribute__((address_space(3))) uint8_t*)(size_t)addr;
 }
@@ -407,20 +399,14 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a8_kernel(GemmArgs a) {
             if (p >= tile.row1) continue;
             uint16_t* o = a.out + (size_t)p * a.N + c0 + fr;
             if (kPhase == 1) {
-                f32x2 v;
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    const float g = acc[mi][ni][x], u = acc[mi][ni + 2][x];
-                    v[ni] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-                }
-                const uint32_t b = to_bf16x2(v);
+                const uint32_t b = f32x2_to_bf16x2(silu_mul(acc[mi][0][x], acc[mi][2][x]),
+                                                   silu_mul(acc[mi][1][x], acc[mi][3][x]));
                 o[64 * wn] = (uint16_t)b;
                 o[64 * wn + 32] = (uint16_t)(b >> 16);
             } else {
 #pragma unroll
                 for (int ni = 0; ni < 4; ni += 2) {
-                    const f32x2 v = {acc[mi][ni][x], acc[mi][ni + 1][x]};
-                    const uint32_t b = to_bf16x2(v);
+                    const uint32_t b = f32x2_to_bf16x2(acc[mi][ni][x], acc[mi][ni + 1][x]);
                     o[128 * wn + 32 * ni] = (uint16_t)b;
                     o[128 * wn + 32 * ni + 32] = (uint16_t)(b >> 16);
                 }

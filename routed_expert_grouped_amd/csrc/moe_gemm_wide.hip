@@ -258,10 +258,11 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_wide_kernel(GemmArgs a) {
             uint16_t* o = a.out + (size_t)p * a.N + c0 + fr;
             if (kPhase == 1) {
                 const float g = acc[mi][0][x], u = acc[mi][1][x];
-                o[wave * 32] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+                o[wave * 32] = f32_to_bf16(silu_mul(g, u));
             } else {
-                o[wave * 64] = f32_to_bf16(acc[mi][0][x]);
-                o[wave * 64 + 32] = f32_to_bf16(acc[mi][1][x]);
+                const uint32_t b = f32x2_to_bf16x2(acc[mi][0][x], acc[mi][1][x]);
+                o[wave * 64] = (uint16_t)b;
+                o[wave * 64 + 32] = (uint16_t)(b >> 16);
             }
         }
     }
