@@ -285,14 +285,16 @@ def test_expert_ffn_call_against_the_oracle(cfg):
 
 
 @pytest.mark.parametrize("T,k,H,E", [(300, 8, 7168, 256), (77, 13, 512, 40), (16, 8, 7168, 256),
-                                     (5, 32, 256, 64)])
+                                     (5, 32, 256, 64), (40, 1, 256, 8), (50, 2, 7168, 16),
+                                     (33, 6, 1024, 64)])
 def test_combine_is_the_slot_ordered_fp32_fma_sum(T, k, H, E):
     """moe_combine and moe_combine_partial bit for bit against the sum they state: fp32 fused
     multiply-adds S + w_0 y_0 + ... + w_{k-1} y_{k-1} in slot order (skipping other ranks'
     experts in the partial form), rounded to bf16.  Emulated exactly in float64: each product
     of an fp32 weight and a bf16 value, plus the fp32 accumulator, is exact in double, so
-    rounding it to fp32 is the fused operation.  k = 13 and 32 leave a partial chunk of the
-    kernel's 8-row load groups."""
+    rounding it to fp32 is the fused operation.  The kernel reads y in groups of 8, then 4, then
+    single rows: k = 1, 2, 6, 8, 13 and 32 take every mix of them, with and without a shared
+    row."""
     rng = np.random.default_rng(T * k)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
     w = rng.random((T, k)).astype(np.float32)
@@ -302,6 +304,7 @@ def test_combine_is_the_slot_ordered_fp32_fma_sum(T, k, H, E):
     d = lambda a: (a if torch.is_tensor(a) else torch.from_numpy(a)).to(DEV)
     yb, Sb = d(y.view(torch.int16)), d(S.view(torch.int16))
     out = moe.moe_combine(yb, d(inv), d(w), Sb, T, k, H)
+    out0 = moe.moe_combine(yb, d(inv), d(w), None, T, k, H)
     e0, e1 = 3, E // 2
     part = moe.moe_combine_partial(yb, d(inv), d(ids), d(w), e0, e1, None, T, k, H)
     torch.cuda.synchronize()
@@ -317,4 +320,5 @@ def test_combine_is_the_slot_ordered_fp32_fma_sum(T, k, H, E):
         return torch.from_numpy(acc).to(torch.bfloat16).view(torch.int16).numpy()
 
     np.testing.assert_array_equal(out.cpu().numpy(), fma_sum(Sf, 0, E))
+    np.testing.assert_array_equal(out0.cpu().numpy(), fma_sum(np.zeros((T, H)), 0, E))
     np.testing.assert_array_equal(part.cpu().numpy(), fma_sum(np.zeros((T, H)), e0, e1))
