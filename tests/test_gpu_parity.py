@@ -286,7 +286,7 @@ def test_expert_ffn_call_against_the_oracle(cfg):
 
 @pytest.mark.parametrize("T,k,H,E", [(300, 8, 7168, 256), (77, 13, 512, 40), (16, 8, 7168, 256),
                                      (5, 32, 256, 64), (40, 1, 256, 8), (50, 2, 7168, 16),
-                                     (33, 6, 1024, 64)])
+                                     (33, 6, 1024, 64), (9, 8, 8200, 16), (12, 3, 40, 8)])
 def test_combine_is_the_slot_ordered_fp32_fma_sum(T, k, H, E):
     """moe_combine and moe_combine_partial bit for bit against the sum they state: fp32 fused
     multiply-adds S + w_0 y_0 + ... + w_{k-1} y_{k-1} in slot order (skipping other ranks'
@@ -294,7 +294,8 @@ def test_combine_is_the_slot_ordered_fp32_fma_sum(T, k, H, E):
     of an fp32 weight and a bf16 value, plus the fp32 accumulator, is exact in double, so
     rounding it to fp32 is the fused operation.  The kernel reads y in groups of 8, then 4, then
     single rows: k = 1, 2, 6, 8, 13 and 32 take every mix of them, with and without a shared
-    row."""
+    row.  A workgroup covers up to 8192 columns of a token: H = 8200 takes two per token, H = 40
+    one partly filled wave."""
     rng = np.random.default_rng(T * k)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
     w = rng.random((T, k)).astype(np.float32)
