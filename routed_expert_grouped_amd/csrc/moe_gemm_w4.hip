@@ -51,7 +51,9 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_kernel(GemmArgs a) {
 
     constexpr int kCols = kPhase == 1 ? kW4N / 2 : kW4N;
     Tile tile;
-    if (!find_tile(kGrouped ? a.offsets : nullptr, a.n_groups, a.rows, kW4M, a.N / kCols, tile))
+    // phase 2 takes N = 128 mod 256 too: the last column tile's upper 128 weight rows are absent
+    if (!find_tile(kGrouped ? a.offsets : nullptr, a.n_groups, a.rows, kW4M, (a.N + kCols - 1) / kCols,
+                   tile))
         return;
 
     const int lane = lane_id(), wave = uniform((int)(threadIdx.x >> 6));
@@ -79,9 +81,9 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_kernel(GemmArgs a) {
         if (kPhase == 1) {
             base = (const uint8_t*)(r < 128 ? m0 : m1);
             wr = c0 + (r & 127);
-        } else {
+        } else {  // rows past N (the absent half of a last tile) read row N - 1, never stored
             base = (const uint8_t*)m0;
-            wr = c0 + r;
+            wr = min(c0 + r, a.N - 1);
         }
         return base + ((size_t)e * a.N + wr) * row_bytes;
     };
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_kernel(GemmArgs a) {
             if (kPhase == 1) {
                 const float g = acc[mi][0][x], u = acc[mi][1][x];
                 o[wn * 32] = f32_to_bf16(silu_mul(g, u));
-            } else {
+            } else if (c0 + wn * 64 < a.N) {  // a wave's 64 columns are all present or all absent
                 const uint32_t b = f32x2_to_bf16x2(acc[mi][0][x], acc[mi][1][x]);
                 o[wn * 64] = (uint16_t)b;
                 o[wn * 64 + 32] = (uint16_t)(b >> 16);
@@ -259,7 +261,8 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_kernel(GemmArgs a) {
 
 bool w4_gemm_fits(int phase, const GemmArgs& a) {
     if (!a.fp4 || use_gemv(a.rows, a.n_groups)) return false;
-    if (a.K % kW4BK != 0 || a.N % (phase == 1 ? kW4N / 2 : kW4N) != 0) return false;
+    // phase 1: 128 h columns a tile; phase 2: 256 y columns a tile, the last one possibly half
+    if (a.K % kW4BK != 0 || a.N % (kW4N / 2) != 0) return false;
     // activation rows are addressed by 32-bit 16-byte chunk indices
     return (int64_t)a.rows * (a.K / 8) < (int64_t(1) << 32);
 }
@@ -269,7 +272,7 @@ moe_status launch_gemm_w4(int phase, const GemmArgs& a, hipStream_t st) {
     const int cols = phase == 1 ? kW4N / 2 : kW4N;
     const int groups = a.offsets ? a.n_groups : 1;
     const int64_t mt = ((int64_t)a.rows + kW4M - 1) / kW4M + std::min<int64_t>(groups, a.rows);
-    const int64_t wgs = mt * (a.N / cols);
+    const int64_t wgs = mt * ((a.N + cols - 1) / cols);
     if (wgs > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((wgs + 7) & ~int64_t(7))), block(512);
     const bool g = a.offsets != nullptr;

@@ -54,7 +54,8 @@ def test_mxfp4_decode_and_scale_layout_exhaustive(I, route):
     dict(T=16, H=256, I=128, E=16, k=2, score_fn="softmax", scores="normal", wdtype="mxfp4"),
     mid(wdtype="mxfp4"),                       # many rows per expert: the 4-bit GEMM
     mid(T=37, E=64, k=8, wdtype="mxfp4"),
-    mid(T=160, H=640, E=8, k=2, wdtype="mxfp4"),              # phase 2 (N = 640) on the decode kernel
+    mid(T=160, H=640, E=8, k=2, wdtype="mxfp4"),              # phase 2 (N = 640): 2.5 column
+                                                              # tiles of the 4-bit GEMM
     mid(T=30, H=128, I=384, E=4, k=2, wdtype="mxfp4"),       # K = 128 in phase 1
     mid(T=60, H=16384, I=256, E=4, k=2, wdtype="mxfp4"),     # the largest H: two scale windows
     mid(T=40, H=256, I=8320, E=3, k=1, wdtype="mxfp4"),      # phase 2: 65 blocks (32 + 32 + 1)
@@ -64,6 +65,8 @@ def test_mxfp4_decode_and_scale_layout_exhaustive(I, route):
     mid(T=300, E=4, k=1, score_fn="softmax", wdtype="mxfp4"),  # 4-bit GEMM: deep m-tile stacks
     mid(T=200, H=16384, I=256, E=4, k=2, wdtype="mxfp4"),    # 4-bit GEMM at K = 16384
     mid(T=200, H=256, I=8320, E=3, k=1, wdtype="mxfp4"),     # 4-bit GEMM phase 2: 65 slots (odd)
+    mid(T=300, H=384, E=8, k=4, wdtype="mxfp4"),             # phase 2 N = 384: one whole and one
+                                                              # half column tile, 150 rows/expert
 ])
 def test_mxfp4_layer(cfg):
     layer = layer_for(cfg, seed=1)
