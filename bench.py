@@ -2,8 +2,8 @@
 
 A step is one pass of the whole path over one batch of synthetic tokens, with every input and
 weight resident in HBM:  route -> permute -> routed gate/up -> routed down -> combine on the
-main stream, and the shared expert's gate/up -> down on a second stream that joins before
-combine.
+main stream, with the shared expert's gate/up and down inside the routed launches at decode
+sizes and on a second stream that joins before combine at prefill sizes.
 
 The headline `value` is tokens/s of the DeepSeek-V3-shaped decode layer (T=16, 256 experts,
 top-8, FP8 block-scaled weights).  The same line carries the 4096-token prefill layer under

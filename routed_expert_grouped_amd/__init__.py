@@ -353,19 +353,20 @@ def _permute_ws(T, k, E, device):
 class MoeLayer:
     """Buffers and the call sequence of one MoE layer forward: route -> permute (one launch,
     moe_route_permute, for T*k <= 2048) -> routed gate/up -> routed down -> combine on the
-    caller's stream, and the shared expert (which only
-    needs x) on a second stream that runs alongside the routed experts and joins before combine.
+    caller's stream.  The shared expert (which only needs x) runs inside the routed launches at
+    decode sizes (fuse_shared, below), and otherwise on a second stream that runs alongside the
+    routed experts and joins before combine.
 
     `experts` and `shared` are objects accepted by expert_weights(); `x` is bf16 bits [T, H]
     (torch.int16) and `scores` fp32 [T, E], all on the GPU.
 
     fuse_shared: at decode sizes (T*k <= 32*E, bf16 activations) the shared expert can run inside
     the routed launches as an extra group (moe_expert_gate_up_shared / moe_expert_down_shared):
-    one grid per phase, no second stream, no cross-stream waits.  "auto" does so for small
-    expert matrices (H*I <= 4M weights), where the layer is launch-bound (tiny layer: 0.035
-    against 0.092 ms a step); for DeepSeek-V3-sized experts the side stream measured faster
-    (FP8 0.647 against 0.650 ms, MXFP4 0.411 against 0.427 ms).  True / False force it.  `h`,
-    `y`, `sh_h` and `sh_y` are then views of the shared buffers.
+    one grid per phase, no second stream, no cross-stream waits; the extra group's tiles take the
+    first workgroups, spread over the XCDs.  "auto" does so wherever it applies: the tiny layer
+    0.035 against 0.092 ms a step, the DeepSeek-V3 decode layer 0.638 against 0.648 ms (FP8
+    weights) and 0.363 against 0.372 ms (MXFP4) with the side stream.  True / False force it.
+    `h`, `y`, `sh_h` and `sh_y` are then views of the shared buffers.
 
     overlap_shared=False runs the shared expert on the caller's stream after the routed experts
     instead of on the side stream (measured equal or slower at every layer size: the side stream
@@ -407,7 +408,7 @@ class MoeLayer:
                 self.sh_h = self.sh_ws[:max(1, T) * I * 2].view(torch.int16).view(-1, I)
         # the shared expert as an extra group of the routed decode launches
         if fuse_shared == "auto":
-            fuse_shared = H * I <= (1 << 22)
+            fuse_shared = True
         self.fused = (bool(fuse_shared) and act == "bf16" and shared is not None and T > 0
                       and T * k <= 32 * E and self.ws_.dtype == self.w.dtype
                       and self.ws_.H == self.w.H and self.ws_.I == self.w.I)

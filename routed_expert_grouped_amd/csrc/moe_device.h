@@ -122,10 +122,13 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
 // rounded up to 8), so each XCD walks one contiguous range of logical tiles, and tiles that are
 // close in that range run at about the same time on the same L2.
 //
-// An optional extra group (extra_rows > 0) follows the n_groups groups: its rows start at
-// extra_base and it has extra_rows of them.  extra_base is passed in rather than read from
-// offsets[n_groups], so that a slice of the grouping (one expert range, whose offsets[n_groups]
-// ends before the last grouped row) still puts the extra rows after all grouped rows.
+// An optional extra group (extra_rows > 0, group index n_groups) has extra_rows rows starting
+// at extra_base.  extra_base is passed in rather than read from offsets[n_groups], so that a
+// slice of the grouping (one expert range, whose offsets[n_groups] ends before the last grouped
+// row) still puts the extra rows after all grouped rows.  Its tiles take the first workgroups
+// (rounded up to a multiple of 8), in plain dispatch order: they spread over all XCDs and run
+// at the start, where at the end of one XCD's range they would lengthen that XCD's work alone.
+// The grouped tiles follow on the workgroups after them, in the XCD-aware order.
 //
 // Within a group, logical tiles go in supertiles of up to kSuperM m-tiles: the m-tiles of one
 // supertile are the fastest index, its n-tiles the next.  Workgroups that read the same weight
@@ -145,11 +148,23 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
                                           int identity_rows, int BM, int n_tiles, Tile& t,
                                           int extra_rows = 0, int extra_base = 0) {
     const int lane = lane_id();
-    const int wg = (int)blockIdx.x;
+    int wg = (int)blockIdx.x;
+    if (extra_rows > 0) {
+        const int xm = (extra_rows + BM - 1) / BM, X = xm * n_tiles, X8 = (X + 7) & ~7;
+        if (wg < X8) {
+            if (wg >= X) return false;
+            t.group = n_groups;
+            t.nt = wg % n_tiles;
+            t.row0 = extra_base + (wg / n_tiles) * BM;
+            t.row1 = min(t.row0 + BM, extra_base + extra_rows);
+            return true;
+        }
+        wg -= X8;  // the grouped tiles from here
+    }
     int total_m, incl = 0, local = 0;
-    const int groups = n_groups + (extra_rows > 0 ? 1 : 0);
+    const int groups = n_groups;
     const int G = (groups + kWave - 1) / kWave;  // groups per lane, contiguous
-    auto count = [&](int g) { return g < n_groups ? offsets[g + 1] - offsets[g] : extra_rows; };
+    auto count = [&](int g) { return offsets[g + 1] - offsets[g]; };
     if (offsets == nullptr) {
         total_m = (identity_rows + BM - 1) / BM;
     } else {
@@ -200,7 +215,7 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
         for (int i = 0; i < G; ++i) {
             const int g = lane * G + i;
             if (g >= groups) break;
-            const int a = g < n_groups ? offsets[g] : extra_base, n = count(g);
+            const int a = offsets[g], n = count(g);
             const int tiles = (n + BM - 1) / BM;
             if (mt < m0 + tiles) {
                 group = g;

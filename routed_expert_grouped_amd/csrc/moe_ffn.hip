@@ -342,10 +342,13 @@ static moe_status launch_phase(int phase, const GemmArgs& a, hipStream_t st) {
                     : a.fp8      ? (kb % 4 == 0 ? 4 : kb % 2 == 0 ? 2 : 1)
                     : (a.fp4 && G == 4 && kb % 2 == 0) ? 2 : 1;
     const int cols = W / split * (phase == 1 ? 8 : 16) * G;
-    const int groups = (a.offsets ? a.n_groups : 1) + (a.extra_rows > 0 ? 1 : 0);
-    const int64_t wgs = (int64_t)max_mtiles(a.rows + a.extra_rows, groups, kGemvBM) * (a.N / cols);
+    // the extra group's tiles (rounded up to 8) first, then the grouped ones (find_tile)
+    const int groups = a.offsets ? a.n_groups : 1;
+    const int64_t xtiles = a.extra_rows > 0
+        ? (((int64_t)(a.extra_rows + kGemvBM - 1) / kGemvBM * (a.N / cols) + 7) & ~int64_t(7)) : 0;
+    const int64_t wgs = xtiles + (((int64_t)max_mtiles(a.rows, groups, kGemvBM) * (a.N / cols) + 7) & ~int64_t(7));
     if (wgs > INT32_MAX) return MOE_ERR_UNSUPPORTED;
-    const dim3 grid((unsigned)((wgs + 7) & ~int64_t(7))), block(W * 64);
+    const dim3 grid((unsigned)wgs), block(W * 64);
 #define MOE_GEMV(F, P, GR) gemv_kernel<F, P, GR, W, 1, 2><<<grid, block, 0, st>>>(a)
 #define MOE_GEMV4(P, GR)                                                           \
     (G == 2 ? gemv_kernel<kMXFP4, P, GR, W, 1, 2><<<grid, block, 0, st>>>(a)        \
