@@ -196,7 +196,7 @@ def summarize_traffic(key, fetch_dir, write_dir, commands):
     read for it."""
     import re
 
-    fetch, write = pmc_per_kernel(fetch_dir), pmc_per_kernel(write_dir)
+    fetch = pmc_per_kernel(fetch_dir)
 
     def probe_copies(d, counter):
         # the device copies of the 1 GiB probe: the copy kernel's largest dispatches (the same
@@ -216,16 +216,27 @@ def summarize_traffic(key, fetch_dir, write_dir, commands):
     if len(gu) != 1:
         raise SystemExit(f"expected one routed gate/up kernel, found {gu}")
     k = gu[0]
+
+    def routed_only(d, counter):
+        # the routed gate/up launches alone: at decode sizes the layer's own launch also carries
+        # the shared expert's tiles, on extra workgroups, so only the smallest grid is kept
+        rows = [r for r in _csv_rows(d, "counter_collection.csv")
+                if r["Kernel_Name"] == k and r["Counter_Name"] == counter]
+        g = min(int(r["Grid_Size"]) for r in rows)
+        vals = [float(r["Counter_Value"]) for r in rows if int(r["Grid_Size"]) == g]
+        return sum(vals) / len(vals), len(vals)
+
+    fk, nd = routed_only(fetch_dir, "FETCH_SIZE")
+    wk, _ = routed_only(write_dir, "WRITE_SIZE")
     rec = dict(copy_probe_bytes=probe, copy_fetch_kib=copy_f, copy_write_kib=copy_w,
-               fetch_factor=ff, write_factor=wf, kernel=k, dispatches=fetch[k]["dispatches"],
-               fetch_kib=fetch[k]["FETCH_SIZE"], write_kib=write[k]["WRITE_SIZE"],
-               traffic_bytes=int(round(fetch[k]["FETCH_SIZE"] * 1024 * ff +
-                                       write[k]["WRITE_SIZE"] * 1024 * wf)),
+               fetch_factor=ff, write_factor=wf, kernel=k, dispatches=nd,
+               fetch_kib=fk, write_kib=wk,
+               traffic_bytes=int(round(fk * 1024 * ff + wk * 1024 * wf)),
                source_files=kernel_sources(k), source_digest=source_digest(kernel_sources(k)),
                commands=commands,
-               note="counters in KiB per dispatch, averaged over the dispatches of the kernel; "
-                    "each scaled by (known bytes of a 1 GiB device copy) / (what the same counter "
-                    "read for that copy)")
+               note="counters in KiB per dispatch, averaged over the kernel's dispatches with the "
+                    "smallest grid (the routed launch alone); each scaled by (known bytes of a 1 GiB "
+                    "device copy) / (what the same counter read for that copy)")
     path = os.path.join(ROOT, "profiles", f"gate_up_{key}_traffic.json")
     json.dump(rec, open(path, "w"), indent=1)
     return path
