@@ -64,6 +64,9 @@ moe_status launch_gemm_a8(int phase, const GemmArgs& a, hipStream_t st);
 // MXFP4 weights with FP8 activations (W4A8): the one-wave-per-SIMD GEMM (moe_gemm_w4a8.hip),
 // for the shapes a8_gemm_fits accepts
 bool w4a8_gemm_fits(int phase, const GemmArgs& a);
+// FP8 activations and FP8 weights, down projection with 160 x 512 tiles (moe_gemm_a8_wide.hip)
+bool a8_wide_gemm_fits(int phase, const GemmArgs& a);
+moe_status launch_gemm_a8_wide(int phase, const GemmArgs& a, hipStream_t st);
 moe_status launch_gemm_w4a8(int phase, const GemmArgs& a, hipStream_t st);
 
 // FP8 weights, bf16 activations: the 160 x 512 tile GEMM (moe_gemm_wide.hip)

@@ -378,6 +378,9 @@ bool a8_gemm_fits(int phase, const GemmArgs& a) {
 moe_status launch_gemm_a8(int phase, const GemmArgs& a, hipStream_t st) {
     if (!a8_gemm_fits(phase, a)) return MOE_ERR_UNSUPPORTED;
     if (a.fp4) return launch_gemm_w4a8(phase, a, st);
+    // the down projection takes 160 x 512 tiles when an average expert fits one 160-row m-tile
+    const int64_t n_exp = a.offsets ? a.n_groups : 1;
+    if (a8_wide_gemm_fits(phase, a) && a.rows <= 160 * n_exp) return launch_gemm_a8_wide(phase, a, st);
     const int cols = phase == 1 ? kA8N / 2 : kA8N;
     const int groups = a.offsets ? a.n_groups : 1;
     const int64_t mt = ((int64_t)a.rows + kA8M - 1) / kA8M + std::min<int64_t>(groups, a.rows);

@@ -84,6 +84,9 @@ def test_quantize_act_ragged_row_counts():
     mid(T=144, H=8192, I=256, E=2, k=2),          # K = 8192, the FP8-code GEMM's largest
     mid(T=200, H=16384, I=256, E=4, k=2),         # the largest H: phase 1 dequantises
     mid(T=150, H=256, I=16384, E=2, k=1),         # the largest I: phase 2 dequantises
+    mid(T=600, I=512, E=8, k=2, scores="zipf"),   # 160 x 512 tiles (150 rows an expert on
+                                                  # average), a hot expert's m-tile stack
+    mid(T=120, H=640, I=768, E=4, k=2),           # 160 x 512 tiles in phase 1 with 5 blocks
 ])
 def test_a8_layer(cfg):
     layer = layer_for(cfg, seed=1)
